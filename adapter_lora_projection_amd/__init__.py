@@ -1,0 +1,12 @@
+"""MI355X (gfx950) multi-adapter LoRA projection: chunked-SGMV shrink/expand and the fused
+single-adapter LoRA+SwiGLU MLP, as hand-written HIP kernels behind a C ABI.
+
+``_lib`` mirrors the C entry points one to one; ``ops`` adds tensor-level helpers that infer
+sizes and strides from torch tensors, allocate outputs and workspaces, and pass the current
+stream. Every step runs in the HIP library; there is no CPU path.
+"""
+
+from ._lib import LoraError, lib, lora_version
+from .ops import expand, schedule_tiles, shrink
+
+__all__ = ["LoraError", "lib", "lora_version", "shrink", "expand", "schedule_tiles"]

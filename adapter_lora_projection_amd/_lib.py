@@ -1,0 +1,115 @@
+"""ctypes binding of ``liblora_mi355x.so`` (argument marshalling only).
+
+The functions named like the C entry points take plain integers or torch tensors (passed as
+device pointers) and raise :class:`LoraError` on a non-OK status. There is no fallback: if the
+library is missing the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora_mi355x.so")
+
+LORA_OK, LORA_EINVAL, LORA_EUNSUPPORTED, LORA_EWORKSPACE, LORA_EHIP, LORA_EVALUE = range(6)
+LORA_F32, LORA_BF16, LORA_F16 = 0, 1, 2
+
+# Every symbol the public header declares, with (restype, argtypes).
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = {
+    "lora_status_str": (ctypes.c_char_p, [_i32]),
+    "lora_version": (ctypes.c_char_p, []),
+    "lora_shrink": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
+                           _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
+    "lora_shrink_workspace_size": (_sz, [_i32, _i64, _i64, _i32, _i32, _i32]),
+    "lora_expand": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _i64,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
+    "lora_expand_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, _i64]),
+    "lora_schedule_tiles": (_i32, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                                   _sz, _vp]),
+    "lora_tuning_override": (None, [_i32, _i32]),
+}
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_str(status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(t) -> int | None:
+    """Device pointer of a tensor (or an int / None passed through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != LORA_OK:
+        raise LoraError(fn, st)
+
+
+def status_str(st: int) -> str:
+    return lib().lora_status_str(st).decode()
+
+
+def lora_version() -> str:
+    return lib().lora_version().decode()
+
+
+def lora_shrink(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr, weight_indices,
+                permutation, lora_ranks, h, ldh, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_shrink(dtype, T, K, S, R, L, G, _p(x), ldx, _p(w_a), lda, _p(seg_indptr),
+                           _p(weight_indices), _p(permutation), _p(lora_ranks), _p(h), ldh,
+                           _p(workspace), workspace_bytes, stream)
+    _check("lora_shrink", st)
+
+
+def lora_shrink_workspace_size(dtype, T, K, S, R, G) -> int:
+    return int(lib().lora_shrink_workspace_size(dtype, T, K, S, R, G))
+
+
+def lora_expand(dtype, T, S, R, L, G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
+                weight_indices, permutation, lora_ranks, scalings, y, ldy, workspace,
+                workspace_bytes, stream) -> None:
+    st = lib().lora_expand(dtype, T, S, R, L, G, N, _p(h), ldh, _p(w_b), ldb, _p(slice_offsets),
+                           _p(seg_indptr), _p(weight_indices), _p(permutation), _p(lora_ranks),
+                           _p(scalings), _p(y), ldy, _p(workspace), workspace_bytes, stream)
+    _check("lora_expand", st)
+
+
+def lora_expand_workspace_size(dtype, T, S, R, G, N) -> int:
+    return int(lib().lora_expand_workspace_size(dtype, T, S, R, G, N))
+
+
+def lora_schedule_tiles(T, G, BM, method, seg_indptr, weight_indices, lora_ranks, tiles,
+                        max_tiles, count, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_schedule_tiles(T, G, BM, method, _p(seg_indptr), _p(weight_indices),
+                                   _p(lora_ranks), _p(tiles), max_tiles, _p(count), _p(workspace),
+                                   workspace_bytes, stream)
+    _check("lora_schedule_tiles", st)
+
+
+def lora_tuning_override(op: int, variant: int) -> None:
+    lib().lora_tuning_override(op, variant)

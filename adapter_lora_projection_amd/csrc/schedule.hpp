@@ -1,0 +1,164 @@
+// Device-side segment scheduler.
+//
+// The compute kernels are launched on a grid whose tile dimension is the host-known bound
+// ceil(T / BM) + G, so no device-to-host read is needed to size a launch (the on-device segment
+// scheduler of "Decode LoRA kernels are optimized", Summary). Tile t of the segment-major list is
+// found from seg_indptr by each workgroup (inline search: one coalesced pass over seg_indptr in
+// chunks of the workgroup size and a block scan of per-segment tile counts), or read from a list
+// built once by the standalone scheduler kernel when the segment count is large.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace lmx {
+
+// Tile record: segment, first sorted position, rows, adapter.
+struct Tile {
+  int g, m0, mlen, a;
+};
+
+// Inclusive scan over the workgroup; `scratch` holds one int per wave. Contains barriers:
+// every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* total) {
+  constexpr int NWAVE = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) scratch[w] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) {
+    int s = scratch[i];
+    before += (i < w) ? s : 0;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return v + before;
+}
+
+// Finds tile `t` (segment-major, BM rows) by scanning seg_indptr. Result in `out` (LDS),
+// out->g = -1 when t is past the last tile. Every thread must call it.
+template <int NT>
+__device__ __forceinline__ void find_tile_inline(const int* __restrict__ seg_indptr,
+                                                 const int* __restrict__ weight_indices, int G,
+                                                 int BM, int t, Tile* out, int* scan_scratch) {
+  if (threadIdx.x == 0) out->g = -1;
+  int carry = 0;
+  for (int c0 = 0; c0 < G; c0 += NT) {
+    const int g = c0 + int(threadIdx.x);
+    int lo = 0, len = 0;
+    if (g < G) {
+      lo = seg_indptr[g];
+      len = max(seg_indptr[g + 1] - lo, 0);
+    }
+    const int nt = (len + BM - 1) / BM;
+    int total;
+    const int incl = block_inclusive_scan<NT>(nt, scan_scratch, &total);
+    const int excl = incl - nt;
+    if (g < G && t >= carry + excl && t < carry + incl) {
+      const int k = t - carry - excl;
+      out->g = g;
+      out->m0 = lo + k * BM;
+      out->mlen = min(BM, len - k * BM);
+      out->a = weight_indices[g];
+    }
+    carry += total;
+    if (t < carry) break;  // uniform: carry and t are the same in every thread
+  }
+  __syncthreads();
+}
+
+// Standalone scheduler: one workgroup writes the whole tile list and its length.
+template <int NT>
+__global__ __launch_bounds__(NT) void schedule_kernel(const int* __restrict__ seg_indptr,
+                                                      const int* __restrict__ weight_indices,
+                                                      int G, int BM, int4* __restrict__ tiles,
+                                                      int* __restrict__ count) {
+  __shared__ int s_scan[NT / 64];
+  __shared__ int s_incl[NT];
+  __shared__ int s_lo[NT];
+  int carry = 0;
+  for (int c0 = 0; c0 < G; c0 += NT) {
+    const int g = c0 + int(threadIdx.x);
+    int lo = 0, len = 0;
+    if (g < G) {
+      lo = seg_indptr[g];
+      len = max(seg_indptr[g + 1] - lo, 0);
+    }
+    const int nt = (len + BM - 1) / BM;
+    int total;
+    const int incl = block_inclusive_scan<NT>(nt, s_scan, &total);
+    s_incl[threadIdx.x] = incl;
+    s_lo[threadIdx.x] = lo;
+    __syncthreads();
+    const int nseg = min(NT, G - c0);
+    for (int t = int(threadIdx.x); t < total; t += NT) {
+      // first segment of the chunk whose inclusive count exceeds t
+      int lo_i = 0, hi_i = nseg - 1;
+      while (lo_i < hi_i) {
+        const int mid = (lo_i + hi_i) >> 1;
+        if (s_incl[mid] > t) hi_i = mid; else lo_i = mid + 1;
+      }
+      const int excl = (lo_i == 0) ? 0 : s_incl[lo_i - 1];
+      const int k = t - excl;
+      const int seg_lo = s_lo[lo_i];
+      const int seg_len = seg_indptr[c0 + lo_i + 1] - seg_lo;
+      tiles[carry + t] = make_int4(c0 + lo_i, seg_lo + k * BM, min(BM, seg_len - k * BM),
+                                   weight_indices[c0 + lo_i]);
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *count = carry;
+}
+
+// Tile for this workgroup: from the prebuilt list when `tiles` is non-null, else inline.
+template <int NT>
+__device__ __forceinline__ void get_tile(const int* __restrict__ seg_indptr,
+                                         const int* __restrict__ weight_indices, int G, int BM,
+                                         const int4* __restrict__ tiles,
+                                         const int* __restrict__ tile_count, int t, Tile* out,
+                                         int* scan_scratch) {
+  if (tiles != nullptr) {
+    if (threadIdx.x == 0) {
+      if (t < *tile_count) {
+        const int4 v = tiles[t];
+        out->g = v.x; out->m0 = v.y; out->mlen = v.z; out->a = v.w;
+      } else {
+        out->g = -1;
+      }
+    }
+    __syncthreads();
+  } else {
+    find_tile_inline<NT>(seg_indptr, weight_indices, G, BM, t, out, scan_scratch);
+  }
+}
+
+// Column block b of the per-slice blocking (blocks never straddle a slice boundary):
+// returns false when b is past the last block. Uniform loads of slice_offsets.
+__device__ __forceinline__ bool find_nblock(const int* __restrict__ slice_offsets, int S, int BN,
+                                            int b, int* s_out, int* n0_out, int* nlen_out) {
+  int lo = slice_offsets[0];
+  for (int s = 0; s < S; ++s) {
+    const int hi = slice_offsets[s + 1];
+    const int len = max(hi - lo, 0);
+    const int nb = (len + BN - 1) / BN;
+    if (b < nb) {
+      *s_out = s;
+      *n0_out = lo + b * BN;
+      *nlen_out = min(BN, len - b * BN);
+      return true;
+    }
+    b -= nb;
+    lo = hi;
+  }
+  return false;
+}
+
+}  // namespace lmx

@@ -1,0 +1,131 @@
+"""Tensor-level helpers over the C ABI: sizes and strides from torch tensors, output and
+workspace allocation, and the current HIP stream. Marshalling only; the work is the library's.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.LORA_F32, torch.bfloat16: _lib.LORA_BF16, torch.float16: _lib.LORA_F16}
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(*ts) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _meta(t: torch.Tensor, n: int | None, name: str) -> None:
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 vector")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name} must have {n} entries")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride of a matrix whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _stacked(t: torch.Tensor, name: str) -> tuple[int, int]:
+    """(rows per adapter, row stride) of a stacked [L][rows][cols] weight whose adapters are
+    packed back to back."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+        raise ValueError(f"{name} must be [L][rows][cols] with packed adapters and unit column stride")
+    return t.shape[1], t.stride(1)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def shrink(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, S: int, R: int,
+           h: torch.Tensor | None = None) -> torch.Tensor:
+    """h = x[perm] A_a^T per segment (``lora_shrink``). x: [T][K] (row stride >= K),
+    w_a: [L][S*R][K]; returns h [T][S*R] in sorted order."""
+    _dev(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, h)
+    T, K = x.shape
+    ldx = _rows(x, "x")
+    rows, lda = _stacked(w_a, "w_a")
+    if rows != S * R or w_a.shape[2] != K:
+        raise ValueError("w_a must be [L][S*R][K]")
+    G = weight_indices.numel()
+    _meta(seg_indptr, G + 1, "seg_indptr")
+    _meta(weight_indices, None, "weight_indices")
+    _meta(permutation, T, "permutation")
+    _meta(lora_ranks, w_a.shape[0], "lora_ranks")
+    if h is None:
+        h = torch.empty((T, S * R), dtype=x.dtype, device=x.device)
+    ldh = _rows(h, "h")
+    dt = dtype_code(x)
+    if w_a.dtype != x.dtype or h.dtype != x.dtype:
+        raise TypeError("x, w_a and h must share a dtype")
+    nbytes = _lib.lora_shrink_workspace_size(dt, T, K, S, R, G)
+    ws = _workspace(nbytes, x.device)
+    _lib.lora_shrink(dt, T, K, S, R, w_a.shape[0], G, x, ldx, w_a, lda, seg_indptr, weight_indices,
+                     permutation, lora_ranks, h, ldh, ws, nbytes, _stream())
+    return h
+
+
+def expand(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks, scalings,
+           y, S: int, R: int) -> torch.Tensor:
+    """y[perm[i], slice] += scale_a * h B_a^T in place (``lora_expand``). h: [T][S*R] sorted
+    order, w_b: [L][N][R], y: [T][>=N] token order. Returns y."""
+    _dev(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks, scalings, y)
+    T = h.shape[0]
+    ldh = _rows(h, "h")
+    N, ldb = _stacked(w_b, "w_b")
+    if w_b.shape[2] != R:
+        raise ValueError("w_b must be [L][N][R]")
+    ldy = _rows(y, "y")
+    if y.shape[0] != T or y.shape[1] < N:
+        raise ValueError("y must be [T][>=N]")
+    G = weight_indices.numel()
+    _meta(slice_offsets, S + 1, "slice_offsets")
+    _meta(seg_indptr, G + 1, "seg_indptr")
+    _meta(weight_indices, None, "weight_indices")
+    _meta(permutation, T, "permutation")
+    _meta(lora_ranks, w_b.shape[0], "lora_ranks")
+    if scalings.dtype != torch.float32 or scalings.numel() != w_b.shape[0]:
+        raise ValueError("scalings must be float32 [L]")
+    dt = dtype_code(y)
+    if h.dtype != y.dtype or w_b.dtype != y.dtype:
+        raise TypeError("h, w_b and y must share a dtype")
+    nbytes = _lib.lora_expand_workspace_size(dt, T, S, R, G, N)
+    ws = _workspace(nbytes, y.device)
+    _lib.lora_expand(dt, T, S, R, w_b.shape[0], G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
+                     weight_indices, permutation, lora_ranks, scalings, y, ldy, ws, nbytes, _stream())
+    return y
+
+
+def schedule_tiles(T: int, seg_indptr, weight_indices, lora_ranks, BM: int, method: int = 0) -> torch.Tensor:
+    """The device segment schedule as an int32 [count][5] tensor of (g, m0, mlen, a, r)."""
+    _dev(seg_indptr, weight_indices, lora_ranks)
+    G = weight_indices.numel()
+    bound = (T + BM - 1) // BM + G
+    dev = seg_indptr.device
+    tiles = torch.full((max(bound, 1), 5), -1, dtype=torch.int32, device=dev)
+    count = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = bound * 16 + 256
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if method == 1 else None
+    _lib.lora_schedule_tiles(T, G, BM, method, seg_indptr, weight_indices, lora_ranks, tiles,
+                             max(bound, 1), count, ws, nbytes if ws is not None else 0, _stream())
+    n = int(count.item())
+    return tiles[:n].clone()

@@ -1,0 +1,167 @@
+/*
+ * lora_mi355x.h -- C ABI of the MI355X (gfx950) multi-adapter LoRA projection library.
+ *
+ * Operations (pages as titled):
+ *   - lora_shrink / lora_expand: the chunked-SGMV LoRA shrink and expand of "Decode LoRA kernels
+ *     are optimized" (sgl-kernel-xpu pull request 550), Summary: a gathered grouped GEMM (rows of
+ *     x read through a token permutation, one rank block per output slice) and a scattered grouped
+ *     GEMM whose epilogue applies the adapter scaling and the per-slice column offsets, driven by
+ *     seg_indptr / weight_indices / permutation / slice offsets. The weight operand is stored
+ *     [out][in] row-major, as in the masked operand load shown in that page's review thread.
+ *   - lora_mlp_fused: the single-adapter LoRA MLP with fused SwiGLU of "Add optional fast lora
+ *     path for qwen2/qwen3 on npu" (ms-swift pull request 9754), What this PR does and
+ *     Compatibility checks (dropout 0, one adapter, no bias, unmerged weights).
+ *   - lora_schedule_tiles: export of the device segment schedule (the on-device segment scheduler
+ *     named in the Summary of pull request 550) for checking.
+ *   - lora_check_metadata: the value checks that pull request 550 (Behaviour changes) moves out of
+ *     the default path; here they are an explicit, synchronizing call.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to device memory (hipMalloc or torch CUDA
+ *     tensors) of the current HIP device; host pointers are named as such.
+ *   - The caller owns every buffer. No entry point allocates, frees or keeps device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
+ *     without waiting, except lora_check_metadata, which waits for its own result.
+ *   - No entry point throws or aborts. Argument errors are reported before anything is enqueued
+ *     and leave every output untouched.
+ *   - Metadata values (seg_indptr, weight_indices, permutation, lora_ranks, slice_offsets) are not
+ *     checked by the compute calls: values outside the rules of lora_check_metadata give
+ *     undefined results (wrong output or a GPU memory fault), as pull request 550 specifies.
+ *   - Element strides (ld*) are in elements, not bytes. 16-byte aligned pointers and strides that
+ *     keep every row 16-byte aligned take the vector-load path; any other alignment is accepted
+ *     and takes narrower loads.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_EINVAL = 1,        /* a null pointer with a nonzero extent, bad sizes or strides */
+  LORA_EUNSUPPORTED = 2,  /* dtype or size outside what the kernels implement */
+  LORA_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_size query */
+  LORA_EHIP = 4,          /* the HIP runtime reported an error while enqueuing */
+  LORA_EVALUE = 5         /* lora_check_metadata found invalid metadata */
+} lora_status;
+
+typedef enum lora_dtype {
+  LORA_F32 = 0,   /* IEEE binary32 */
+  LORA_BF16 = 1,  /* bfloat16 */
+  LORA_F16 = 2    /* IEEE binary16 */
+} lora_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* lora_status_str(lora_status s);
+
+/* Library version string, e.g. "lora_mi355x 0.1 gfx950". */
+const char* lora_version(void);
+
+/*
+ * lora_shrink -- h = x[perm] * A_a^T per segment, one rank block per slice.
+ *
+ * For segment g (sorted positions seg_indptr[g] .. seg_indptr[g+1]-1), adapter
+ * a = weight_indices[g], rank r = lora_ranks[a], every sorted position i in the segment, slice
+ * s < S and j < R:
+ *     h[i][s*R + j] = round( sum_{k<K} x[permutation[i]][k] * A[a][s*R + j][k] )   for j < r
+ *     h[i][s*R + j] = 0                                                             for j >= r
+ * accumulated in fp32 and rounded once (round to nearest even) to `dtype`.
+ *
+ *   dtype          element type of x, w_a and h.
+ *   T              tokens (rows of x and of h); T == 0 is a no-op.
+ *   K              input features (columns read from each x / A row), K >= 1.
+ *   S, R           slices and padded rank; 1 <= S, 1 <= R, S*R <= 512.
+ *   L              adapters stacked in w_a.
+ *   G              segments; G == 0 is a no-op.
+ *   x              device [T][ldx], ldx >= K; row t is token t. Only the first K entries of a row
+ *                  are read.
+ *   w_a            device [L*S*R][lda], lda >= K: row (a*S + s)*R + j holds A[a][s*R+j][:].
+ *                  Rows with j >= lora_ranks[a] are never read.
+ *   seg_indptr     device int32 [G+1]: 0 = seg_indptr[0] <= ... <= seg_indptr[G] = T.
+ *   weight_indices device int32 [G], values in [0, L).
+ *   permutation    device int32 [T], a bijection of [0, T): sorted position i reads token row
+ *                  permutation[i].
+ *   lora_ranks     device int32 [L], values in [0, R].
+ *   h              device [T][ldh], ldh >= S*R; row i is sorted position i. Columns >= S*R are
+ *                  not written.
+ *   workspace      device scratch of at least lora_shrink_workspace_size(...) bytes; may be NULL
+ *                  when that size is 0. Not read before written; contents undefined afterwards.
+ */
+lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t L,
+                        int32_t G, const void* x, int64_t ldx, const void* w_a, int64_t lda,
+                        const int32_t* seg_indptr, const int32_t* weight_indices,
+                        const int32_t* permutation, const int32_t* lora_ranks, void* h, int64_t ldh,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                                  int32_t G);
+
+/*
+ * lora_expand -- y[perm[i]][slice s] += scale_a * h_i,s * B_a^T (scaled scatter-add).
+ *
+ * For segment g (adapter a, rank r, scale = scalings[a]), sorted position i in it, slice s and
+ * output column n with slice_offsets[s] <= n < slice_offsets[s+1]:
+ *     y[permutation[i]][n] = round( y[permutation[i]][n]
+ *                                   + scale * sum_{j<r} h[i][s*R + j] * B[a][n][j] )
+ * with an fp32 accumulation and one rounding to `dtype` per stored element. Entries of y outside
+ * the slices, and every row of a rank-0 adapter, are neither read nor written.
+ *
+ *   T, S, R, L, G  as for lora_shrink.
+ *   N              columns covered by the slices; slice_offsets[S] == N.
+ *   h              device [T][ldh], ldh >= S*R, sorted order (the output of lora_shrink).
+ *   w_b            device [L*N][ldb], ldb >= R: row a*N + n holds B[a][n][:]. Entries with
+ *                  j >= lora_ranks[a] are never read.
+ *   slice_offsets  device int32 [S+1]: 0 <= slice_offsets[0] <= ... <= slice_offsets[S] = N.
+ *   scalings       device float32 [L] (alpha / rank of each adapter).
+ *   y              device [T][ldy] read and written in place, ldy >= N; row t is token t.
+ *   workspace      as for lora_shrink, sized by lora_expand_workspace_size.
+ */
+lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t L, int32_t G,
+                        int64_t N, const void* h, int64_t ldh, const void* w_b, int64_t ldb,
+                        const int32_t* slice_offsets, const int32_t* seg_indptr,
+                        const int32_t* weight_indices, const int32_t* permutation,
+                        const int32_t* lora_ranks, const float* scalings, void* y, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t G,
+                                  int64_t N);
+
+/*
+ * lora_schedule_tiles -- the segment schedule the compute kernels use, exported for checking.
+ *
+ * Each non-empty segment g is cut into row tiles of at most BM sorted positions starting at
+ * seg_indptr[g]; empty segments give none. The list is segment-major with ascending starts.
+ * Writes tiles[5*t + {0..4}] = {g, m0, mlen, a, r} (a = weight_indices[g], r = lora_ranks[a])
+ * for t < *count, and *count.
+ *
+ *   BM         tile height, 1 <= BM <= 4096.
+ *   method     0: the per-workgroup search the kernels run inline; 1: the standalone scheduler
+ *              kernel used when G is large. Both must give the same list.
+ *   tiles      device int32 [max_tiles][5]; max_tiles >= T/BM + G (rounded up) suffices.
+ *   count      device int32 [1].
+ *   workspace  device scratch of at least 16*(ceil(T/BM) + G) + 256 bytes for method 1.
+ */
+lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method,
+                                const int32_t* seg_indptr, const int32_t* weight_indices,
+                                const int32_t* lora_ranks, int32_t* tiles, int64_t max_tiles,
+                                int32_t* count, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * lora_tuning_override -- pins the kernel shape the library picks for an operation, for
+ * measurement sweeps. op 0 = shrink (variant 0..2), op 1 = expand (variant 0..1); variant -1
+ * restores the automatic choice. Process-wide, not thread-safe; results are identical for every
+ * variant up to fp32 summation order.
+ */
+void lora_tuning_override(int32_t op, int32_t variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

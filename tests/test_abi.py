@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every symbol the public headers declare, and rejects bad
+arguments on the host (no GPU needed: only argument-error paths and size queries are called)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from adapter_lora_projection_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(hdr).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(lora_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = _declared()
+    assert {"lora_shrink", "lora_expand", "lora_schedule_tiles"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+    assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version():
+    assert _lib.status_str(0) == "LORA_OK"
+    assert "EINVAL" in _lib.status_str(1)
+    assert "unknown" in _lib.status_str(99)
+    assert "gfx950" in _lib.lora_version()
+
+
+def _shrink(**kw):
+    args = dict(dtype=1, T=8, K=16, S=1, R=16, L=1, G=1, x=0x1000, ldx=16, w_a=0x2000, lda=16,
+                seg_indptr=0x3000, weight_indices=0x4000, permutation=0x5000, lora_ranks=0x6000,
+                h=0x7000, ldh=16, workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return _lib.lib().lora_shrink(*args.values())
+
+
+def _expand(**kw):
+    args = dict(dtype=1, T=8, S=1, R=16, L=1, G=1, N=32, h=0x1000, ldh=16, w_b=0x2000, ldb=16,
+                slice_offsets=0x3000, seg_indptr=0x4000, weight_indices=0x5000, permutation=0x6000,
+                lora_ranks=0x7000, scalings=0x8000, y=0x9000, ldy=32, workspace=None,
+                workspace_bytes=0, stream=None)
+    args.update(kw)
+    return _lib.lib().lora_expand(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.LORA_EUNSUPPORTED),
+    (dict(T=-1), _lib.LORA_EINVAL),
+    (dict(S=0), _lib.LORA_EINVAL),
+    (dict(R=0), _lib.LORA_EINVAL),
+    (dict(R=2048), _lib.LORA_EUNSUPPORTED),
+    (dict(K=0), _lib.LORA_EINVAL),
+    (dict(x=None), _lib.LORA_EINVAL),
+    (dict(permutation=None), _lib.LORA_EINVAL),
+    (dict(h=None), _lib.LORA_EINVAL),
+    (dict(ldx=15), _lib.LORA_EINVAL),
+    (dict(lda=8), _lib.LORA_EINVAL),
+    (dict(ldh=15), _lib.LORA_EINVAL),
+    (dict(T=5000, G=5000), _lib.LORA_EWORKSPACE),
+    (dict(T=0, x=None, h=None), _lib.LORA_OK),
+    (dict(G=0, x=None), _lib.LORA_OK),
+])
+def test_shrink_host_validation(kw, code):
+    assert _shrink(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=-1), _lib.LORA_EUNSUPPORTED),
+    (dict(N=-1), _lib.LORA_EINVAL),
+    (dict(scalings=None), _lib.LORA_EINVAL),
+    (dict(slice_offsets=None), _lib.LORA_EINVAL),
+    (dict(ldb=15), _lib.LORA_EINVAL),
+    (dict(ldy=31), _lib.LORA_EINVAL),
+    (dict(ldh=8), _lib.LORA_EINVAL),
+    (dict(S=65), _lib.LORA_EUNSUPPORTED),
+    (dict(T=5000, G=5000), _lib.LORA_EWORKSPACE),
+    (dict(N=0, y=None), _lib.LORA_OK),
+    (dict(T=0, h=None, y=None), _lib.LORA_OK),
+])
+def test_expand_host_validation(kw, code):
+    assert _expand(**kw) == code
+
+
+def test_workspace_sizes():
+    assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) == 0
+    assert _lib.lora_expand_workspace_size(1, 50, 3, 16, 4, 6144) == 0
+    n = _lib.lora_shrink_workspace_size(1, 16384, 256, 3, 16, 16384)
+    assert n >= 16 * 16384
+    assert _lib.lora_shrink_workspace_size(1, 0, 256, 3, 16, 4) == 0
+
+
+def test_schedule_host_validation():
+    L = _lib.lib()
+    assert L.lora_schedule_tiles(10, 2, 0, 0, 1, 1, 1, 1, 100, 1, None, 0, None) == _lib.LORA_EINVAL
+    assert L.lora_schedule_tiles(10, 2, 4, 2, 1, 1, 1, 1, 100, 1, None, 0, None) == _lib.LORA_EINVAL
+    assert L.lora_schedule_tiles(10, 2, 4, 0, 1, 1, 1, 1, 4, 1, None, 0, None) == _lib.LORA_EINVAL
+    assert L.lora_schedule_tiles(10, 2, 4, 1, 1, 1, 1, 1, 100, 1, None, 0, None) == _lib.LORA_EWORKSPACE

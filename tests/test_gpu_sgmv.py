@@ -1,0 +1,222 @@
+"""GPU parity of lora_shrink / lora_expand / lora_schedule_tiles against the CPU oracle.
+
+Every call goes through the C ABI (ctypes binding). Cases: the four SGMV workloads at full size
+(every output element compared), small cases spanning several tiles with ragged tails, the token
+sweep, every kernel shape, and the edge cases: empty segments, 16,384 one-token segments, rank-0
+and odd-rank adapters, NaN in rank padding and in row-stride gaps, misaligned base pointers and
+strides, B = 0, T = 0 / G = 0, permutation covariance.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import lora_inputs as li
+import oracle
+from tests.parity import assert_close_lowp, check_h, check_y, f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _alp():
+    import adapter_lora_projection_amd as alp
+
+    return alp
+
+
+def _run_pair(c, d=None, variant=(None, None)):
+    alp = _alp()
+    from adapter_lora_projection_amd import _lib
+
+    d = d or to_dev(c)
+    try:
+        if variant[0] is not None:
+            _lib.lora_tuning_override(0, variant[0])
+        if variant[1] is not None:
+            _lib.lora_tuning_override(1, variant[1])
+        h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
+                       d["lora_ranks"], c.S, c.R)
+        y = d["y_in"].clone()
+        alp.expand(h, d["B"], d["slice_offsets"], d["seg_indptr"], d["weight_indices"],
+                   d["permutation"], d["lora_ranks"], d["scalings"], y, c.S, c.R)
+        torch.cuda.synchronize()
+    finally:
+        _lib.lora_tuning_override(0, -1)
+        _lib.lora_tuning_override(1, -1)
+    return h.cpu(), y.cpu()
+
+
+def _check_pair(c, h, y):
+    check_h(c, h)
+    # expand is checked on the GPU's own h (its input), so the two checks are independent
+    check_y(c, h, y)
+
+
+# ------------------------------------------------------------------ the workloads at full size
+
+def test_tiny_f32():
+    c = li.config_tiny_f32()
+    print("case", c.name, flush=True)
+    h, y = _run_pair(c)
+    _check_pair(c, h, y)
+
+
+def test_decode_qkv_bf16():
+    c = li.config_decode_qkv()
+    print("case", c.name, flush=True)
+    h, y = _run_pair(c)
+    _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("part", [0, 1])
+def test_prefill_bf16(part):
+    c = li.config_prefill()[part]
+    print("case", c.name, flush=True)
+    h, y = _run_pair(c)
+    _check_pair(c, h, y)
+
+
+def test_irregular_f16():
+    c = li.config_irregular()
+    print("case", c.name, flush=True)
+    h, y = _run_pair(c)
+    _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("T", li.SWEEP_TOKENS)
+def test_sweep(T):
+    c = li.sweep_case(T)
+    print("case", c.name, flush=True)
+    h, y = _run_pair(c)
+    _check_pair(c, h, y)
+
+
+# ------------------------------------------------------------------ every kernel shape
+
+@pytest.mark.parametrize("sv", [0, 1, 2])
+@pytest.mark.parametrize("ev", [0, 1])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_variants_small(sv, ev, dtype):
+    """Several tiles per segment plus ragged tails, odd ranks, K tail, unaligned slices."""
+    c = li.make_sgmv(f"var_{dtype}", seed=40, T=301, K=517, S=3, R=32, L=5,
+                     slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
+    print("case", c.name, sv, ev, flush=True)
+    h, y = _run_pair(c, variant=(sv, ev))
+    _check_pair(c, h, y)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_empty_and_zero_sizes():
+    alp = _alp()
+    c = li.make_sgmv("empties", seed=41, T=64, K=96, S=2, R=16, L=6, slice_offsets=[0, 40, 72],
+                     dtype="bf16", fixed_indptr=[0, 0, 30, 30, 30, 64, 64],
+                     fixed_weight_indices=[5, 0, 1, 2, 3, 4])
+    h, y = _run_pair(c)
+    _check_pair(c, h, y)
+    # T == 0 and G == 0 are no-ops that touch nothing
+    d = to_dev(c)
+    z = torch.zeros(0, dtype=torch.int32, device="cuda")
+    hh = torch.full((64, 32), 7.0, dtype=torch.bfloat16, device="cuda")
+    alp.shrink(d["x"][:0], d["A"], torch.zeros(1, dtype=torch.int32, device="cuda"), z, z,
+               d["lora_ranks"], 2, 16, h=hh[:0])
+    assert (hh == 7).all()
+
+
+def test_one_token_segments_16384():
+    """16,384 segments of one token each (the standalone scheduler path)."""
+    T = 16384
+    c = li.make_sgmv("ones", seed=42, T=T, K=256, S=3, R=16, L=8, slice_offsets=[0, 128, 160, 192],
+                     dtype="bf16", lengths="ones")
+    print("case", c.name, flush=True)
+    h, y = _run_pair(c)
+    _check_pair(c, h, y)
+
+
+def test_nan_padding_and_stride_gaps_misaligned():
+    """NaN in A rows / B columns beyond each rank and in the row-stride gaps of x, A, B, h and y
+    must never reach an output; base pointers offset by one element exercise unaligned loads."""
+    alp = _alp()
+    c = li.make_sgmv("nanpad", seed=43, T=200, K=301, S=2, R=16, L=4, slice_offsets=[0, 77, 141],
+                     dtype="f16", ranks=[16, 3, 9, 1])
+    d = to_dev(c)
+    nan = float("nan")
+    T, K, S, R, L, N = c.T, c.K, c.S, c.R, c.L, c.N
+    xb = torch.full((T, K + 13), nan, dtype=torch.float16, device="cuda")
+    x = xb[:, 1:K + 1]
+    x.copy_(d["x"])
+    Ab = torch.full((L * S * R * (K + 7) + 1,), nan, dtype=torch.float16, device="cuda")
+    A = Ab[1:].view(L, S * R, K + 7)[:, :, :K]
+    A.copy_(d["A"])
+    for a in range(L):
+        r = c.lora_ranks[a].item()
+        A.unflatten(1, (S, R))[a, :, r:, :] = nan
+    Bb = torch.full((L * N * (R + 3) + 1,), nan, dtype=torch.float16, device="cuda")
+    B = Bb[1:].view(L, N, R + 3)[:, :, :R]
+    B.copy_(d["B"])
+    for a in range(L):
+        B[a, :, c.lora_ranks[a].item():] = nan
+    hb = torch.full((T, S * R + 5), nan, dtype=torch.float16, device="cuda")
+    h = hb[:, :S * R]
+    alp.shrink(x, A, d["seg_indptr"], d["weight_indices"], d["permutation"], d["lora_ranks"], S, R, h=h)
+    yb = torch.full((T, N + 9), nan, dtype=torch.float16, device="cuda")
+    yb[:, 1:N + 1] = d["y_in"]
+    y = yb[:, 1:N + 1]
+    alp.expand(h, B, d["slice_offsets"], d["seg_indptr"], d["weight_indices"], d["permutation"],
+               d["lora_ranks"], d["scalings"], y, S, R)
+    torch.cuda.synchronize()
+    hc, ybc = h.cpu(), yb.cpu()
+    assert torch.isfinite(hc).all()
+    assert torch.isnan(hb[:, S * R:]).all()
+    check_h(c, hc)
+    check_y(c, hc, ybc[:, 1:N + 1])
+    assert torch.isnan(ybc[:, 0]).all() and torch.isnan(ybc[:, N + 1:]).all()
+
+
+def test_b_zero_exact():
+    c = li.make_sgmv("bzero", seed=44, T=333, K=128, S=3, R=16, L=4, slice_offsets=[0, 64, 96, 128],
+                     dtype="bf16")
+    c.B.zero_()
+    h, y = _run_pair(c)
+    assert torch.equal(y.float(), c.y_in.float())  # value compare: +0 == -0
+
+
+def test_permutation_covariance_bitwise():
+    """Relabelling tokens permutes y rows and leaves h unchanged, bitwise."""
+    c = li.make_sgmv("cov", seed=45, T=500, K=256, S=3, R=16, L=4, slice_offsets=[0, 256, 320, 384],
+                     dtype="bf16")
+    h1, y1 = _run_pair(c)
+    pi = torch.from_numpy(np.random.default_rng(5).permutation(c.T))
+    c2 = li.make_sgmv("cov", seed=45, T=500, K=256, S=3, R=16, L=4, slice_offsets=[0, 256, 320, 384],
+                      dtype="bf16")
+    c2.x = torch.empty_like(c.x); c2.x[pi] = c.x
+    c2.y_in = torch.empty_like(c.y_in); c2.y_in[pi] = c.y_in
+    c2.permutation = pi[c.permutation.long()].to(torch.int32)
+    h2, y2 = _run_pair(c2)
+    assert torch.equal(h1, h2)
+    assert torch.equal(y2[pi], y1)
+
+
+def test_deterministic_repeat():
+    c = li.config_irregular()
+    d = to_dev(c)
+    h1, y1 = _run_pair(c, d)
+    h2, y2 = _run_pair(c, d)
+    assert torch.equal(h1, h2) and torch.equal(y1, y2)
+
+
+# ------------------------------------------------------------------ the schedule (bit-exact)
+
+@pytest.mark.parametrize("method", [0, 1])
+@pytest.mark.parametrize("BM", [1, 16, 64, 100])
+def test_schedule_bit_exact(method, BM):
+    alp = _alp()
+    for c in (li.config_irregular(), li.config_decode_qkv(),
+              li.make_sgmv("ones", seed=46, T=3000, K=8, S=1, R=16, L=8, slice_offsets=[0, 16],
+                           dtype="bf16", lengths="ones")):
+        got = alp.schedule_tiles(c.T, c.seg_indptr.cuda(), c.weight_indices.cuda(),
+                                 c.lora_ranks.cuda(), BM, method).cpu().numpy()
+        ref = oracle.tile_list(c.seg_indptr, c.weight_indices, c.lora_ranks, BM)
+        assert np.array_equal(got, ref), (c.name, method, BM)
