@@ -60,30 +60,127 @@ struct Traits<DT_F16> {
   }
 };
 
-// One 16-byte operand fragment: kPerFrag consecutive elements of a row starting at element k,
-// zero-filled at and beyond `kend`. Uses a single dwordx4 load when the address is 16-byte
-// aligned and the fragment is whole, dword loads when it is 4-byte aligned, element loads
-// otherwise.
+// Branch-free 16-byte operand fetch, split in two so that a run of fetches stays in flight:
+// fetch() only computes an address and issues the load(s); raw() / masked(valid) (called where the
+// operand is consumed) funnel-shift and, for masked(), zero every element at or beyond `valid`
+// (the same count that was passed to fetch()).
+// `p` points at an element of a row, `valid` is the number of elements from p that belong to the
+// operand (<= 0: none; a fragment holds 16/sizeof(S) elements) and `safe` is an element address
+// known to be readable (fetched instead of p when nothing is valid).
+//
+// ALIGNED: p and safe are 16-byte aligned, one load; a partial fragment stays inside its own
+// aligned block. Otherwise p may sit at any element boundary: the two aligned 16-byte blocks
+// covering the fragment are loaded and shifted; a block that holds no valid byte is replaced by
+// the first block, so no load touches a 16-byte block without a valid byte in it (such a block
+// never shares a page with memory the operand does not own).
 template <typename S>
-__device__ __forceinline__ uint4 load_frag(const S* __restrict__ row, int64_t k, int64_t kend) {
-  constexpr int n = 16 / sizeof(S);
-  const S* p = row + k;
-  if (k + n <= kend) {
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
-    if ((addr & 15u) == 0) return *reinterpret_cast<const uint4*>(p);
-    if ((addr & 3u) == 0) {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-      return make_uint4(q[0], q[1], q[2], q[3]);
-    }
-  }
-  union {
-    S e[n];
-    uint4 v;
-  } u;
+__device__ __forceinline__ uint4 mask_elems(uint4 v, int valid) {
+  uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (sizeof(S) == 2) {
 #pragma unroll
-  for (int i = 0; i < n; ++i) u.e[i] = (k + i < kend) ? p[i] : S(0);
-  return u.v;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = (2 * i < valid ? 0x0000ffffu : 0u) | (2 * i + 1 < valid ? 0xffff0000u : 0u);
+      u[i] &= m;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = i < valid ? u[i] : 0u;
+  }
+  return make_uint4(u[0], u[1], u[2], u[3]);
 }
+
+// 16-byte load through an explicitly global pointer (a generic pointer would become a flat load,
+// which the compiler cannot track precisely and answers with full waits).
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(1))) u32x4_t gu4;
+  const u32x4_t v = *(gu4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <typename S, bool ALIGNED>
+struct Frag;
+
+template <typename S>
+struct Frag<S, true> {
+  uint4 a;
+  __device__ __forceinline__ void fetch(const S* p, int v, const S* safe) {
+    a = gload16(v > 0 ? p : safe);
+  }
+  __device__ __forceinline__ uint4 raw() const { return a; }
+  __device__ __forceinline__ uint4 masked(int valid) const { return mask_elems<S>(a, valid); }
+};
+
+template <typename S>
+struct Frag<S, false> {
+  uint4 a, b;
+  uint32_t off;
+  __device__ __forceinline__ void fetch(const S* p, int v, const S* safe) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(v > 0 ? p : safe);
+    const uintptr_t lo = pa & ~uintptr_t(15);
+    off = uint32_t(pa & 15u);
+    const bool hi_ok = v > 0 && int(off) + v * int(sizeof(S)) > 16;
+    a = gload16(reinterpret_cast<const void*>(lo));
+    b = gload16(reinterpret_cast<const void*>(hi_ok ? lo + 16 : lo));
+  }
+  __device__ __forceinline__ uint4 raw() const {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t d = off >> 2, sh = off & 3u;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w0 = d == 0 ? w[i] : d == 1 ? w[i + 1] : d == 2 ? w[i + 2] : w[i + 3];
+      const uint32_t w1 = d == 0 ? w[i + 1] : d == 1 ? w[i + 2] : d == 2 ? w[i + 3] : w[i + 4];
+      o[i] = __builtin_amdgcn_alignbyte(w1, w0, sh);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  __device__ __forceinline__ uint4 masked(int valid) const { return mask_elems<S>(raw(), valid); }
+};
+
+// 8-byte variant of Frag for the streamed output rows (4 elements of a 16-bit type, 2 of fp32).
+__device__ __forceinline__ uint2 gload8(const void* p) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  typedef const __attribute__((address_space(1))) u32x2_t gu2;
+  const u32x2_t v = *(gu2*)(p);
+  return make_uint2(v.x, v.y);
+}
+
+template <typename S, bool ALIGNED>
+struct Frag8;
+
+template <typename S>
+struct Frag8<S, true> {
+  uint2 a;
+  __device__ __forceinline__ void fetch(const S* p, int v, const S* safe) {
+    a = gload8(v > 0 ? p : safe);
+  }
+  __device__ __forceinline__ uint2 raw() const { return a; }
+};
+
+template <typename S>
+struct Frag8<S, false> {
+  uint2 a, b;
+  uint32_t off;
+  __device__ __forceinline__ void fetch(const S* p, int v, const S* safe) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(v > 0 ? p : safe);
+    const uintptr_t lo = pa & ~uintptr_t(7);
+    off = uint32_t(pa & 7u);
+    const bool hi_ok = v > 0 && int(off) + v * int(sizeof(S)) > 8;
+    a = gload8(reinterpret_cast<const void*>(lo));
+    b = gload8(reinterpret_cast<const void*>(hi_ok ? lo + 8 : lo));
+  }
+  __device__ __forceinline__ uint2 raw() const {
+    const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+    const uint32_t d = off >> 2, sh = off & 3u;
+    const uint32_t o0 = __builtin_amdgcn_alignbyte(d ? w[2] : w[1], d ? w[1] : w[0], sh);
+    const uint32_t o1 = __builtin_amdgcn_alignbyte(d ? w[3] : w[2], d ? w[2] : w[1], sh);
+    return make_uint2(o0, o1);
+  }
+};
+
+// Wave index as a scalar, so loop bounds derived from it stay uniform branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
 
 // acc += A_frag * B_frag over one fragment step (32 reduction indices for 16-bit types,
 // 16 for fp32 as four 16x16x4 steps over the fragment's four elements).

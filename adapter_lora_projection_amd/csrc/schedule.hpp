@@ -12,9 +12,10 @@
 
 namespace lmx {
 
-// Tile record: segment, first sorted position, rows, adapter.
+// Tile record: segment, first sorted position, rows, adapter, its rank and scaling.
 struct Tile {
-  int g, m0, mlen, a;
+  int g, m0, mlen, a, r;
+  float sigma;
 };
 
 // Inclusive scan over the workgroup; `scratch` holds one int per wave. Contains barriers:
@@ -43,19 +44,24 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* to
 }
 
 // Finds tile `t` (segment-major, BM rows) by scanning seg_indptr. Result in `out` (LDS),
-// out->g = -1 when t is past the last tile. Every thread must call it.
+// out->g = -1 when t is past the last tile. Every thread must call it. Each thread loads its
+// segment's bounds, adapter, rank and (when `scalings` is non-null) scaling up front, so the
+// winning thread can publish the whole record without another dependent load.
 template <int NT>
 __device__ __forceinline__ void find_tile_inline(const int* __restrict__ seg_indptr,
-                                                 const int* __restrict__ weight_indices, int G,
+                                                 const int* __restrict__ weight_indices,
+                                                 const int* __restrict__ lora_ranks,
+                                                 const float* __restrict__ scalings, int G,
                                                  int BM, int t, Tile* out, int* scan_scratch) {
   if (threadIdx.x == 0) out->g = -1;
   int carry = 0;
   for (int c0 = 0; c0 < G; c0 += NT) {
     const int g = c0 + int(threadIdx.x);
-    int lo = 0, len = 0;
+    int lo = 0, len = 0, a = 0;
     if (g < G) {
       lo = seg_indptr[g];
       len = max(seg_indptr[g + 1] - lo, 0);
+      a = weight_indices[g];
     }
     const int nt = (len + BM - 1) / BM;
     int total;
@@ -66,7 +72,9 @@ __device__ __forceinline__ void find_tile_inline(const int* __restrict__ seg_ind
       out->g = g;
       out->m0 = lo + k * BM;
       out->mlen = min(BM, len - k * BM);
-      out->a = weight_indices[g];
+      out->a = a;
+      out->r = lora_ranks[a];
+      out->sigma = scalings != nullptr ? scalings[a] : 0.f;
     }
     carry += total;
     if (t < carry) break;  // uniform: carry and t are the same in every thread
@@ -121,7 +129,9 @@ __global__ __launch_bounds__(NT) void schedule_kernel(const int* __restrict__ se
 // Tile for this workgroup: from the prebuilt list when `tiles` is non-null, else inline.
 template <int NT>
 __device__ __forceinline__ void get_tile(const int* __restrict__ seg_indptr,
-                                         const int* __restrict__ weight_indices, int G, int BM,
+                                         const int* __restrict__ weight_indices,
+                                         const int* __restrict__ lora_ranks,
+                                         const float* __restrict__ scalings, int G, int BM,
                                          const int4* __restrict__ tiles,
                                          const int* __restrict__ tile_count, int t, Tile* out,
                                          int* scan_scratch) {
@@ -130,13 +140,16 @@ __device__ __forceinline__ void get_tile(const int* __restrict__ seg_indptr,
       if (t < *tile_count) {
         const int4 v = tiles[t];
         out->g = v.x; out->m0 = v.y; out->mlen = v.z; out->a = v.w;
+        out->r = lora_ranks[v.w];
+        out->sigma = scalings != nullptr ? scalings[v.w] : 0.f;
       } else {
         out->g = -1;
       }
     }
     __syncthreads();
   } else {
-    find_tile_inline<NT>(seg_indptr, weight_indices, G, BM, t, out, scan_scratch);
+    find_tile_inline<NT>(seg_indptr, weight_indices, lora_ranks, scalings, G, BM, t, out,
+                         scan_scratch);
   }
 }
 

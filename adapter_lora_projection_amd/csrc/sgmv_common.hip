@@ -1,0 +1,107 @@
+// Dispatch of the SGMV kernels by storage type, kernel-shape tables, and the standalone segment
+// scheduler with its tile-list export.
+#include "device_common.hpp"
+#include "schedule.hpp"
+#include "sgmv_kernels.hpp"
+
+namespace lmx {
+
+hipError_t launch_shrink_bf16(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);
+hipError_t launch_shrink_f16(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);
+hipError_t launch_shrink_f32(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);
+hipError_t launch_expand_bf16(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
+hipError_t launch_expand_f16(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
+hipError_t launch_expand_f32(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
+
+// Token rows per tile (16 * token groups) and waves of each kernel shape; these tables mirror the
+// variant lists of sgmv_impl.hpp.
+static const int kShrinkBM[] = {16, 32, 32, 16};
+static const int kExpandBM[] = {16, 16, 16};
+static const int kExpandWaves[] = {4, 8, 4};
+
+int num_shrink_variants() { return int(sizeof(kShrinkBM) / sizeof(int)); }
+int num_expand_variants() { return int(sizeof(kExpandBM) / sizeof(int)); }
+int shrink_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kShrinkBM[variant]; }
+int expand_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kExpandBM[variant]; }
+int expand_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 4 : kExpandWaves[variant]; }
+int expand_max_rank(int dtype) { return 2 * (dtype == DT_F32 ? Traits<DT_F32>::kStep : Traits<DT_BF16>::kStep); }
+
+hipError_t launch_shrink(int dtype, const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st) {
+  switch (dtype) {
+    case DT_F32: return launch_shrink_f32(a, plan, st);
+    case DT_BF16: return launch_shrink_bf16(a, plan, st);
+    default: return launch_shrink_f16(a, plan, st);
+  }
+}
+
+hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st) {
+  switch (dtype) {
+    case DT_F32: return launch_expand_f32(a, plan, st);
+    case DT_BF16: return launch_expand_bf16(a, plan, st);
+    default: return launch_expand_f16(a, plan, st);
+  }
+}
+
+hipError_t launch_schedule(const int* seg_indptr, const int* weight_indices, int G, int BM,
+                           int4* tiles, int* count, hipStream_t st) {
+  hipLaunchKernelGGL((schedule_kernel<1024>), dim3(1), dim3(1024), 0, st, seg_indptr,
+                     weight_indices, G, BM, tiles, count);
+  return hipGetLastError();
+}
+
+// Export of the inline search: workgroup t runs the same search the compute kernels run and
+// writes its tile (g, m0, mlen, a, r) at position t; the count is the number of valid tiles.
+template <int NT>
+__global__ __launch_bounds__(NT) void export_inline_tiles_kernel(
+    const int* __restrict__ seg_indptr, const int* __restrict__ weight_indices,
+    const int* __restrict__ lora_ranks, int G, int BM, int* __restrict__ out,
+    int* __restrict__ count) {
+  __shared__ Tile s_tile;
+  __shared__ int s_scan[NT / 64];
+  find_tile_inline<NT>(seg_indptr, weight_indices, lora_ranks, nullptr, G, BM, int(blockIdx.x),
+                       &s_tile, s_scan);
+  if (threadIdx.x == 0 && s_tile.g >= 0) {
+    int* o = out + int64_t(blockIdx.x) * 5;
+    o[0] = s_tile.g; o[1] = s_tile.m0; o[2] = s_tile.mlen; o[3] = s_tile.a; o[4] = s_tile.r;
+    atomicAdd(count, 1);
+  }
+}
+
+__global__ void export_list_tiles_kernel(const int4* __restrict__ tiles,
+                                         const int* __restrict__ tile_count,
+                                         const int* __restrict__ lora_ranks, int bound,
+                                         int* __restrict__ out, int* __restrict__ count) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n = *tile_count;
+  if (t == 0) *count = n;
+  if (t < n && t < bound) {
+    const int4 v = tiles[t];
+    int* o = out + int64_t(t) * 5;
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; o[4] = lora_ranks[v.w];
+  }
+}
+
+__global__ void zero_int_kernel(int* p) { *p = 0; }
+
+hipError_t launch_zero_int(int* p, hipStream_t st) {
+  hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_export_tiles(int method, const int* seg_indptr, const int* weight_indices,
+                               const int* lora_ranks, int G, int BM, int bound, int* out,
+                               int* count, int4* ws_tiles, int* ws_count, hipStream_t st) {
+  if (method == 0) {
+    hipLaunchKernelGGL(zero_int_kernel, dim3(1), dim3(1), 0, st, count);
+    hipLaunchKernelGGL((export_inline_tiles_kernel<256>), dim3(bound), dim3(256), 0, st,
+                       seg_indptr, weight_indices, lora_ranks, G, BM, out, count);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_schedule(seg_indptr, weight_indices, G, BM, ws_tiles, ws_count, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(export_list_tiles_kernel, dim3((bound + 255) / 256), dim3(256), 0, st,
+                     ws_tiles, ws_count, lora_ranks, bound, out, count);
+  return hipGetLastError();
+}
+
+}  // namespace lmx

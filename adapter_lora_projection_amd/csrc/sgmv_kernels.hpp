@@ -34,21 +34,28 @@ struct ExpandArgs {
   const int* tile_count;
   int64_t N, ldh, ldb, ldy;
   int S, R, G;
+  int BN;  // columns per workgroup block (a multiple of 64 * waves)
 };
 
 struct ShrinkPlan {
-  int variant;  // kernel shape, see shrink_plan_bm
-  int grid_x;   // tile-dimension bound ceil(T / BM) + G
+  int variant;   // kernel shape
+  int grid_x;    // tile-dimension bound ceil(T / BM) + G
+  bool aligned;  // x, A bases and row strides are 16-byte aligned
 };
 
 struct ExpandPlan {
   int variant;
   int grid_x;
+  bool aligned_b;  // h, B bases and row strides (and the slice width R) are 16-byte aligned
+  bool aligned_y;  // y base and row stride are 16-byte aligned
 };
 
-int shrink_plan_bm(int variant);
-int expand_plan_bm(int variant);
-int expand_plan_bn(int variant);
+int num_shrink_variants();
+int num_expand_variants();
+int shrink_plan_bm(int dtype, int variant);
+int expand_plan_bm(int dtype, int variant);
+int expand_plan_waves(int dtype, int variant);
+int expand_max_rank(int dtype);  // largest padded rank the expand kernels take
 
 hipError_t launch_shrink(int dtype, const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);
 hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);

@@ -1,0 +1,313 @@
+"""Benchmark: effective HBM bandwidth of the multi-adapter LoRA shrink+expand on one MI355X.
+
+Workload: the decode-QKV projection shape (bf16; 4 adapters of rank 16; K = 4096; three output
+slices of 4096, 1024 and 1024 columns; uniform-random segment lengths; random adapter order and
+token permutation; x ~ N(0,1), A, B ~ N(0,0.02), scale 2) at the nine token counts
+tok = 50, 128, 256, 512, 1024, 2048, 4096, 6144, 8192. One step = lora_shrink then lora_expand for
+every token count, all inputs resident in HBM. The step is captured once into a HIP graph and
+replayed; the nine cases (about 0.75 GB of distinct data) evict one another from L2 and the
+Infinity Cache between reuses, so every case streams from HBM.
+
+value = algorithmic bytes of one step / time of one step (GB/s), with algorithmic bytes counted
+per call as: x rows + valid rank rows of A of the adapters used + valid h entries (shrink);
+valid h entries + valid rank columns of B of the adapters used + y read and written (expand);
+plus the int32 metadata.
+
+The single adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4) is timed
+in the same run and reported in its own object when the library provides it.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def _kernel_source_sha() -> str:
+    d = os.path.join(ROOT, "adapter_lora_projection_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(c) -> dict:
+    """Algorithmic bytes and flops of one shrink and one expand call on case c."""
+    E = ESIZE[c.dtype]
+    lens = np.diff(c.seg_indptr.numpy()).astype(np.int64)
+    widx = c.weight_indices.numpy()
+    ranks = c.lora_ranks.numpy().astype(np.int64)
+    used = sorted({int(widx[g]) for g in range(len(widx)) if lens[g] > 0})
+    rows_r = int(sum(lens[g] * ranks[widx[g]] for g in range(len(widx))))  # sum_i r_a(i)
+    meta_s = 4 * (len(lens) + 1 + len(widx) + c.T + c.L)
+    meta_e = meta_s + 4 * (c.S + 1) + 4 * c.L
+    h_bytes = c.S * rows_r * E
+    shrink_b = c.T * c.K * E + sum(c.S * int(ranks[a]) * c.K * E for a in used) + h_bytes + meta_s
+    expand_b = h_bytes + sum(c.N * int(ranks[a]) * E for a in used) + 2 * c.T * c.N * E + meta_e
+    return {"shrink_bytes": shrink_b, "expand_bytes": expand_b,
+            "shrink_flops": 2 * c.S * rows_r * c.K, "expand_flops": 2 * c.N * rows_r}
+
+
+class SgmvCaseRun:
+    """Device buffers and pre-marshalled C-ABI argument tuples for one case."""
+
+    def __init__(self, c, lib, stream):
+        import torch
+
+        self.c = c
+        dt = {"f32": 0, "bf16": 1, "f16": 2}[c.dtype]
+        dev = "cuda"
+        self.d = {k: getattr(c, k).to(dev).contiguous() for k in
+                  ("slice_offsets", "seg_indptr", "weight_indices", "permutation", "lora_ranks",
+                   "scalings", "x", "A", "B", "y_in")}
+        d = self.d
+        self.h = torch.empty((c.T, c.S * c.R), dtype=d["x"].dtype, device=dev)
+        self.y = d["y_in"].clone()
+        ws_s = lib.lora_shrink_workspace_size(dt, c.T, c.K, c.S, c.R, c.G)
+        ws_e = lib.lora_expand_workspace_size(dt, c.T, c.S, c.R, c.G, c.N)
+        self.ws = torch.empty(max(ws_s, ws_e, 1), dtype=torch.uint8, device=dev)
+        p = lambda t: t.data_ptr()
+        self.shrink_args = (dt, c.T, c.K, c.S, c.R, c.L, c.G, p(d["x"]), c.K, p(d["A"]), c.K,
+                            p(d["seg_indptr"]), p(d["weight_indices"]), p(d["permutation"]),
+                            p(d["lora_ranks"]), p(self.h), c.S * c.R, p(self.ws), ws_s, stream)
+        self.expand_args = (dt, c.T, c.S, c.R, c.L, c.G, c.N, p(self.h), c.S * c.R, p(d["B"]), c.R,
+                            p(d["slice_offsets"]), p(d["seg_indptr"]), p(d["weight_indices"]),
+                            p(d["permutation"]), p(d["lora_ranks"]), p(d["scalings"]), p(self.y),
+                            c.N, p(self.ws), ws_e, stream)
+        self.alg = algorithmic(c)
+
+    def shrink(self, L):
+        st = L.lora_shrink(*self.shrink_args)
+        if st:
+            raise RuntimeError(f"lora_shrink status {st}")
+
+    def expand(self, L):
+        st = L.lora_expand(*self.expand_args)
+        if st:
+            raise RuntimeError(f"lora_expand status {st}")
+
+
+def cpu_baseline(seconds_cap: float = 30.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+    import oracle
+    import lora_inputs as li
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max((i["num_threads"] for i in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = 1
+    sample = (50, 128, 256, 512, 1024, 2048)
+    total_b = 0
+    total_t = 0.0
+    for tok in sample:
+        c = li.sweep_case(tok)
+        alg = algorithmic(c)
+        t0 = time.perf_counter()
+        h = oracle.shrink(c.x, c.A, c.seg_indptr, c.weight_indices, c.permutation, c.lora_ranks,
+                          c.S, c.R, "bf16")
+        oracle.expand(h, c.B, c.slice_offsets, c.seg_indptr, c.weight_indices, c.permutation,
+                      c.lora_ranks, c.scalings, c.y_in, c.R, "bf16")
+        total_t += time.perf_counter() - t0
+        total_b += alg["shrink_bytes"] + alg["expand_bytes"]
+        if total_t > seconds_cap:
+            break
+    cores = min(len(os.sched_getaffinity(0)), blas_threads)
+    return {"value": round(total_b / total_t / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one fp64 oracle shrink+expand pass at tok {list(sample)} of the same sweep "
+                      f"({total_t:.1f} s; BLAS threads {blas_threads})"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every step runs on a single MI355X).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}))
+        return 0
+
+    import lora_inputs as li
+    from adapter_lora_projection_amd import _lib
+
+    L = _lib.lib()  # raises if the HIP library is not built: there is no other path
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream().cuda_stream
+    runs = [SgmvCaseRun(li.sweep_case(t), L, stream) for t in li.SWEEP_TOKENS]
+    print(f"[bench] {len(runs)} cases resident on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    def step():
+        for r in runs:
+            r.shrink(L)
+            r.expand(L)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel breakdown (eager, events around every launch) -> dominant kernel
+    reps = 5
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in runs]
+    acc = np.zeros((len(runs), 2))
+    for _ in range(reps):
+        for i, r in enumerate(runs):
+            ev[i][0].record()
+            r.shrink(L)
+            ev[i][1].record()
+            r.expand(L)
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        for i in range(len(runs)):
+            acc[i, 0] += ev[i][0].elapsed_time(ev[i][1])
+            acc[i, 1] += ev[i][1].elapsed_time(ev[i][2])
+    acc /= reps  # ms
+    dom_i, dom_op = np.unravel_index(np.argmax(acc), acc.shape)
+    print(f"[bench] breakdown done; dominant kernel: {'shrink' if dom_op == 0 else 'expand'} "
+          f"tok={runs[dom_i].c.T}", file=sys.stderr, flush=True)
+
+    # the timed region: K steps
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()  # warm on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=cap_stream):
+            # the binding's stream argument is baked into the argument tuples: rebuild them for
+            # the capture stream so every launch is recorded
+            for r in runs:
+                a = list(r.shrink_args); a[-1] = cap_stream.cuda_stream
+                L.lora_shrink(*a)
+                b = list(r.expand_args); b[-1] = cap_stream.cuda_stream
+                L.lora_expand(*b)
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # dominant kernel's launches, live, with events on the stream it runs on
+    dr = runs[dom_i]
+    fn = dr.shrink if dom_op == 0 else dr.expand
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in kev:
+        a.record()
+        fn(L)
+        b.record()
+    torch.cuda.synchronize()
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+    dom_bytes = dr.alg["shrink_bytes"] if dom_op == 0 else dr.alg["expand_bytes"]
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    step_bytes = sum(r.alg["shrink_bytes"] + r.alg["expand_bytes"] for r in runs)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    per_case = []
+    for i, r in enumerate(runs):
+        b = r.alg["shrink_bytes"] + r.alg["expand_bytes"]
+        us = (acc[i, 0] + acc[i, 1]) * 1e3
+        per_case.append({"tok": r.c.T, "shrink_us": round(acc[i, 0] * 1e3, 2),
+                         "expand_us": round(acc[i, 1] * 1e3, 2),
+                         "pair_gbps": round(b / (us * 1e-6) / 1e9, 1),
+                         "pair_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+    mean_case = float(np.mean([p["pair_gbps"] for p in per_case]))
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    dom_name = f"{'shrink' if dom_op == 0 else 'expand'}_tok{dr.c.T}"
+    if os.path.exists(tpath):
+        try:
+            tj = json.load(open(tpath))
+            ent = tj.get("kernels", {}).get(dom_name)
+            if ent and tj.get("source_sha") == _kernel_source_sha():
+                traffic = ent["hbm_bytes_per_launch"]
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": "effective HBM GB/s (and % of peak) for LoRA shrink+expand, tok 50-8192",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the decode-QKV workload)",
+        "config": {"workload": "decode-QKV bf16 LoRA shrink+expand, 4 adapters r16, K=4096, "
+                               "N=4096+1024+1024, tok sweep 50..8192 (9 cases per step)",
+                   "tokens_per_step": int(sum(li.SWEEP_TOKENS)), "bytes_per_step": int(step_bytes),
+                   "timing": "graph replay" if graph is not None else "eager",
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+                   "mean_case_gbps": round(mean_case, 1),
+                   "per_case": per_case},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": dom_name, "avg_launch_us": round(dom_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(dom_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

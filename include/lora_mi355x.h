@@ -111,7 +111,8 @@ size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_
  * with an fp32 accumulation and one rounding to `dtype` per stored element. Entries of y outside
  * the slices, and every row of a rank-0 adapter, are neither read nor written.
  *
- *   T, S, R, L, G  as for lora_shrink.
+ *   T, S, L, G     as for lora_shrink.
+ *   R              padded rank, 1 <= R <= 64 (bf16, fp16) or 32 (fp32).
  *   N              columns covered by the slices; slice_offsets[S] == N.
  *   h              device [T][ldh], ldh >= S*R, sorted order (the output of lora_shrink).
  *   w_b            device [L*N][ldb], ldb >= R: row a*N + n holds B[a][n][:]. Entries with
@@ -154,7 +155,8 @@ lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method
 
 /*
  * lora_tuning_override -- pins the kernel shape the library picks for an operation, for
- * measurement sweeps. op 0 = shrink (variant 0..2), op 1 = expand (variant 0..1); variant -1
+ * measurement sweeps. op 0 = shrink (variant 0..3), op 1 = expand (variant 0..2), op 2 = expand
+ * columns per workgroup (rounded up to the kernel's chunk multiple); -1 or any other value
  * restores the automatic choice. Process-wide, not thread-safe; results are identical for every
  * variant up to fp32 summation order.
  */

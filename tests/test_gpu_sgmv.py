@@ -95,8 +95,8 @@ def test_sweep(T):
 
 # ------------------------------------------------------------------ every kernel shape
 
-@pytest.mark.parametrize("sv", [0, 1, 2])
-@pytest.mark.parametrize("ev", [0, 1])
+@pytest.mark.parametrize("sv", range(4))
+@pytest.mark.parametrize("ev", range(3))
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_variants_small(sv, ev, dtype):
     """Several tiles per segment plus ragged tails, odd ranks, K tail, unaligned slices."""
