@@ -7,6 +7,6 @@ stream. Every step runs in the HIP library; there is no CPU path.
 """
 
 from ._lib import LoraError, lib, lora_version
-from .ops import expand, schedule_tiles, shrink
+from .ops import expand, mlp_fused, schedule_tiles, shrink
 
-__all__ = ["LoraError", "lib", "lora_version", "shrink", "expand", "schedule_tiles"]
+__all__ = ["LoraError", "lib", "lora_version", "shrink", "expand", "schedule_tiles", "mlp_fused"]

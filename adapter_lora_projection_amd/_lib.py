@@ -30,6 +30,9 @@ SIGNATURES = {
     "lora_schedule_tiles": (_i32, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                    _sz, _vp]),
     "lora_tuning_override": (None, [_i32, _i32]),
+    "lora_mlp_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
+    "lora_mlp_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
 }
 
 
@@ -109,6 +112,18 @@ def lora_schedule_tiles(T, G, BM, method, seg_indptr, weight_indices, lora_ranks
                                    _p(lora_ranks), _p(tiles), max_tiles, _p(count), _p(workspace),
                                    workspace_bytes, stream)
     _check("lora_schedule_tiles", st)
+
+
+def lora_mlp_fused(dtype, M, H, I, r, scale, x, ldx, w_gate, w_up, w_down, a_gate, b_gate, a_up,
+                   b_up, a_down, b_down, out, ldo, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_mlp_fused(dtype, M, H, I, r, scale, _p(x), ldx, _p(w_gate), _p(w_up),
+                              _p(w_down), _p(a_gate), _p(b_gate), _p(a_up), _p(b_up), _p(a_down),
+                              _p(b_down), _p(out), ldo, _p(workspace), workspace_bytes, stream)
+    _check("lora_mlp_fused", st)
+
+
+def lora_mlp_workspace_size(dtype, M, H, I, r) -> int:
+    return int(lib().lora_mlp_workspace_size(dtype, M, H, I, r))
 
 
 def lora_tuning_override(op: int, variant: int) -> None:

@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "../../include/lora_mi355x.h"
+#include "mlp_kernels.hpp"
 #include "sgmv_kernels.hpp"
 
 namespace {
@@ -60,6 +61,27 @@ size_t schedule_bytes(int64_t T, int32_t G, int bm) {
 }
 
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_EHIP; }
+
+// Workspace of the fused MLP: byte offsets of its five sections (256-byte aligned).
+struct MlpLayout {
+  int64_t rp;  // rank rounded up to 32
+  size_t xa_gu, lb_gu, hmid, xa_d, lb_d, total;
+};
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
+  MlpLayout L{};
+  L.rp = cdiv(r, 32) * 32;
+  size_t off = 0;
+  L.xa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
+  L.lb_gu = off; off += align256(size_t(2 * I) * 2 * L.rp * 2);
+  L.hmid = off; off += align256(size_t(M) * I * 2);
+  L.xa_d = off; off += align256(size_t(M) * L.rp * 2);
+  L.lb_d = off; off += align256(size_t(H) * L.rp * 2);
+  L.total = off;
+  return L;
+}
 
 }  // namespace
 
@@ -124,7 +146,7 @@ lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   lmx::ShrinkArgs a{};
   a.x = x; a.w_a = w_a; a.seg_indptr = seg_indptr; a.weight_indices = weight_indices;
   a.permutation = permutation; a.lora_ranks = lora_ranks; a.h = h;
-  a.K = K; a.ldx = ldx; a.lda = lda; a.ldh = ldh; a.S = S; a.R = R; a.G = G;
+  a.K = K; a.ldx = ldx; a.lda = lda; a.ldh = ldh; a.S = S; a.R = R; a.G = G; a.T = int(T);
   if (need > 0) {
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + 256);
     int* count = static_cast<int*>(workspace);
@@ -183,6 +205,87 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
   const bool aligned_y = al16(y) && (ldy * e) % 16 == 0;
   lmx::ExpandPlan plan{variant, int(bound), aligned_b, aligned_y};
   return hip_status(lmx::launch_expand(int(dtype), a, plan, st));
+}
+
+size_t lora_mlp_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r) {
+  (void)dtype;
+  if (M <= 0 || H <= 0 || I <= 0 || r <= 0) return 0;
+  return mlp_layout(M, H, I, r).total;
+}
+
+lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r,
+                           float scale, const void* x, int64_t ldx, const void* w_gate,
+                           const void* w_up, const void* w_down, const void* a_gate,
+                           const void* b_gate, const void* a_up, const void* b_up,
+                           const void* a_down, const void* b_down, void* out, int64_t ldo,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != LORA_BF16) return valid_dtype(dtype) ? LORA_EUNSUPPORTED : LORA_EUNSUPPORTED;
+  if (M < 0 || H < 1 || I < 1 || r < 1) return LORA_EINVAL;
+  if (r > 64 || H % 32 != 0 || I % 32 != 0) return LORA_EUNSUPPORTED;
+  if (M >= INT_MAX || H >= INT_MAX / 4 || I >= INT_MAX / 4) return LORA_EUNSUPPORTED;
+  if (M == 0) return LORA_OK;
+  if (!x || !w_gate || !w_up || !w_down || !a_gate || !b_gate || !a_up || !b_up || !a_down ||
+      !b_down || !out)
+    return LORA_EINVAL;
+  if (ldx < H || ldo < H) return LORA_EINVAL;
+  if (!al16(x) || (ldx * 2) % 16 != 0 || !al16(w_gate) || !al16(w_up) || !al16(w_down))
+    return LORA_EUNSUPPORTED;
+  const MlpLayout L = mlp_layout(M, H, I, r);
+  if (workspace == nullptr || workspace_bytes < L.total || !al16(workspace)) return LORA_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* xa_gu = reinterpret_cast<uint16_t*>(ws + L.xa_gu);
+  uint16_t* lb_gu = reinterpret_cast<uint16_t*>(ws + L.lb_gu);
+  uint16_t* hmid = reinterpret_cast<uint16_t*>(ws + L.hmid);
+  uint16_t* xa_d = reinterpret_cast<uint16_t*>(ws + L.xa_d);
+  uint16_t* lb_d = reinterpret_cast<uint16_t*>(ws + L.lb_d);
+  const int64_t rp = L.rp;
+  auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  hipError_t e;
+  // 1. scaled LoRA-B operands: [s B_g | 0] and [0 | s B_u] stacked, and s B_d
+  if ((e = lmx::launch_scale_lora_b(u16(b_gate), r, int(I), r, scale, lb_gu, 2 * rp, 0, st)) != hipSuccess) return LORA_EHIP;
+  if ((e = lmx::launch_scale_lora_b(u16(b_up), r, int(I), r, scale, lb_gu + I * 2 * rp, 2 * rp, int(rp), st)) != hipSuccess) return LORA_EHIP;
+  if ((e = lmx::launch_scale_lora_b(u16(b_down), r, int(H), r, scale, lb_d, rp, 0, st)) != hipSuccess) return LORA_EHIP;
+  // 2. [xa_g | xa_u] = round(x [A_g; A_u]^T), ranks padded with zeros to rp
+  {
+    lmx::ShrinkArgs a{};
+    a.x = x; a.ldx = ldx; a.K = H; a.S = 2; a.R = int(rp); a.G = 1; a.T = int(M);
+    a.dense_rank = r; a.w_a_slice[0] = a_gate; a.w_a_slice[1] = a_up; a.w_a = a_gate; a.lda = H;
+    a.h = xa_gu; a.ldh = 2 * rp;
+    const int v = shrink_variant(M, 2, int(rp));
+    const int bm = lmx::shrink_plan_bm(LORA_BF16, v);
+    lmx::ShrinkPlan plan{v, int(cdiv(M, bm)), al16(x) && al16(a_gate) && al16(a_up) && (ldx * 2) % 16 == 0 && (H * 2) % 16 == 0};
+    if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
+  }
+  // 3. hmid = round(silu(x W_g^T + s xa_g B_g^T) * (x W_u^T + s xa_u B_u^T))
+  {
+    lmx::GemmArgs g{};
+    g.A = u16(x); g.lda = ldx; g.W0 = u16(w_gate); g.W1 = u16(w_up); g.ldw = H;
+    g.A2 = xa_gu; g.lda2 = 2 * rp; g.B2 = lb_gu; g.ldb2 = 2 * rp;
+    g.C = hmid; g.ldc = I; g.M = int(M); g.N = int(I); g.K = int(H); g.K2 = int(2 * rp);
+    if ((e = lmx::launch_gemm_lora(g, true, st)) != hipSuccess) return LORA_EHIP;
+  }
+  // 4. xa_d = round(hmid A_d^T)
+  {
+    lmx::ShrinkArgs a{};
+    a.x = hmid; a.ldx = I; a.K = I; a.S = 1; a.R = int(rp); a.G = 1; a.T = int(M);
+    a.dense_rank = r; a.w_a_slice[0] = a_down; a.w_a = a_down; a.lda = I;
+    a.h = xa_d; a.ldh = rp;
+    const int v = shrink_variant(M, 1, int(rp));
+    const int bm = lmx::shrink_plan_bm(LORA_BF16, v);
+    lmx::ShrinkPlan plan{v, int(cdiv(M, bm)), al16(a_down) && (I * 2) % 16 == 0};
+    if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
+  }
+  // 5. out = round(hmid W_d^T + s xa_d B_d^T)
+  {
+    lmx::GemmArgs g{};
+    g.A = hmid; g.lda = I; g.W0 = u16(w_down); g.W1 = u16(w_down); g.ldw = I;
+    g.A2 = xa_d; g.lda2 = rp; g.B2 = lb_d; g.ldb2 = rp;
+    g.C = static_cast<uint16_t*>(out); g.ldc = ldo; g.M = int(M); g.N = int(H); g.K = int(I);
+    g.K2 = int(rp);
+    if ((e = lmx::launch_gemm_lora(g, false, st)) != hipSuccess) return LORA_EHIP;
+  }
+  return LORA_OK;
 }
 
 lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method,

@@ -1,0 +1,278 @@
+// Single-adapter LoRA MLP with fused SwiGLU for gfx950 ("Add optional fast lora path for
+// qwen2/qwen3 on npu", What this PR does: the Qwen MLP forward with LoRA on the gate, up and down
+// projections and a fused SwiGLU; Compatibility checks: dropout 0, one adapter, no bias).
+//
+// out = round(hmid W_d^T + s * xa_d B_d^T),   hmid = round(silu(g) * u),
+// g = x W_g^T + s * xa_g B_g^T,  u = x W_u^T + s * xa_u B_u^T,  xa_* = round(x A_*^T)
+//
+// Launches on the caller's stream:
+//   1. the scaled LoRA-B operands s*B_g, s*B_u, s*B_d in bf16, zero padded (small; exact when s
+//      is a power of two, as alpha / rank usually is);
+//   2. LoRA-A products of x for gate and up (the dense mode of the shrink kernel, both slices in
+//      one pass over x) -> xa_gu [M][2*rp] = [xa_g | xa_u] (rp = rank rounded up to 32);
+//   3. gate/up GEMM over K = H + 2*rp: the last 2*rp reduction columns are [xa_g | xa_u] against
+//      [s*B_g | 0] for gate rows and [0 | s*B_u] for up rows, so the LoRA term accumulates with
+//      the base product. One workgroup computes 256 rows x 128 output columns of BOTH
+//      projections (its B tile holds the 128 gate rows then the 128 up rows), so every lane
+//      holds g and u of the same outputs and the epilogue stores hmid = silu(g) * u in bf16;
+//   4. LoRA-A product of hmid for down -> xa_d [M][rp];
+//   5. down GEMM over K = I + rp -> out.
+//
+// GEMM main loop: 256x256x64 block tiles, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16, both
+// operands K-contiguous ([rows][K] row-major, as nn.Linear stores them) staged through LDS with
+// a 72-element row pitch (bank-conflict free 16-byte fragment reads), double buffered: the next
+// tile's global loads are in flight while the current tile feeds the MFMAs.
+#include "device_common.hpp"
+#include "mlp_kernels.hpp"
+#include "sgmv_kernels.hpp"
+
+#include <type_traits>
+
+namespace lmx {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int kBM = 256;  // rows of A per block
+constexpr int kBR = 256;  // rows of W per block (B operand)
+constexpr int kBK = 32;   // K per stage (64 bytes per row)
+constexpr int kStages = 4;
+constexpr int kAhead = kStages - 1;              // stages in flight
+constexpr int kStageElems = (kBM + kBR) * kBK;  // elements per stage (32 KiB)
+
+__device__ __forceinline__ f32x16_t mma32(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// LDS tiles hold rows of 64 bytes (4 chunks of 16 bytes) with the chunk index XOR-swizzled by
+// (row / 4) % 4, so that the 16 lanes of each 16-byte read phase hit 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+// One direct-to-LDS 16-byte load per lane: the wave writes 1 KiB of LDS at byte address
+// `lds_addr` (wave-uniform; lane L at +16 L), i.e. 16 rows x 64 bytes. Issued from an asm block
+// with no register outputs: the compiler does not track it, so the pipeline's waits on these
+// loads are explicit (s_waitcnt vmcnt); the compiler's own waits on other loads stay correct
+// because the counter completes in order and can only over-wait.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));
+}
+
+}  // namespace
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
+  // One LDS array per pipeline stage.
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[kStageElems];
+  auto stage = [&](auto sc) -> uint16_t* {
+    constexpr int s = decltype(sc)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int wi = w >> 1, wj = w & 1;  // wave row / column in the 2x2 wave grid
+  // block coordinates: column blocks walk fastest inside groups of 8 row blocks
+  const int nbn = SWIGLU ? (p.N + 127) / 128 : (p.N + 255) / 256;
+  const int nbm = (p.M + kBM - 1) / kBM;
+  const int group = int(blockIdx.x) / (8 * nbn);
+  const int first_m = group * 8;
+  const int gsize = min(nbm - first_m, 8);
+  const int local = int(blockIdx.x) - group * 8 * nbn;
+  const int bm = first_m + local % gsize;
+  const int bn = local / gsize;
+  const int m0 = bm * kBM;
+  const int n0 = SWIGLU ? bn * 128 : bn * 256;
+
+  // DMA mapping: wave w fills tile rows [64 w, 64 w + 64) of A and of W, 16 rows per
+  // instruction; lane L covers row 16 i + L / 4 and LDS slot L % 4, which holds global chunk
+  // swz(row, slot). Stages past K read the LoRA columns (A2, B2).
+  const int drow = lane >> 2, dslot = lane & 3;
+  const int nk1 = p.K / kBK;
+  const int nk = nk1 + p.K2 / kBK;
+  // kernel arguments as values (selecting between argument fields per lane would load them
+  // through vector memory)
+  const uint16_t* const pA = p.A;
+  const uint16_t* const pA2 = p.A2;
+  const uint16_t* const pW0 = p.W0;
+  const uint16_t* const pW1 = p.W1;
+  const uint16_t* const pB2 = p.B2;
+  const int64_t plda = p.lda, plda2 = p.lda2, pldw = p.ldw, pldb2 = p.ldb2;
+  const int pM = p.M, pN = p.N;
+  auto issue = [&](auto sc, int kt) {
+    uint16_t* sa = stage(sc);
+    uint16_t* sb = sa + kBM * kBK;
+    const bool lora = kt >= nk1;
+    const int koff = (lora ? kt - nk1 : kt) * kBK;
+    const uint16_t* abase = lora ? pA2 : pA;
+    const int64_t lda = lora ? plda2 : plda;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = w * 64 + i * 16 + drow;
+      const int kk = koff + swz(row, dslot) * 8;
+      dma16(abase + int64_t(min(m0 + row, pM - 1)) * lda + kk,
+            lds_addr(sa + (w * 64 + i * 16) * kBK));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = w * 64 + i * 16 + drow;
+      const int kk = koff + swz(row, dslot) * 8;
+      const uint16_t* wsrc;
+      if (SWIGLU) {
+        const int n = min(n0 + (row & 127), pN - 1);
+        const bool up = row >= 128;  // uniform per instruction: 16 rows never straddle 128
+        wsrc = lora ? pB2 + int64_t(up ? pN + n : n) * pldb2 + kk
+                    : (up ? pW1 : pW0) + int64_t(n) * pldw + kk;
+      } else {
+        const int n = min(n0 + row, pN - 1);
+        wsrc = lora ? pB2 + int64_t(n) * pldb2 + kk : pW0 + int64_t(n) * pldw + kk;
+      }
+      dma16(wsrc, lds_addr(sb + (w * 64 + i * 16) * kBK));
+    }
+  };
+
+  // this wave's B rows inside the block tile, per 32-row column block
+  int brow0[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    brow0[cb] = SWIGLU ? (cb < 2 ? wj * 64 + cb * 32 : 128 + wj * 64 + (cb - 2) * 32)
+                       : wj * 128 + cb * 32;
+  const int lr = lane & 31, lc = lane >> 5;  // MFMA operand row and chunk-in-slice
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x16_t{};
+
+  // prologue: kAhead stages in flight
+  if (0 < nk) issue(std::integral_constant<int, 0>{}, 0);
+  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
+  if (2 < nk) issue(std::integral_constant<int, 2>{}, 2);
+
+  // main loop, unrolled over the 4 stages so every LDS reference names its stage array
+  auto step = [&](auto sc, int kt) {
+    constexpr int s = decltype(sc)::value;
+    // wait for this stage's loads (younger stages stay in flight), then publish to all waves.
+    // s_waitcnt immediate: vmcnt bits 3:0 (low) and 15:14 (high), expcnt 6:4 and lgkmcnt 11:8
+    // left at their maxima. 8 loads per stage and wave.
+    const int younger = min(nk - 1 - kt, kAhead - 1);
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);       // vmcnt(16)
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+    __syncthreads();
+    if (kt + kAhead < nk) issue(std::integral_constant<int, (s + kAhead) % kStages>{}, kt + kAhead);
+    const uint16_t* sa = stage(sc);
+    const uint16_t* sb = sa + kBM * kBK;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int chunk = ks * 2 + lc;
+      uint4 fa[4], fb[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int row = wi * 128 + rb * 32 + lr;
+        fa[rb] = *reinterpret_cast<const uint4*>(sa + row * kBK + swz(row, chunk) * 8);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int row = brow0[cb] + lr;
+        fb[cb] = *reinterpret_cast<const uint4*>(sb + row * kBK + swz(row, chunk) * 8);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mma32(fa[rb], fb[cb], acc[rb][cb]);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += kStages) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
+    if (kt + 3 < nk) step(std::integral_constant<int, 3>{}, kt + 3);
+  }
+
+  // epilogue. Output layout of a 32x32 block: lane l holds column l % 32 and rows
+  // 8 * (v / 4) + 4 * (l / 32) + v % 4 for registers v = 0..15.
+  const int rq = lc * 4;
+  const int col_base = SWIGLU ? n0 + wj * 64 : n0 + wj * 128;
+  if constexpr (SWIGLU) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int rbase = m0 + wi * 128 + rb * 32;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int n = col_base + cb * 32 + lr;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = rbase + 8 * (v >> 2) + rq + (v & 3);
+          const float g = acc[rb][cb][v], u = acc[rb][cb + 2][v];
+          if (row < p.M) p.C[int64_t(row) * p.ldc + n] = Traits<DT_BF16>::from_f32(silu(g) * u);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int rbase = m0 + wi * 128 + rb * 32;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int n = col_base + cb * 32 + lr;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = rbase + 8 * (v >> 2) + rq + (v & 3);
+          if (row < p.M) p.C[int64_t(row) * p.ldc + n] = Traits<DT_BF16>::from_f32(acc[rb][cb][v]);
+        }
+      }
+    }
+  }
+}
+
+__global__ void scale_lora_b_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int n, int r,
+                                    float scale, uint16_t* __restrict__ dst, int64_t ld_dst,
+                                    int col0) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(n) * ld_dst) return;
+  const int row = int(i / ld_dst), j = int(i % ld_dst) - col0;
+  uint16_t v = 0;
+  if (j >= 0 && j < r)
+    v = Traits<DT_BF16>::from_f32(Traits<DT_BF16>::to_f32(src[int64_t(row) * ld_src + j]) * scale);
+  dst[i] = v;
+}
+
+hipError_t launch_scale_lora_b(const uint16_t* src, int64_t ld_src, int n, int r, float scale,
+                               uint16_t* dst, int64_t ld_dst, int col0, hipStream_t st) {
+  const int64_t total = int64_t(n) * ld_dst;
+  hipLaunchKernelGGL(scale_lora_b_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                     src, ld_src, n, r, scale, dst, ld_dst, col0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_lora(const GemmArgs& a, bool swiglu, hipStream_t st) {
+  const int nbm = (a.M + kBM - 1) / kBM;
+  const int nbn = swiglu ? (a.N + 127) / 128 : (a.N + 255) / 256;
+  dim3 grid(nbm * nbn);
+  if (swiglu)
+    hipLaunchKernelGGL(gemm_lora_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(gemm_lora_kernel<false>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace lmx

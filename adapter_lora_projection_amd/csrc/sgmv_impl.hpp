@@ -48,9 +48,18 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
   __shared__ int s_scan[NW];
   __shared__ f32x4_t s_red[(NW > 1) ? NW : 1][CB * MT][64];
 
-  get_tile<NT>(p.seg_indptr, p.weight_indices, p.lora_ranks, nullptr, p.G, BM, p.tiles,
-               p.tile_count, int(blockIdx.x), &s_tile, s_scan);
-  const Tile tile = s_tile;
+  Tile tile;
+  if (p.seg_indptr != nullptr) {
+    get_tile<NT>(p.seg_indptr, p.weight_indices, p.lora_ranks, nullptr, p.G, BM, p.tiles,
+                 p.tile_count, int(blockIdx.x), &s_tile, s_scan);
+    tile = s_tile;
+  } else {  // dense: one segment over all rows
+    tile.g = int(blockIdx.x) * BM < p.T ? 0 : -1;
+    tile.m0 = int(blockIdx.x) * BM;
+    tile.mlen = min(BM, p.T - tile.m0);
+    tile.a = 0;
+    tile.r = p.dense_rank;
+  }
   if (tile.g < 0) return;
 
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -72,7 +81,8 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + li;
     tok_ok[mt] = m < tile.mlen;
-    const int tok = p.permutation[tile.m0 + (tok_ok[mt] ? m : 0)];
+    const int pos = tile.m0 + (tok_ok[mt] ? m : 0);
+    const int tok = p.permutation != nullptr ? p.permutation[pos] : pos;
     xrow[mt] = x + int64_t(tok) * p.ldx;
   }
   const S* arow[CB];
@@ -85,7 +95,11 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
     const int j = 16 * b + li;
     col_ok[cb] = (blk < nblk) && (j < r);
     any_col |= (blk < nblk) && (16 * b < r);
-    arow[cb] = wa + (int64_t(a * p.S + (blk < nblk ? s : 0)) * p.R + (col_ok[cb] ? j : 0)) * p.lda;
+    const int ss = blk < nblk ? s : 0;
+    const S* slice_base = (ss < 4 && p.w_a_slice[ss] != nullptr)
+                              ? reinterpret_cast<const S*>(p.w_a_slice[ss])
+                              : wa + int64_t(a * p.S + ss) * p.R * p.lda;
+    arow[cb] = slice_base + int64_t(col_ok[cb] ? j : 0) * p.lda;
   }
 
   f32x4_t acc[CB][MT];

@@ -18,6 +18,12 @@ struct ShrinkArgs {
   const int* tile_count;  // its length (device), when tiles is non-null
   int64_t K, ldx, lda, ldh;
   int S, R, G;
+  // Internal dense mode (used by the fused MLP): seg_indptr == nullptr means one segment over
+  // all T rows with adapter 0 of rank `dense_rank`; permutation == nullptr means identity; a
+  // non-null w_a_slice[s] replaces the stacked layout for slice s (R rows of stride lda).
+  int T;
+  int dense_rank;
+  const void* w_a_slice[4];
 };
 
 struct ExpandArgs {

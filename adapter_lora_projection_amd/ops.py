@@ -129,3 +129,29 @@ def schedule_tiles(T: int, seg_indptr, weight_indices, lora_ranks, BM: int, meth
                              max(bound, 1), count, ws, nbytes if ws is not None else 0, _stream())
     n = int(count.item())
     return tiles[:n].clone()
+
+
+def mlp_fused(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_down, scale: float,
+              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """out = down(silu(gate(x)) * up(x)) with LoRA on all three projections (``lora_mlp_fused``).
+    x: [M][H] bf16; w_gate, w_up: [I][H]; w_down: [H][I]; a_*: [r][in]; b_*: [out][r]."""
+    _dev(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_down, out, workspace)
+    M, H = x.shape
+    I = w_gate.shape[0]
+    r = a_gate.shape[0]
+    for t, shape, name in ((w_gate, (I, H), "w_gate"), (w_up, (I, H), "w_up"), (w_down, (H, I), "w_down"),
+                           (a_gate, (r, H), "a_gate"), (a_up, (r, H), "a_up"), (a_down, (r, I), "a_down"),
+                           (b_gate, (I, r), "b_gate"), (b_up, (I, r), "b_up"), (b_down, (H, r), "b_down")):
+        if tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+    ldx = _rows(x, "x")
+    if out is None:
+        out = torch.empty((M, H), dtype=x.dtype, device=x.device)
+    ldo = _rows(out, "out")
+    nbytes = _lib.lora_mlp_workspace_size(_lib.LORA_BF16, M, H, I, r)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _lib.lora_mlp_fused(_lib.LORA_BF16, M, H, I, r, float(scale), x, ldx, w_gate, w_up, w_down,
+                        a_gate, b_gate, a_up, b_up, a_down, b_down, out, ldo, workspace,
+                        workspace.numel(), _stream())
+    return out

@@ -133,6 +133,39 @@ size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_
                                   int64_t N);
 
 /*
+ * lora_mlp_fused -- single-adapter LoRA MLP with fused SwiGLU (bf16).
+ *
+ *   out = round( hmid W_d^T + scale * xa_d B_d^T ),      xa_d = round( hmid A_d^T ),
+ *   hmid = round( silu(g) * u ),  silu(z) = z / (1 + exp(-z)),
+ *   g = x W_g^T + scale * xa_g B_g^T,   u = x W_u^T + scale * xa_u B_u^T,
+ *   xa_g = round( x A_g^T ),  xa_u = round( x A_u^T ),
+ * with fp32 accumulation and round-to-nearest-even to bf16 at exactly the stored tensors named
+ * (xa_*, hmid, out). The scale multiplies the LoRA-B weights in bf16; this is exact for a
+ * power-of-two scale (alpha / rank usually is), otherwise s*B_* carries one extra rounding.
+ * Dropout 0, no bias, unmerged weights: the conditions of the fast path this implements.
+ *
+ *   dtype        LORA_BF16 only (others: LORA_EUNSUPPORTED).
+ *   M, H, I      tokens, hidden size, intermediate size; H and I multiples of 32; M == 0 no-op.
+ *   r            LoRA rank, 1 <= r <= 64.
+ *   x            device [M][ldx], ldx >= H, 16-byte aligned rows.
+ *   w_gate, w_up device [I][H] contiguous (nn.Linear layout), 16-byte aligned.
+ *   w_down       device [H][I] contiguous, 16-byte aligned.
+ *   a_gate, a_up device [r][H]; b_gate, b_up device [I][r]; a_down device [r][I];
+ *   b_down       device [H][r]; all contiguous, any alignment.
+ *   out          device [M][ldo], ldo >= H; written, not read.
+ *   workspace    device, >= lora_mlp_workspace_size(...) bytes, 16-byte aligned (holds hmid:
+ *                M*I bf16, plus small LoRA buffers). Contents undefined afterwards.
+ */
+lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r,
+                           float scale, const void* x, int64_t ldx, const void* w_gate,
+                           const void* w_up, const void* w_down, const void* a_gate,
+                           const void* b_gate, const void* a_up, const void* b_up,
+                           const void* a_down, const void* b_down, void* out, int64_t ldo,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+size_t lora_mlp_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r);
+
+/*
  * lora_schedule_tiles -- the segment schedule the compute kernels use, exported for checking.
  *
  * Each non-empty segment g is cut into row tiles of at most BM sorted positions starting at

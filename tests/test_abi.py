@@ -108,3 +108,37 @@ def test_schedule_host_validation():
     assert L.lora_schedule_tiles(10, 2, 4, 2, 1, 1, 1, 1, 100, 1, None, 0, None) == _lib.LORA_EINVAL
     assert L.lora_schedule_tiles(10, 2, 4, 0, 1, 1, 1, 1, 4, 1, None, 0, None) == _lib.LORA_EINVAL
     assert L.lora_schedule_tiles(10, 2, 4, 1, 1, 1, 1, 1, 100, 1, None, 0, None) == _lib.LORA_EWORKSPACE
+
+
+def _mlp(**kw):
+    args = dict(dtype=1, M=8, H=64, I=96, r=16, scale=2.0, x=0x1000, ldx=64, w_gate=0x2000, w_up=0x3000,
+                w_down=0x4000, a_gate=0x5000, b_gate=0x6000, a_up=0x7000, b_up=0x8000, a_down=0x9000,
+                b_down=0xA000, out=0xB000, ldo=64, workspace=0x100000, workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return _lib.lib().lora_mlp_fused(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), _lib.LORA_EUNSUPPORTED),
+    (dict(dtype=2), _lib.LORA_EUNSUPPORTED),
+    (dict(H=48, ldx=48, ldo=48), _lib.LORA_EUNSUPPORTED),
+    (dict(I=100), _lib.LORA_EUNSUPPORTED),
+    (dict(r=65), _lib.LORA_EUNSUPPORTED),
+    (dict(r=0), _lib.LORA_EINVAL),
+    (dict(M=-1), _lib.LORA_EINVAL),
+    (dict(x=None), _lib.LORA_EINVAL),
+    (dict(b_down=None), _lib.LORA_EINVAL),
+    (dict(ldx=32), _lib.LORA_EINVAL),
+    (dict(x=0x1002), _lib.LORA_EUNSUPPORTED),
+    (dict(workspace=None), _lib.LORA_EWORKSPACE),
+    (dict(workspace_bytes=1024), _lib.LORA_EWORKSPACE),
+    (dict(M=0, x=None, out=None), _lib.LORA_OK),
+])
+def test_mlp_host_validation(kw, code):
+    assert _mlp(**kw) == code
+
+
+def test_mlp_workspace_size_covers_hmid():
+    M, H, I = 4096, 4096, 12288
+    n = _lib.lora_mlp_workspace_size(1, M, H, I, 16)
+    assert n >= M * I * 2 and n < M * I * 2 + 64 * (1 << 20)
