@@ -18,10 +18,10 @@
 //   4. LoRA-A product of hmid for down -> xa_d [M][rp];
 //   5. down GEMM over K = I + rp -> out.
 //
-// GEMM main loop: 256x256x64 block tiles, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16, both
-// operands K-contiguous ([rows][K] row-major, as nn.Linear stores them) staged through LDS with
-// a 72-element row pitch (bank-conflict free 16-byte fragment reads), double buffered: the next
-// tile's global loads are in flight while the current tile feeds the MFMAs.
+// GEMM main loop: 256x256x32 block stages, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16, both
+// operands K-contiguous ([rows][K] row-major, as nn.Linear stores them) loaded straight into
+// LDS (global_load_lds_dwordx4) four stages deep, with XOR-swizzled 64-byte rows so 16-byte
+// fragment reads are bank-conflict free; fragment reads of the next k slice overlap the MFMAs.
 #include "device_common.hpp"
 #include "mlp_kernels.hpp"
 #include "sgmv_kernels.hpp"
@@ -37,8 +37,7 @@ namespace {
 constexpr int kBM = 256;  // rows of A per block
 constexpr int kBR = 256;  // rows of W per block (B operand)
 constexpr int kBK = 32;   // K per stage (64 bytes per row)
-constexpr int kStages = 4;
-constexpr int kAhead = kStages - 1;              // stages in flight
+constexpr int kStages = 4;                       // LDS buffers, all in flight
 constexpr int kStageElems = (kBM + kBR) * kBK;  // elements per stage (32 KiB)
 
 __device__ __forceinline__ f32x16_t mma32(uint4 a, uint4 b, f32x16_t c) {
@@ -87,15 +86,27 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int wi = w >> 1, wj = w & 1;  // wave row / column in the 2x2 wave grid
-  // block coordinates: column blocks walk fastest inside groups of 8 row blocks
+  // Block coordinates. Workgroup i runs on XCD i % 8. When the block grid tiles into 16 x 16
+  // super-tiles, the 32 workgroups an XCD runs together form a 4 x 8 sub-grid of one
+  // super-tile, so each K slice of an A tile is read by 8 of its CUs and each slice of a W tile
+  // by 4 out of the XCD's L2. Otherwise column blocks walk fastest inside groups of 8 row blocks.
   const int nbn = SWIGLU ? (p.N + 127) / 128 : (p.N + 255) / 256;
   const int nbm = (p.M + kBM - 1) / kBM;
-  const int group = int(blockIdx.x) / (8 * nbn);
-  const int first_m = group * 8;
-  const int gsize = min(nbm - first_m, 8);
-  const int local = int(blockIdx.x) - group * 8 * nbn;
-  const int bm = first_m + local % gsize;
-  const int bn = local / gsize;
+  int bm, bn;
+  if (nbm % 16 == 0 && nbn % 16 == 0) {
+    const int id = int(blockIdx.x);
+    const int super = id >> 8, xcd = id & 7, slot = (id >> 3) & 31;
+    const int nsn = nbn / 16;  // super-tiles per row of super-tiles
+    bm = (super / nsn) * 16 + 4 * (xcd >> 1) + (slot & 3);
+    bn = (super % nsn) * 16 + 8 * (xcd & 1) + (slot >> 2);
+  } else {
+    const int group = int(blockIdx.x) / (8 * nbn);
+    const int first_m = group * 8;
+    const int gsize = min(nbm - first_m, 8);
+    const int local = int(blockIdx.x) - group * 8 * nbn;
+    bm = first_m + local % gsize;
+    bn = local / gsize;
+  }
   const int m0 = bm * kBM;
   const int n0 = SWIGLU ? bn * 128 : bn * 256;
 
@@ -160,44 +171,63 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x16_t{};
 
-  // prologue: kAhead stages in flight
+  // Software pipeline. Stage kt lives in buffer kt % 4. Step kt: read the fragments of its
+  // second 16-wide k slice while the MFMAs of the first run; then wait for stage kt+1's loads and
+  // meet at the barrier (which also certifies every wave is done reading stage kt), refill stage
+  // kt's buffer with stage kt+4, read stage kt+1's first slice and run the MFMAs of the second.
+  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto read = [&](const uint16_t* sbase, int ks, uint4* fa, uint4* fb) {
+    const uint16_t* sa = sbase;
+    const uint16_t* sb = sbase + kBM * kBK;
+    const int chunk = ks * 2 + lc;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int row = wi * 128 + rb * 32 + lr;
+      fa[rb] = *reinterpret_cast<const uint4*>(sa + row * kBK + swz(row, chunk) * 8);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int row = brow0[cb] + lr;
+      fb[cb] = *reinterpret_cast<const uint4*>(sb + row * kBK + swz(row, chunk) * 8);
+    }
+  };
+  auto mma_all = [&](const uint4* fa, const uint4* fb) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mma32(fa[rb], fb[cb], acc[rb][cb]);
+  };
+  // wait until at most `younger` stages of this wave's loads are outstanding (8 loads per stage).
+  // s_waitcnt immediate: vmcnt bits 3:0 (low) and 15:14 (high), expcnt 6:4 and lgkmcnt 11:8
+  // left at their maxima.
+  auto wait_stages = [&](int younger) {
+    if (younger >= 3) __builtin_amdgcn_s_waitcnt(0x4F78);       // vmcnt(24)
+    else if (younger == 2) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+  };
+
+  // prologue: four stages in flight, stage 0 published, its first slice read
   if (0 < nk) issue(std::integral_constant<int, 0>{}, 0);
   if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
   if (2 < nk) issue(std::integral_constant<int, 2>{}, 2);
+  if (3 < nk) issue(std::integral_constant<int, 3>{}, 3);
+  wait_stages(min(nk - 1, 3));
+  __syncthreads();
+  read(st0, 0, fa0, fb0);
 
-  // main loop, unrolled over the 4 stages so every LDS reference names its stage array
   auto step = [&](auto sc, int kt) {
     constexpr int s = decltype(sc)::value;
-    // wait for this stage's loads (younger stages stay in flight), then publish to all waves.
-    // s_waitcnt immediate: vmcnt bits 3:0 (low) and 15:14 (high), expcnt 6:4 and lgkmcnt 11:8
-    // left at their maxima. 8 loads per stage and wave.
-    const int younger = min(nk - 1 - kt, kAhead - 1);
-    if (younger >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);       // vmcnt(16)
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
-    __syncthreads();
-    if (kt + kAhead < nk) issue(std::integral_constant<int, (s + kAhead) % kStages>{}, kt + kAhead);
-    const uint16_t* sa = stage(sc);
-    const uint16_t* sb = sa + kBM * kBK;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = ks * 2 + lc;
-      uint4 fa[4], fb[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int row = wi * 128 + rb * 32 + lr;
-        fa[rb] = *reinterpret_cast<const uint4*>(sa + row * kBK + swz(row, chunk) * 8);
-      }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int row = brow0[cb] + lr;
-        fb[cb] = *reinterpret_cast<const uint4*>(sb + row * kBK + swz(row, chunk) * 8);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mma32(fa[rb], fb[cb], acc[rb][cb]);
+    read(stage(sc), 1, fa1, fb1);
+    mma_all(fa0, fb0);
+    if (kt + 1 < nk) {
+      wait_stages(min(nk - 2 - kt, 2));
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
+      __syncthreads();
+      if (kt + 4 < nk) issue(sc, kt + 4);
+      read(stage(std::integral_constant<int, (s + 1) % kStages>{}), 0, fa0, fb0);
     }
+    mma_all(fa1, fb1);
   };
   for (int kt = 0; kt < nk; kt += kStages) {
     step(std::integral_constant<int, 0>{}, kt);
