@@ -17,6 +17,7 @@ constexpr int kMaxSlices = 64;
 constexpr int kMaxRank = 1024;
 
 int g_shrink_override = -1;
+int g_sk_override = -1;  // shrink workgroups along x in stream-K mode; 0 = direct mode
 int g_expand_override = -1;
 int g_expand_bn_override = -1;
 
@@ -40,15 +41,26 @@ int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves) {
   return int(bn);
 }
 
-// Kernel shape for a shrink call, from host-known sizes only.
-// Shapes picked from rocprofv3 sweeps on MI355X over the decode, prefill and irregular
-// workloads: small problems favour one 16-column block per workgroup with 8 waves splitting K;
-// large ones 32-token tiles covering up to 4 blocks with a 4-deep x ring.
+// Kernel shape for a shrink call, from host-known sizes only (rocprofv3 sweeps on MI355X over
+// the decode sweep, prefill and irregular workloads). Small token counts: one token group and
+// one 16-column block per workgroup, 8 waves splitting K. Otherwise two token groups per
+// workgroup sharing each A fragment, over 3 column blocks, or 4 when the slices have 4 or fewer
+// blocks that 3 does not divide.
 int shrink_variant(int64_t T, int32_t S, int32_t R) {
   if (g_shrink_override >= 0) return g_shrink_override;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  return T * std::max<int64_t>(1, nblk / 4) >= 4096 ? 2 : 3;
+  if (nblk % 3 == 0) return T <= 2048 ? 0 : 3;
+  return nblk <= 4 ? 1 : 3;
 }
+
+// Shrink launch plan and workspace: [0, sched) the standalone scheduler's tile list (only for
+// many segments), then the stream-K partial planes. Stream-K gives every compute unit an equal
+// share of the (tile, reduction step) work, about one workgroup per compute unit.
+struct ShrinkWs {
+  int variant, bm, grid_x, mp;
+  int64_t bound, q;  // tile bound; stream-K steps per workgroup (0 = direct mode)
+  size_t sched, part, total;
+};
 
 int expand_variant(int64_t T) {
   if (g_expand_override >= 0) return g_expand_override;
@@ -60,25 +72,61 @@ size_t schedule_bytes(int64_t T, int32_t G, int bm) {
   return size_t(cdiv(T, bm) + G) * 16 + 256;
 }
 
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+ShrinkWs shrink_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t G) {
+  ShrinkWs w{};
+  w.variant = shrink_variant(T, S, R);
+  w.bm = lmx::shrink_plan_bm(dtype, w.variant);
+  w.bound = cdiv(T, w.bm) + G;
+  const int64_t nsteps = cdiv(K, dtype == LORA_F32 ? 16 : 32);
+  const int64_t nblk = int64_t(S) * ((R + 15) / 16);
+  const int64_t gy = cdiv(nblk, lmx::shrink_plan_cb(dtype, w.variant));
+  // Shared (tile, step) work pays for its second launch only when one workgroup per tile leaves
+  // compute units idle and each workgroup would stream a lot: about 1 KB per fragment load.
+  const int64_t direct_wgs = w.bound * gy;
+  const int64_t frags = lmx::shrink_plan_bm(dtype, w.variant) / 16 + lmx::shrink_plan_cb(dtype, w.variant);
+  const bool shared = direct_wgs < 256 && nsteps * frags * 1024 >= (int64_t(512) << 10);
+  const int64_t P = g_sk_override >= 0 ? g_sk_override : (shared ? std::max<int64_t>(1, 256 / gy) : 0);
+  w.sched = schedule_bytes(T, G, w.bm);
+  w.part = align256(w.sched);
+  if (P == 0) {
+    w.q = 0;
+    w.grid_x = int(w.bound);
+    w.total = w.sched;
+  } else {
+    const int64_t units = w.bound * nsteps;
+    w.q = cdiv(units, P);
+    w.grid_x = int(cdiv(units, w.q));
+    w.mp = int((nsteps - 1) / w.q + 2);
+    w.total = w.part + size_t(w.mp) * size_t(T) * size_t(S) * size_t(R) * 4;
+  }
+  return w;
+}
+
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_EHIP; }
 
-// Workspace of the fused MLP: byte offsets of its five sections (256-byte aligned).
+// Workspace of the fused MLP: byte offsets of its six sections (256-byte aligned).
 struct MlpLayout {
-  int64_t rp;  // rank rounded up to 32
-  size_t xa_gu, lb_gu, hmid, xa_d, lb_d, total;
+  int64_t rp;           // rank rounded up to 32
+  ShrinkWs s_gu, s_d;   // plans of the two LoRA-A products (dense mode, one segment)
+  size_t xa_gu, lb_gu, hmid, xa_d, lb_d, part, total;
 };
-
-size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   MlpLayout L{};
   L.rp = cdiv(r, 32) * 32;
+  // dense mode has no segments: the tile bound is ceil(M / BM)
+  L.s_gu = shrink_ws(LORA_BF16, M, H, 2, int(L.rp), 0);
+  L.s_d = shrink_ws(LORA_BF16, M, I, 1, int(L.rp), 0);
   size_t off = 0;
   L.xa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
   L.lb_gu = off; off += align256(size_t(2 * I) * 2 * L.rp * 2);
   L.hmid = off; off += align256(size_t(M) * I * 2);
   L.xa_d = off; off += align256(size_t(M) * L.rp * 2);
   L.lb_d = off; off += align256(size_t(H) * L.rp * 2);
+  L.part = off;
+  off += align256(std::max(L.s_gu.total - L.s_gu.part, L.s_d.total - L.s_d.part));
   L.total = off;
   return L;
 }
@@ -105,13 +153,13 @@ void lora_tuning_override(int32_t op, int32_t variant) {
   if (op == 0) g_shrink_override = (variant >= 0 && variant < lmx::num_shrink_variants()) ? variant : -1;
   if (op == 1) g_expand_override = (variant >= 0 && variant < lmx::num_expand_variants()) ? variant : -1;
   if (op == 2) g_expand_bn_override = (variant > 0 && variant <= 65536) ? variant : -1;
+  if (op == 3) g_sk_override = (variant >= 0 && variant <= 65535) ? variant : -1;
 }
 
 size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
                                   int32_t G) {
-  (void)dtype; (void)K; (void)S; (void)R;
-  if (T <= 0 || G <= 0) return 0;
-  return schedule_bytes(T, G, lmx::shrink_plan_bm(int(dtype), shrink_variant(T, S, R)));
+  if (T <= 0 || G <= 0 || K <= 0 || S <= 0 || R <= 0 || !valid_dtype(dtype)) return 0;
+  return shrink_ws(int(dtype), T, K, S, R, G).total;
 }
 
 size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t G,
@@ -135,11 +183,13 @@ lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   if (!x || !w_a || !seg_indptr || !weight_indices || !permutation || !lora_ranks || !h)
     return LORA_EINVAL;
   if (ldx < K || lda < K || ldh < int64_t(S) * R) return LORA_EINVAL;
-  const int variant = shrink_variant(T, S, R);
-  const int bm = lmx::shrink_plan_bm(int(dtype), variant);
-  const size_t need = schedule_bytes(T, G, bm);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_EWORKSPACE;
-  const int64_t bound = cdiv(T, bm) + G;
+  if (int64_t(S) * R * T * 16 >= int64_t(1) << 62) return LORA_EUNSUPPORTED;
+  const ShrinkWs ws = shrink_ws(int(dtype), T, K, S, R, G);
+  const int variant = ws.variant;
+  const int bm = ws.bm;
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total)) return LORA_EWORKSPACE;
+  if (ws.q > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return LORA_EWORKSPACE;
+  const int64_t bound = ws.bound;
   if (bound >= INT_MAX) return LORA_EUNSUPPORTED;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -147,17 +197,21 @@ lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   a.x = x; a.w_a = w_a; a.seg_indptr = seg_indptr; a.weight_indices = weight_indices;
   a.permutation = permutation; a.lora_ranks = lora_ranks; a.h = h;
   a.K = K; a.ldx = ldx; a.lda = lda; a.ldh = ldh; a.S = S; a.R = R; a.G = G; a.T = int(T);
-  if (need > 0) {
+  if (ws.sched > 0) {
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + 256);
     int* count = static_cast<int*>(workspace);
     hipError_t e = lmx::launch_schedule(seg_indptr, weight_indices, G, bm, tiles, count, st);
     if (e != hipSuccess) return LORA_EHIP;
     a.tiles = tiles; a.tile_count = count;
   }
+  a.sk_q = ws.q; a.sk_tiles = int(bound); a.sk_mp = ws.mp;
+  if (ws.q > 0) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part);
   const int e = esize(dtype);
   const bool aligned = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
-  lmx::ShrinkPlan plan{variant, int(bound), aligned};
-  return hip_status(lmx::launch_shrink(int(dtype), a, plan, st));
+  lmx::ShrinkPlan plan{variant, ws.grid_x, aligned};
+  if (lmx::launch_shrink(int(dtype), a, plan, st) != hipSuccess) return LORA_EHIP;
+  if (ws.q > 0) return hip_status(lmx::launch_shrink_sk_reduce(int(dtype), a, bm, st));
+  return LORA_OK;
 }
 
 lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t L, int32_t G,
@@ -252,10 +306,13 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
     a.x = x; a.ldx = ldx; a.K = H; a.S = 2; a.R = int(rp); a.G = 1; a.T = int(M);
     a.dense_rank = r; a.w_a_slice[0] = a_gate; a.w_a_slice[1] = a_up; a.w_a = a_gate; a.lda = H;
     a.h = xa_gu; a.ldh = 2 * rp;
-    const int v = shrink_variant(M, 2, int(rp));
-    const int bm = lmx::shrink_plan_bm(LORA_BF16, v);
-    lmx::ShrinkPlan plan{v, int(cdiv(M, bm)), al16(x) && al16(a_gate) && al16(a_up) && (ldx * 2) % 16 == 0 && (H * 2) % 16 == 0};
+    const ShrinkWs& sp = L.s_gu;
+    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp;
+    a.part = reinterpret_cast<float*>(ws + L.part);
+    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al16(x) && al16(a_gate) && al16(a_up) && (ldx * 2) % 16 == 0 && (H * 2) % 16 == 0};
     if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
+    if (sp.q > 0 && (e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st)) != hipSuccess)
+      return LORA_EHIP;
   }
   // 3. hmid = round(silu(x W_g^T + s xa_g B_g^T) * (x W_u^T + s xa_u B_u^T))
   {
@@ -271,10 +328,13 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
     a.x = hmid; a.ldx = I; a.K = I; a.S = 1; a.R = int(rp); a.G = 1; a.T = int(M);
     a.dense_rank = r; a.w_a_slice[0] = a_down; a.w_a = a_down; a.lda = I;
     a.h = xa_d; a.ldh = rp;
-    const int v = shrink_variant(M, 1, int(rp));
-    const int bm = lmx::shrink_plan_bm(LORA_BF16, v);
-    lmx::ShrinkPlan plan{v, int(cdiv(M, bm)), al16(a_down) && (I * 2) % 16 == 0};
+    const ShrinkWs& sp = L.s_d;
+    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp;
+    a.part = reinterpret_cast<float*>(ws + L.part);
+    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al16(a_down) && (I * 2) % 16 == 0};
     if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
+    if (sp.q > 0 && (e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st)) != hipSuccess)
+      return LORA_EHIP;
   }
   // 5. out = round(hmid W_d^T + s xa_d B_d^T)
   {

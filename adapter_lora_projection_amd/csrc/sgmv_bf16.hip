@@ -8,6 +8,10 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a, const ShrinkPlan& plan, hipSt
   return launch_shrink_dt<DT_BF16>(a, plan, st);
 }
 
+hipError_t launch_shrink_sk_reduce_bf16(const ShrinkArgs& a, int bm, hipStream_t st) {
+  return launch_shrink_sk_reduce_dt<DT_BF16>(a, bm, st);
+}
+
 hipError_t launch_expand_bf16(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st) {
   return launch_expand_dt<DT_BF16>(a, plan, st);
 }

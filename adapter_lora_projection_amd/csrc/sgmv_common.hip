@@ -10,18 +10,25 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a, const ShrinkPlan& plan, hipSt
 hipError_t launch_shrink_f16(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);
 hipError_t launch_shrink_f32(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);
 hipError_t launch_expand_bf16(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
+hipError_t launch_shrink_sk_reduce_bf16(const ShrinkArgs& a, int bm, hipStream_t st);
+hipError_t launch_shrink_sk_reduce_f16(const ShrinkArgs& a, int bm, hipStream_t st);
+hipError_t launch_shrink_sk_reduce_f32(const ShrinkArgs& a, int bm, hipStream_t st);
 hipError_t launch_expand_f16(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
 hipError_t launch_expand_f32(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
 
 // Token rows per tile (16 * token groups) and waves of each kernel shape; these tables mirror the
 // variant lists of sgmv_impl.hpp.
-static const int kShrinkBM[] = {16, 32, 32, 16};
+static const int kShrinkBM[] = {16, 32, 64, 32, 16};
+static const int kShrinkWaves[] = {8, 4, 4, 4, 4};
+static const int kShrinkCB[] = {1, 4, 3, 3, 3};
 static const int kExpandBM[] = {16, 16, 16};
 static const int kExpandWaves[] = {4, 8, 4};
 
 int num_shrink_variants() { return int(sizeof(kShrinkBM) / sizeof(int)); }
 int num_expand_variants() { return int(sizeof(kExpandBM) / sizeof(int)); }
 int shrink_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kShrinkBM[variant]; }
+int shrink_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 8 : kShrinkWaves[variant]; }
+int shrink_plan_cb(int dtype, int variant) { return dtype == DT_F32 ? 1 : kShrinkCB[variant]; }
 int expand_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kExpandBM[variant]; }
 int expand_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 4 : kExpandWaves[variant]; }
 int expand_max_rank(int dtype) { return 2 * (dtype == DT_F32 ? Traits<DT_F32>::kStep : Traits<DT_BF16>::kStep); }
@@ -31,6 +38,14 @@ hipError_t launch_shrink(int dtype, const ShrinkArgs& a, const ShrinkPlan& plan,
     case DT_F32: return launch_shrink_f32(a, plan, st);
     case DT_BF16: return launch_shrink_bf16(a, plan, st);
     default: return launch_shrink_f16(a, plan, st);
+  }
+}
+
+hipError_t launch_shrink_sk_reduce(int dtype, const ShrinkArgs& a, int bm, hipStream_t st) {
+  switch (dtype) {
+    case DT_F32: return launch_shrink_sk_reduce_f32(a, bm, st);
+    case DT_BF16: return launch_shrink_sk_reduce_bf16(a, bm, st);
+    default: return launch_shrink_sk_reduce_f16(a, bm, st);
   }
 }
 

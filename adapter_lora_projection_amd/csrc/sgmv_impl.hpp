@@ -25,6 +25,7 @@
 #include "schedule.hpp"
 #include "sgmv_kernels.hpp"
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -32,35 +33,42 @@ namespace lmx {
 
 // ------------------------------------------------------------------------------------ shrink
 
-// AL: x and A rows 16-byte aligned. KFULL: additionally K is a multiple of the chunk width, so
-// no fragment is partial or past the end and no operand needs masking (a lane outside the tile
-// or the rank only produces outputs that are never stored).
-template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL>
-__global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
-  using Tr = Traits<DT>;
-  using S = typename Tr::store_t;
-  constexpr int NT = NW * 64;
-  constexpr int KSTEP = Tr::kStep;
-  constexpr int EPF = Tr::kPerFrag;
-  constexpr int BM = 16 * MT;
-
-  __shared__ Tile s_tile;
-  __shared__ int s_scan[NW];
-  __shared__ f32x4_t s_red[(NW > 1) ? NW : 1][CB * MT][64];
-
+// Tile t of a shrink call: from the segment schedule, or rows [t*BM, (t+1)*BM) of the single
+// dense segment (internal mode, seg_indptr null). Every thread must call it.
+template <int NT>
+__device__ __forceinline__ Tile shrink_tile(const ShrinkArgs& p, int BM, int t, Tile* s_tile,
+                                            int* s_scan) {
   Tile tile;
   if (p.seg_indptr != nullptr) {
     get_tile<NT>(p.seg_indptr, p.weight_indices, p.lora_ranks, nullptr, p.G, BM, p.tiles,
-                 p.tile_count, int(blockIdx.x), &s_tile, s_scan);
-    tile = s_tile;
-  } else {  // dense: one segment over all rows
-    tile.g = int(blockIdx.x) * BM < p.T ? 0 : -1;
-    tile.m0 = int(blockIdx.x) * BM;
+                 p.tile_count, t, s_tile, s_scan);
+    tile = *s_tile;
+  } else {
+    tile.g = t * BM < p.T ? 0 : -1;
+    tile.m0 = t * BM;
     tile.mlen = min(BM, p.T - tile.m0);
     tile.a = 0;
     tile.r = p.dense_rank;
+    tile.sigma = 0.f;
   }
-  if (tile.g < 0) return;
+  return tile;
+}
+
+// One piece of shrink work: reduction steps [k0, k1) of `tile` for the column blocks of this
+// workgroup (grid y). Returns, in `out`, the workgroup's fp32 sums in MFMA layout for the
+// (column block, token group) pairs idx = w, w + NW, ... that this wave finalises.
+//
+// AL: x and A rows 16-byte aligned. KFULL: additionally K is a multiple of the step width, so no
+// fragment is partial or past the end and no operand needs masking (a lane outside the tile or
+// the rank only produces outputs that are never stored).
+template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL>
+__device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& tile, int k0, int k1,
+                                             f32x4_t (*s_red)[CB * MT][64],
+                                             f32x4_t (&out)[(CB * MT + NW - 1) / NW]) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  constexpr int KSTEP = Tr::kStep;
+  constexpr int EPF = Tr::kPerFrag;
 
   const int lane = threadIdx.x & 63, w = wave_id();
   const int li = lane & 15, lg = lane >> 4;
@@ -72,7 +80,6 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
 
   const S* __restrict__ x = reinterpret_cast<const S*>(p.x);
   const S* __restrict__ wa = reinterpret_cast<const S*>(p.w_a);
-  S* __restrict__ h = reinterpret_cast<S*>(p.h);
 
   // Operand rows of this lane; masked lanes keep a valid row and load nothing useful from it.
   const S* xrow[MT];
@@ -96,9 +103,13 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
     col_ok[cb] = (blk < nblk) && (j < r);
     any_col |= (blk < nblk) && (16 * b < r);
     const int ss = blk < nblk ? s : 0;
-    const S* slice_base = (ss < 4 && p.w_a_slice[ss] != nullptr)
-                              ? reinterpret_cast<const S*>(p.w_a_slice[ss])
-                              : wa + int64_t(a * p.S + ss) * p.R * p.lda;
+    // (a constant-index selection: a runtime index into the argument block would make the
+    // compiler copy the whole block to scratch memory)
+    const void* own = nullptr;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) own = (ss == q) ? p.w_a_slice[q] : own;
+    const S* slice_base = own != nullptr ? reinterpret_cast<const S*>(own)
+                                         : wa + int64_t(a * p.S + ss) * p.R * p.lda;
     arow[cb] = slice_base + int64_t(col_ok[cb] ? j : 0) * p.lda;
   }
 
@@ -109,58 +120,70 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
     for (int mt = 0; mt < MT; ++mt) acc[cb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (any_col) {
-    // Each wave owns a contiguous range of fragment steps. x (streamed from HBM) is fetched D
-    // steps ahead in a register ring; A (small, L2-resident) one step ahead.
-    const int nsteps = (K + KSTEP - 1) / KSTEP;
-    const int per = (nsteps + NW - 1) / NW;
-    const int s0 = w * per, s1 = min(s0 + per, nsteps);
-    Frag<S, AL> xr[D][MT], ar[2][CB];
-    auto fetch_x = [&](auto slot, int st) {
+    // Each wave owns a contiguous part of the piece's steps. The A and x fragments of a step are
+    // fetched together D steps ahead into one register ring, so the loads complete in the order
+    // they are consumed and a wait for one step never drains a later step's loads.
+    const int per = (max(0, k1 - k0) + NW - 1) / NW;
+    const int s0 = k0 + w * per, s1 = min(s0 + per, k1);
+    const int cnt = max(0, s1 - s0);
+    Frag<S, AL> xr[D][MT], ar[D][CB];
+    auto fetch = [&](auto slot, int q) {
       constexpr int d = decltype(slot)::value;
-      const int k = st * KSTEP + lg * EPF;
-      const bool in = st < s1;
+      const bool in = q < cnt;
+      const int k = (in ? s0 + q : s0) * KSTEP + lg * EPF;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        ar[d][cb].fetch(arow[cb] + k, in ? (KFULL ? EPF : (col_ok[cb] ? K - k : 0)) : 0, arow[cb]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         xr[d][mt].fetch(xrow[mt] + k, in ? (KFULL ? EPF : (tok_ok[mt] ? K - k : 0)) : 0, xrow[mt]);
     };
-    auto fetch_a = [&](auto slot, int st) {
+    // The scheduler must not reorder the ring's loads: a wait is a count of outstanding loads,
+    // so a slot issued out of order makes the first wait inside the loop drain the whole ring.
+    [&]<int... dd>(std::integer_sequence<int, dd...>) {
+      ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
+    }(std::make_integer_sequence<int, D>{});
+    auto consume = [&](auto slot, int q) {
       constexpr int d = decltype(slot)::value;
-      const int k = st * KSTEP + lg * EPF;
-      const bool in = st < s1;
+      uint4 av[CB], xv[MT];
+      const int kk = (s0 + q) * KSTEP + lg * EPF;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        ar[d][cb].fetch(arow[cb] + k, in ? (KFULL ? EPF : (col_ok[cb] ? K - k : 0)) : 0, arow[cb]);
+        av[cb] = KFULL ? ar[d][cb].raw() : ar[d][cb].masked(col_ok[cb] ? K - kk : 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        xv[mt] = KFULL ? xr[d][mt].raw() : xr[d][mt].masked(tok_ok[mt] ? K - kk : 0);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[cb][mt] = mma_step<DT>(av[cb], xv[mt], acc[cb][mt]);
     };
-    using I0 = std::integral_constant<int, 0>;
-    [&]<int... dd>(std::integer_sequence<int, dd...>) {
-      (fetch_x(std::integral_constant<int, dd>{}, s0 + dd), ...);
-    }(std::make_integer_sequence<int, D>{});
-    fetch_a(I0{}, s0);
-    for (int s = s0; s < s1; s += D) {
+    // Full groups of D steps run without guards, so every path into a wait has the same loads
+    // outstanding and each wait is exactly "this slot's loads have landed". The last partial
+    // group consumes what the ring already holds and fetches nothing.
+    const int nfull = cnt / D;
+    for (int gi = 0; gi < nfull; ++gi) {
+      const int q0 = gi * D;
       [&]<int... dd>(std::integer_sequence<int, dd...>) {
         auto step = [&](auto ddc) {
           constexpr int d = decltype(ddc)::value;
-          const int st = s + d;
-          if (st < s1) {
-            fetch_a(std::integral_constant<int, (d + 1) & 1>{}, st + 1);
-            uint4 av[CB], xv[MT];
-            const int kk = st * KSTEP + lg * EPF;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-              av[cb] = KFULL ? ar[d & 1][cb].raw() : ar[d & 1][cb].masked(col_ok[cb] ? K - kk : 0);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              xv[mt] = KFULL ? xr[d][mt].raw() : xr[d][mt].masked(tok_ok[mt] ? K - kk : 0);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt) acc[cb][mt] = mma_step<DT>(av[cb], xv[mt], acc[cb][mt]);
-            fetch_x(ddc, st + D);
-          }
+          consume(ddc, q0 + d);
+          __builtin_amdgcn_sched_barrier(0);
+          fetch(ddc, q0 + d + D);
+          __builtin_amdgcn_sched_barrier(0);
         };
         (step(std::integral_constant<int, dd>{}), ...);
       }(std::make_integer_sequence<int, D>{});
     }
+    const int rem = cnt - nfull * D;
+    const int qt = nfull * D;
+    [&]<int... dd>(std::integer_sequence<int, dd...>) {
+      auto tail = [&](auto ddc) {
+        constexpr int d = decltype(ddc)::value;
+        if (d < rem) consume(ddc, qt + d);
+      };
+      (tail(std::integral_constant<int, dd>{}), ...);
+    }(std::make_integer_sequence<int, D>{});
   }
 
   // fixed-order reduction of the waves' partial sums
@@ -170,34 +193,147 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) s_red[w][cb * MT + mt][lane] = acc[cb][mt];
     __syncthreads();
+#pragma unroll
+    for (int n = 0; n < (CB * MT + NW - 1) / NW; ++n) {
+      const int idx = w + n * NW;
+      if (idx < CB * MT) {
+        f32x4_t sum = s_red[0][idx][lane];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) sum += s_red[w2][idx][lane];
+        out[n] = sum;
+      }
+    }
+    __syncthreads();  // s_red is reused by the next piece
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) out[cb * MT + mt] = acc[cb][mt];
+  }
+}
+
+// Shrink. Direct mode (sk_q == 0): workgroup x = tile x, all K steps, h written here.
+// Stream-K mode: the flattened work [0, tiles bound * steps) is cut into equal ranges of sk_q
+// steps, one per workgroup x, so every compute unit streams the same amount whatever the
+// segment lengths; each tile piece of a range is written as fp32 partial sums to plane
+// j = workgroup - first workgroup of the tile, rows = the tile's sorted positions, and
+// shrink_sk_reduce_kernel adds the planes in order.
+template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL>
+__global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  constexpr int NT = NW * 64;
+  constexpr int BM = 16 * MT;
+  constexpr int NOUT = (CB * MT + NW - 1) / NW;
+
+  __shared__ Tile s_tile;
+  __shared__ int s_scan[NW];
+  __shared__ f32x4_t s_red[(NW > 1) ? NW : 1][CB * MT][64];
+
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int li = lane & 15, lg = lane >> 4;
+  const int NB = (p.R + 15) >> 4;
+  const int nblk = p.S * NB;
+  const int64_t nsteps = (p.K + Tr::kStep - 1) / Tr::kStep;
+
+  // Stores the sums this wave finalises: to h (rounded) or to a partial slot (fp32).
+  auto store = [&](const Tile& tile, const f32x4_t (&sums)[NOUT], float* slot) {
+#pragma unroll
+    for (int n = 0; n < NOUT; ++n) {
+      const int idx = (NW > 1) ? w + n * NW : n;
+      if (idx >= CB * MT) continue;
+      const int cb = idx / MT, mt = idx - (idx / MT) * MT;
+      const int blk = int(blockIdx.y) * CB + cb;
+      const int m = mt * 16 + li;
+      if (blk >= nblk || m >= tile.mlen) continue;
+      const int s = blk / NB, b = blk - (blk / NB) * NB;
+      if (slot != nullptr) {
+        float* prow = slot + int64_t(m) * (p.S * p.R) + s * p.R;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int c = 16 * b + 4 * lg + v;
+          if (c < tile.r) prow[c] = sums[n][v];
+        }
+      } else {
+        S* hrow = reinterpret_cast<S*>(p.h) + int64_t(tile.m0 + m) * p.ldh + s * p.R;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int c = 16 * b + 4 * lg + v;  // rank column inside the slice
+          if (c < p.R) hrow[c] = (c < tile.r) ? Tr::from_f32(sums[n][v]) : S(0);
+        }
+      }
+    }
+  };
+
+  if (p.sk_q == 0) {
+    const Tile tile = shrink_tile<NT>(p, BM, int(blockIdx.x), &s_tile, s_scan);
+    if (tile.g < 0) return;
+    f32x4_t sums[NOUT];
+    shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, 0, int(nsteps), s_red, sums);
+    store(tile, sums, nullptr);
+    return;
   }
 
-  for (int idx = w; idx < CB * MT; idx += NW) {
-    const int cb = idx / MT, mt = idx - (idx / MT) * MT;
-    f32x4_t sum;
-    if constexpr (NW > 1) {
-      sum = s_red[0][idx][lane];
-#pragma unroll
-      for (int w2 = 1; w2 < NW; ++w2) sum += s_red[w2][idx][lane];
-    } else {
-      sum = acc[0][0];
-#pragma unroll
-      for (int c2 = 0; c2 < CB; ++c2)
-#pragma unroll
-        for (int m2 = 0; m2 < MT; ++m2)
-          if (c2 * MT + m2 == idx) sum = acc[c2][m2];
+  const int64_t units = int64_t(p.sk_tiles) * nsteps;
+  int64_t u = int64_t(blockIdx.x) * p.sk_q;
+  const int64_t uend = min(u + int64_t(p.sk_q), units);
+  while (u < uend) {
+    const int t = int(u / nsteps);
+    const int k0 = int(u - int64_t(t) * nsteps);
+    const int k1 = int(min(nsteps, int64_t(k0) + (uend - u)));
+    const Tile tile = shrink_tile<NT>(p, BM, t, &s_tile, s_scan);
+    if (tile.g < 0) break;  // past the last tile (uniform over the workgroup)
+    const int j = int(blockIdx.x) - int((int64_t(t) * nsteps) / p.sk_q);
+    float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
+    if (tile.r > 0) {
+      f32x4_t sums[NOUT];
+      shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, k0, k1, s_red, sums);
+      store(tile, sums, slot);
     }
-    const int blk = int(blockIdx.y) * CB + cb;
-    if (blk >= nblk) continue;
-    const int m = mt * 16 + li;
-    if (m >= tile.mlen) continue;
-    const int s = blk / NB, b = blk - (blk / NB) * NB;
-    S* hrow = h + int64_t(tile.m0 + m) * p.ldh + s * p.R;
+    u += k1 - k0;
+    __syncthreads();  // every wave has read the shared tile record before the next search
+  }
+}
+
+// Adds the stream-K pieces of tile blockIdx.x in workgroup order, rounds once and writes h,
+// with exact zeros in the rank padding.
+template <int DT>
+__global__ __launch_bounds__(256) void shrink_sk_reduce_kernel(ShrinkArgs p, int BM) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  __shared__ Tile s_tile;
+  __shared__ int s_scan[4];
+  const int t = int(blockIdx.x);
+  const Tile tile = shrink_tile<256>(p, BM, t, &s_tile, s_scan);
+  if (tile.g < 0) return;
+  const int64_t nsteps = (p.K + Tr::kStep - 1) / Tr::kStep;
+  const int wfirst = int((int64_t(t) * nsteps) / p.sk_q);
+  const int wlast = int((int64_t(t + 1) * nsteps - 1) / p.sk_q);
+  const int SR = p.S * p.R;
+  const float* base = p.part + int64_t(tile.m0) * SR;
+  const int64_t plane = int64_t(p.T) * SR;
+  S* __restrict__ h = reinterpret_cast<S*>(p.h);
+  for (int e = int(threadIdx.x); e < tile.mlen * SR; e += 256) {
+    const int m = e / SR, c = e - (e / SR) * SR;
+    const int cr = c - (c / p.R) * p.R;
+    S v = S(0);
+    if (cr < tile.r) {
+      // planes in order; eight loads are issued before their additions
+      const float* src = base + e;
+      const int np = wlast - wfirst + 1;
+      float acc = src[0];
+      int j = 1;
+      for (; j + 8 <= np; j += 8) {
+        float b[8];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int c = 16 * b + 4 * lg + v;  // rank column inside the slice
-      if (c < p.R) hrow[c] = (c < r) ? Tr::from_f32(sum[v]) : S(0);
+        for (int i = 0; i < 8; ++i) b[i] = src[(j + i) * plane];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += b[i];
+      }
+      for (; j < np; ++j) acc += src[j * plane];
+      v = Tr::from_f32(acc);
     }
+    h[int64_t(tile.m0 + m) * p.ldh + c] = v;
   }
 }
 
@@ -283,7 +419,7 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
       }
     }
   };
-  auto do_chunk = [&](auto slot, int i) {
+  auto do_chunk = [&](auto slot, int i, auto refill) {
     constexpr int d = decltype(slot)::value;
     f32x4_t acc[4];
 #pragma unroll
@@ -322,20 +458,32 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
         }
       }
     }
-    fetch(slot, i + D);
+    if constexpr (decltype(refill)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(slot, i + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
+  // Ring slots are issued strictly in order (waits count outstanding loads), and full groups of
+  // D chunks run without guards so every path into a wait has the same loads outstanding; the
+  // last partial group consumes what the ring holds and fetches nothing.
   [&]<int... dd>(std::integer_sequence<int, dd...>) {
-    (fetch(std::integral_constant<int, dd>{}, dd), ...);
+    ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
   }(std::make_integer_sequence<int, D>{});
-  for (int i = 0; i < nci; i += D) {
+  const int nfull = nci / D;
+  for (int gi = 0; gi < nfull; ++gi) {
     [&]<int... dd>(std::integer_sequence<int, dd...>) {
-      auto one = [&](auto ddc) {
-        constexpr int d = decltype(ddc)::value;
-        if (i + d < nci) do_chunk(ddc, i + d);
-      };
-      (one(std::integral_constant<int, dd>{}), ...);
+      (do_chunk(std::integral_constant<int, dd>{}, gi * D + dd, std::true_type{}), ...);
     }(std::make_integer_sequence<int, D>{});
   }
+  const int rem = nci - nfull * D;
+  [&]<int... dd>(std::integer_sequence<int, dd...>) {
+    auto one = [&](auto ddc) {
+      constexpr int d = decltype(ddc)::value;
+      if (d < rem) do_chunk(ddc, nfull * D + d, std::false_type{});
+    };
+    (one(std::integral_constant<int, dd>{}), ...);
+  }(std::make_integer_sequence<int, D>{});
 }
 
 template <int DT, int NW, int JS, int D, bool ALB, bool ALY>
@@ -365,14 +513,15 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
 // ------------------------------------------------------------------------------------ launchers
 
 // Kernel shapes. Shrink: (token groups of 16 per tile, 16-column blocks per workgroup, waves,
-// ring depth of the streamed x fragments). Expand: (waves, ring depth of the
+// ring depth of the streamed A and x fragments). Expand: (waves, ring depth of the
 // streamed y chunks); expand tiles are 16 tokens. fp32 (small correctness workloads) has one
 // shape of each.
 #define LMX_SHRINK_VARIANTS(X) \
-  X(0, 1, 1, 16, 4)            \
-  X(1, 2, 4, 8, 8)             \
-  X(2, 2, 4, 4, 4)             \
-  X(3, 1, 1, 8, 4)
+  X(0, 1, 1, 8, 4)             \
+  X(1, 2, 4, 4, 4)             \
+  X(2, 4, 3, 4, 4)             \
+  X(3, 2, 3, 4, 4)             \
+  X(4, 1, 3, 4, 4)
 #define LMX_EXPAND_VARIANTS(X) \
   X(0, 4, 3)                   \
   X(1, 8, 2)                   \
@@ -407,6 +556,12 @@ hipError_t launch_shrink_dt(const ShrinkArgs& a, const ShrinkPlan& plan, hipStre
     }
     return hipErrorInvalidValue;
   }
+}
+
+template <int DT>
+hipError_t launch_shrink_sk_reduce_dt(const ShrinkArgs& a, int bm, hipStream_t st) {
+  hipLaunchKernelGGL((shrink_sk_reduce_kernel<DT>), dim3(a.sk_tiles), dim3(256), 0, st, a, bm);
+  return hipGetLastError();
 }
 
 template <int DT, int NW, int JS, int D>

@@ -24,6 +24,12 @@ struct ShrinkArgs {
   int T;
   int dense_rank;
   const void* w_a_slice[4];
+  // Stream-K mode when sk_q > 0: the work [0, sk_tiles * steps) is cut into ranges of sk_q
+  // steps, one per workgroup x; the pieces go to part[plane < sk_mp][T][S*R] (fp32, rows by
+  // sorted position) and launch_shrink_sk_reduce adds them into h.
+  int64_t sk_q;
+  int sk_tiles, sk_mp;
+  float* part;
 };
 
 struct ExpandArgs {
@@ -45,7 +51,7 @@ struct ExpandArgs {
 
 struct ShrinkPlan {
   int variant;   // kernel shape
-  int grid_x;    // tile-dimension bound ceil(T / BM) + G
+  int grid_x;    // direct: tile bound ceil(T / BM) + G; stream-K: workgroups with work
   bool aligned;  // x, A bases and row strides are 16-byte aligned
 };
 
@@ -64,6 +70,10 @@ int expand_plan_waves(int dtype, int variant);
 int expand_max_rank(int dtype);  // largest padded rank the expand kernels take
 
 hipError_t launch_shrink(int dtype, const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);
+// Second launch of a stream-K shrink: one workgroup per tile adds its pieces in order.
+hipError_t launch_shrink_sk_reduce(int dtype, const ShrinkArgs& a, int bm, hipStream_t st);
+int shrink_plan_waves(int dtype, int variant);
+int shrink_plan_cb(int dtype, int variant);
 hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
 hipError_t launch_schedule(const int* seg_indptr, const int* weight_indices, int G, int BM,
                            int4* tiles, int* count, hipStream_t st);

@@ -16,7 +16,7 @@ plus the int32 metadata.
 The single adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4) is timed
 in the same run and reported in its own object when the library provides it.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-mlp]
 """
 
 from __future__ import annotations
@@ -104,6 +104,67 @@ class SgmvCaseRun:
             raise RuntimeError(f"lora_expand status {st}")
 
 
+def load_traffic() -> dict:
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter runs, keyed by
+    kernel and workload; empty when the kernel sources changed since the counters were taken."""
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        tj = json.load(open(tpath))
+    except (OSError, ValueError):
+        return {}
+    if tj.get("source_sha") != _kernel_source_sha():
+        return {}
+    return {k: v["hbm_bytes_per_launch"] for k, v in tj.get("kernels", {}).items()}
+
+
+def mlp_flops(M: int, H: int, I: int, r: int) -> tuple[int, int]:
+    """(frozen-weight flops, LoRA flops) of one fused LoRA+SwiGLU MLP forward."""
+    base = 2 * M * H * I * 3
+    lora = 2 * M * r * (2 * H) + 2 * M * r * (2 * I) + 2 * M * r * I + 2 * M * r * H
+    return base, lora
+
+
+def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
+    """The single-adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4),
+    timed with HIP events on the stream it is launched on; roofline against dense bf16 MFMA."""
+    import torch
+
+    import lora_inputs as li
+    from adapter_lora_projection_amd import _lib
+
+    c = li.config_mlp()
+    g = lambda t: t.to("cuda").contiguous()
+    w = [g(t) for t in (c.x, c.w_gate, c.w_up, c.w_down, c.a_gate, c.b_gate, c.a_up, c.b_up,
+                        c.a_down, c.b_down)]
+    out = torch.empty((c.M, c.H), dtype=torch.bfloat16, device="cuda")
+    nbytes = _lib.lora_mlp_workspace_size(_lib.LORA_BF16, c.M, c.H, c.I, c.r)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    p = [t.data_ptr() for t in w]
+    call = lambda: _lib.lora_mlp_fused(_lib.LORA_BF16, c.M, c.H, c.I, c.r, c.scale, p[0], c.H,
+                                       *p[1:], out.data_ptr(), c.H, ws.data_ptr(), nbytes, stream)
+    for _ in range(max(warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(steps, 1))]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    base, lora = mlp_flops(c.M, c.H, c.I, c.r)
+    tflops = (base + lora) / (ms * 1e-3) / 1e12
+    return {"workload": f"fused LoRA+SwiGLU MLP bf16, M={c.M} H={c.H} I={c.I} r={c.r} "
+                        f"scale={c.scale:g}", "ms_per_call": round(ms, 4),
+            "flops_per_call": int(base + lora), "value": round(tflops, 1), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_table.get("mlp_fused"),
+                         "kernel": "lora_mlp_fused (all seven launches of one call)"}}
+
+
 def cpu_baseline(seconds_cap: float = 30.0) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload (host cores)."""
     import oracle
@@ -143,6 +204,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true", help="leave out the fused MLP object")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
@@ -265,17 +327,9 @@ def main() -> int:
                          "pair_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
     mean_case = float(np.mean([p["pair_gbps"] for p in per_case]))
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    traffic_table = load_traffic()
     dom_name = f"{'shrink' if dom_op == 0 else 'expand'}_tok{dr.c.T}"
-    if os.path.exists(tpath):
-        try:
-            tj = json.load(open(tpath))
-            ent = tj.get("kernels", {}).get(dom_name)
-            if ent and tj.get("source_sha") == _kernel_source_sha():
-                traffic = ent["hbm_bytes_per_launch"]
-        except Exception:
-            traffic = None
+    traffic = traffic_table.get(dom_name)
 
     out = {
         "metric": "effective HBM GB/s (and % of peak) for LoRA shrink+expand, tok 50-8192",
@@ -302,6 +356,9 @@ def main() -> int:
                      "traffic": traffic, "kernel": dom_name, "avg_launch_us": round(dom_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(dom_bytes)},
     }
+    if not args.no_mlp:
+        print("[bench] timing the fused LoRA+SwiGLU MLP", file=sys.stderr, flush=True)
+        out["mlp"] = mlp_object(args.steps, args.warmup, traffic_table)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()

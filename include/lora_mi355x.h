@@ -89,8 +89,12 @@ const char* lora_version(void);
  *   lora_ranks     device int32 [L], values in [0, R].
  *   h              device [T][ldh], ldh >= S*R; row i is sorted position i. Columns >= S*R are
  *                  not written.
- *   workspace      device scratch of at least lora_shrink_workspace_size(...) bytes; may be NULL
- *                  when that size is 0. Not read before written; contents undefined afterwards.
+ *   workspace      device scratch of at least lora_shrink_workspace_size(...) bytes, 16-byte
+ *                  aligned; may be NULL when that size is 0. It holds the segment schedule for
+ *                  many segments and the fp32 partial sums of the split reduction: the
+ *                  (tile, K step) work is shared out evenly over about one workgroup per compute
+ *                  unit, and a second launch adds each tile's pieces in a fixed order. Not read
+ *                  before written; contents undefined afterwards.
  */
 lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t L,
                         int32_t G, const void* x, int64_t ldx, const void* w_a, int64_t lda,
@@ -188,10 +192,12 @@ lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method
 
 /*
  * lora_tuning_override -- pins the kernel shape the library picks for an operation, for
- * measurement sweeps. op 0 = shrink (variant 0..3), op 1 = expand (variant 0..2), op 2 = expand
- * columns per workgroup (rounded up to the kernel's chunk multiple); -1 or any other value
- * restores the automatic choice. Process-wide, not thread-safe; results are identical for every
- * variant up to fp32 summation order.
+ * measurement sweeps. op 0 = shrink (variant 0..4), op 1 = expand (variant 0..2), op 2 = expand
+ * columns per workgroup (rounded up to the kernel's chunk multiple), op 3 = shrink workgroups
+ * sharing the (tile, K step) work (1..65535; 0 = one workgroup per tile over all of K, no
+ * second launch; the workspace query follows it); -1 or any other value restores the
+ * automatic choice. Process-wide, not thread-safe; results are identical for every variant up
+ * to fp32 summation order.
  */
 void lora_tuning_override(int32_t op, int32_t variant);
 

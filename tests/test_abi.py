@@ -95,8 +95,20 @@ def test_expand_host_validation(kw, code):
 
 
 def test_workspace_sizes():
-    assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) == 0
     assert _lib.lora_expand_workspace_size(1, 50, 3, 16, 4, 6144) == 0
+    try:
+        # one workgroup per tile over all of K: nothing needed for few segments
+        _lib.lora_tuning_override(3, 0)
+        assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) == 0
+        # shared work over 256 workgroups: 50 tokens in 16-token tiles give a bound of
+        # 4 + 4 segments = 8 tiles of 128 steps, 4 steps per workgroup, at most
+        # 127 // 4 + 2 = 33 pieces per tile, each an fp32 plane of [T][S*R]
+        _lib.lora_tuning_override(3, 256)
+        assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) == 33 * 50 * 48 * 4
+        assert _lib.lora_shrink_workspace_size(2, 50, 4096, 3, 16, 4) == 33 * 50 * 48 * 4
+    finally:
+        _lib.lora_tuning_override(3, -1)
+    assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) % 4 == 0
     n = _lib.lora_shrink_workspace_size(1, 16384, 256, 3, 16, 16384)
     assert n >= 16 * 16384
     assert _lib.lora_shrink_workspace_size(1, 0, 256, 3, 16, 4) == 0

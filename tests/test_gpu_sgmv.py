@@ -26,7 +26,7 @@ def _alp():
     return alp
 
 
-def _run_pair(c, d=None, variant=(None, None)):
+def _run_pair(c, d=None, variant=(None, None), ksplit=None):
     alp = _alp()
     from adapter_lora_projection_amd import _lib
 
@@ -36,6 +36,8 @@ def _run_pair(c, d=None, variant=(None, None)):
             _lib.lora_tuning_override(0, variant[0])
         if variant[1] is not None:
             _lib.lora_tuning_override(1, variant[1])
+        if ksplit is not None:
+            _lib.lora_tuning_override(3, ksplit)
         h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
                        d["lora_ranks"], c.S, c.R)
         y = d["y_in"].clone()
@@ -45,6 +47,7 @@ def _run_pair(c, d=None, variant=(None, None)):
     finally:
         _lib.lora_tuning_override(0, -1)
         _lib.lora_tuning_override(1, -1)
+        _lib.lora_tuning_override(3, -1)
     return h.cpu(), y.cpu()
 
 
@@ -95,15 +98,30 @@ def test_sweep(T):
 
 # ------------------------------------------------------------------ every kernel shape
 
-@pytest.mark.parametrize("sv", range(4))
+@pytest.mark.parametrize("direct", [False, True])
+@pytest.mark.parametrize("sv", range(5))
 @pytest.mark.parametrize("ev", range(3))
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-def test_variants_small(sv, ev, dtype):
-    """Several tiles per segment plus ragged tails, odd ranks, K tail, unaligned slices."""
+def test_variants_small(sv, ev, dtype, direct):
+    """Several tiles per segment plus ragged tails, odd ranks, K tail, unaligned slices; every
+    shrink shape both with the shared (tile, step) work and with one workgroup per tile."""
     c = li.make_sgmv(f"var_{dtype}", seed=40, T=301, K=517, S=3, R=32, L=5,
                      slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
-    print("case", c.name, sv, ev, flush=True)
-    h, y = _run_pair(c, variant=(sv, ev))
+    print("case", c.name, sv, ev, direct, flush=True)
+    h, y = _run_pair(c, variant=(sv, ev), ksplit=0 if direct else None)
+    _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("wgs", [0, 1, 7, 64, 1000])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_shared_work_split(wgs, dtype):
+    """The (tile, K step) work shared over `wgs` workgroups (0 = one per tile): a single
+    workgroup walking every tile, ranges that start and end inside tiles, and one step per
+    workgroup (up to 18 pieces per tile, summed by the second launch)."""
+    c = li.make_sgmv(f"sk_{dtype}", seed=43, T=203, K=517, S=3, R=32, L=5,
+                     slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
+    print("case", c.name, wgs, flush=True)
+    h, y = _run_pair(c, ksplit=wgs)
     _check_pair(c, h, y)
 
 
