@@ -83,10 +83,10 @@ ShrinkWs shrink_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
   const int64_t gy = cdiv(nblk, lmx::shrink_plan_cb(dtype, w.variant));
   // Shared (tile, step) work pays for its second launch only when one workgroup per tile leaves
-  // compute units idle and each workgroup would stream a lot: about 1 KB per fragment load.
+  // half the compute units idle and each workgroup would stream a lot (1 KB per fragment load).
   const int64_t direct_wgs = w.bound * gy;
   const int64_t frags = lmx::shrink_plan_bm(dtype, w.variant) / 16 + lmx::shrink_plan_cb(dtype, w.variant);
-  const bool shared = direct_wgs < 256 && nsteps * frags * 1024 >= (int64_t(512) << 10);
+  const bool shared = direct_wgs < 128 && nsteps * frags * 1024 >= (int64_t(512) << 10);
   const int64_t P = g_sk_override >= 0 ? g_sk_override : (shared ? std::max<int64_t>(1, 256 / gy) : 0);
   w.sched = schedule_bytes(T, G, w.bm);
   w.part = align256(w.sched);
