@@ -17,6 +17,7 @@ constexpr int kMaxSlices = 64;
 constexpr int kMaxRank = 1024;
 
 int g_shrink_override = -1;
+int g_lds_override = -1;  // shrink kernel family: 0 = register ring, 1 = LDS-staged where eligible
 int g_sk_override = -1;  // shrink workgroups along x in stream-K mode; 0 = direct mode
 int g_expand_override = -1;
 int g_expand_bn_override = -1;
@@ -57,8 +58,9 @@ int shrink_variant(int64_t T, int32_t S, int32_t R) {
 // many segments), then the stream-K partial planes. Stream-K gives every compute unit an equal
 // share of the (tile, reduction step) work, about one workgroup per compute unit.
 struct ShrinkWs {
-  int variant, bm, grid_x, mp;
-  int64_t bound, q;  // tile bound; stream-K steps per workgroup (0 = direct mode)
+  bool lds;          // LDS-staged kernel (else the register-ring kernel)
+  int variant, bm, grid_x, mp, unit;
+  int64_t bound, q;  // tile bound; stream-K units per workgroup (0 = direct mode)
   size_t sched, part, total;
 };
 
@@ -74,19 +76,55 @@ size_t schedule_bytes(int64_t T, int32_t G, int bm) {
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-ShrinkWs shrink_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t G) {
-  ShrinkWs w{};
-  w.variant = shrink_variant(T, S, R);
-  w.bm = lmx::shrink_plan_bm(dtype, w.variant);
-  w.bound = cdiv(T, w.bm) + G;
-  const int64_t nsteps = cdiv(K, dtype == LORA_F32 ? 16 : 32);
+// The LDS-staged shrink covers the 16-bit types whose x and A rows are 16-byte aligned and
+// whose K is a multiple of 8; its shape is the smallest column-block count that holds every
+// block of the slices (or 12 blocks per workgroup beyond that).
+int shrink_lds_variant(int32_t S, int32_t R) {
+  if (g_shrink_override >= 0 && g_shrink_override < lmx::num_shrink_lds_variants())
+    return g_shrink_override;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  const int64_t gy = cdiv(nblk, lmx::shrink_plan_cb(dtype, w.variant));
+  for (int v = 0; v < lmx::num_shrink_lds_variants(); ++v)
+    if (lmx::shrink_lds_ncb(v) >= nblk) return v;
+  return lmx::num_shrink_lds_variants() - 1;
+}
+
+// Which shrink kernel to run when the LDS-staged one is eligible (rocprofv3 sweeps on MI355X):
+// it pays for its shared-work second launch when every compute unit streams a lot of x
+// (T * K at least 24 Mi elements: decode tok >= 6144, prefill down-proj, the MLP's down LoRA-A)
+// and the slices have few column blocks; the register-ring kernel is faster below that.
+bool prefer_lds(int64_t T, int64_t K, int32_t S, int32_t R) {
+  if (g_lds_override >= 0) return g_lds_override == 1;
+  const int64_t nblk = int64_t(S) * ((R + 15) / 16);
+  return T * K >= (int64_t(24) << 20) && nblk <= 4;
+}
+
+ShrinkWs shrink_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t G, bool lds) {
+  ShrinkWs w{};
+  w.lds = lds;
+  const int64_t nblk = int64_t(S) * ((R + 15) / 16);
+  int64_t gy, frags;
+  if (lds) {
+    w.variant = shrink_lds_variant(S, R);
+    w.bm = lmx::kShrinkLdsBM;
+    w.unit = lmx::kShrinkLdsUnit;
+    gy = cdiv(nblk, lmx::shrink_lds_ncb(w.variant));
+    frags = (w.bm + 16 * lmx::shrink_lds_ncb(w.variant)) / 8;  // 1 KiB loads per stage
+  } else {
+    w.variant = shrink_variant(T, S, R);
+    w.bm = lmx::shrink_plan_bm(dtype, w.variant);
+    w.unit = dtype == LORA_F32 ? 16 : 32;
+    gy = cdiv(nblk, lmx::shrink_plan_cb(dtype, w.variant));
+    frags = w.bm / 16 + lmx::shrink_plan_cb(dtype, w.variant);  // 1 KiB loads per step
+  }
+  w.bound = cdiv(T, w.bm) + G;
+  const int64_t nsteps = cdiv(K, w.unit);
   // Shared (tile, step) work pays for its second launch only when one workgroup per tile leaves
-  // half the compute units idle and each workgroup would stream a lot (1 KB per fragment load).
+  // half the compute units idle and each workgroup would stream a lot.
+  // (The LDS-staged kernel is chosen only for such problems: it always shares when its tiles
+  // leave compute units idle.)
   const int64_t direct_wgs = w.bound * gy;
-  const int64_t frags = lmx::shrink_plan_bm(dtype, w.variant) / 16 + lmx::shrink_plan_cb(dtype, w.variant);
-  const bool shared = direct_wgs < 128 && nsteps * frags * 1024 >= (int64_t(512) << 10);
+  const bool shared = lds ? direct_wgs < 256
+                          : direct_wgs < 128 && nsteps * frags * 1024 >= (int64_t(512) << 10);
   const int64_t P = g_sk_override >= 0 ? g_sk_override : (shared ? std::max<int64_t>(1, 256 / gy) : 0);
   w.sched = schedule_bytes(T, G, w.bm);
   w.part = align256(w.sched);
@@ -110,6 +148,7 @@ lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_E
 struct MlpLayout {
   int64_t rp;           // rank rounded up to 32
   ShrinkWs s_gu, s_d;   // plans of the two LoRA-A products (dense mode, one segment)
+  ShrinkWs r_gu, r_d;   // the same with the register-ring kernel (unaligned A pointers)
   size_t xa_gu, lb_gu, hmid, xa_d, lb_d, part, total;
 };
 
@@ -117,8 +156,12 @@ MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   MlpLayout L{};
   L.rp = cdiv(r, 32) * 32;
   // dense mode has no segments: the tile bound is ceil(M / BM)
-  L.s_gu = shrink_ws(LORA_BF16, M, H, 2, int(L.rp), 0);
-  L.s_d = shrink_ws(LORA_BF16, M, I, 1, int(L.rp), 0);
+  // plans for both shrink families (the LDS-staged one needs aligned A pointers, known only
+  // at call time); the partials section fits either
+  L.s_gu = shrink_ws(LORA_BF16, M, H, 2, int(L.rp), 0, prefer_lds(M, H, 2, int(L.rp)));
+  L.s_d = shrink_ws(LORA_BF16, M, I, 1, int(L.rp), 0, prefer_lds(M, I, 1, int(L.rp)));
+  L.r_gu = shrink_ws(LORA_BF16, M, H, 2, int(L.rp), 0, false);
+  L.r_d = shrink_ws(LORA_BF16, M, I, 1, int(L.rp), 0, false);
   size_t off = 0;
   L.xa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
   L.lb_gu = off; off += align256(size_t(2 * I) * 2 * L.rp * 2);
@@ -126,7 +169,8 @@ MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   L.xa_d = off; off += align256(size_t(M) * L.rp * 2);
   L.lb_d = off; off += align256(size_t(H) * L.rp * 2);
   L.part = off;
-  off += align256(std::max(L.s_gu.total - L.s_gu.part, L.s_d.total - L.s_d.part));
+  off += align256(std::max(std::max(L.s_gu.total - L.s_gu.part, L.s_d.total - L.s_d.part),
+                           std::max(L.r_gu.total - L.r_gu.part, L.r_d.total - L.r_d.part)));
   L.total = off;
   return L;
 }
@@ -154,12 +198,16 @@ void lora_tuning_override(int32_t op, int32_t variant) {
   if (op == 1) g_expand_override = (variant >= 0 && variant < lmx::num_expand_variants()) ? variant : -1;
   if (op == 2) g_expand_bn_override = (variant > 0 && variant <= 65536) ? variant : -1;
   if (op == 3) g_sk_override = (variant >= 0 && variant <= 65535) ? variant : -1;
+  if (op == 4) g_lds_override = (variant == 0 || variant == 1) ? variant : -1;
 }
 
 size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
                                   int32_t G) {
   if (T <= 0 || G <= 0 || K <= 0 || S <= 0 || R <= 0 || !valid_dtype(dtype)) return 0;
-  return shrink_ws(int(dtype), T, K, S, R, G).total;
+  // the kernel family depends on pointer alignment, which the query does not see: cover both
+  const size_t reg = shrink_ws(int(dtype), T, K, S, R, G, false).total;
+  if (dtype == LORA_F32 || K % 8 != 0 || g_lds_override == 0) return reg;
+  return std::max(reg, shrink_ws(int(dtype), T, K, S, R, G, true).total);
 }
 
 size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t G,
@@ -184,7 +232,10 @@ lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
     return LORA_EINVAL;
   if (ldx < K || lda < K || ldh < int64_t(S) * R) return LORA_EINVAL;
   if (int64_t(S) * R * T * 16 >= int64_t(1) << 62) return LORA_EUNSUPPORTED;
-  const ShrinkWs ws = shrink_ws(int(dtype), T, K, S, R, G);
+  const int e = esize(dtype);
+  const bool aligned = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
+  const bool lds = dtype != LORA_F32 && aligned && K % 8 == 0 && prefer_lds(T, K, S, R);
+  const ShrinkWs ws = shrink_ws(int(dtype), T, K, S, R, G, lds);
   const int variant = ws.variant;
   const int bm = ws.bm;
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total)) return LORA_EWORKSPACE;
@@ -204,11 +255,9 @@ lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
     if (e != hipSuccess) return LORA_EHIP;
     a.tiles = tiles; a.tile_count = count;
   }
-  a.sk_q = ws.q; a.sk_tiles = int(bound); a.sk_mp = ws.mp;
+  a.sk_q = ws.q; a.sk_tiles = int(bound); a.sk_mp = ws.mp; a.sk_unit = ws.unit;
   if (ws.q > 0) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part);
-  const int e = esize(dtype);
-  const bool aligned = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
-  lmx::ShrinkPlan plan{variant, ws.grid_x, aligned};
+  lmx::ShrinkPlan plan{variant, ws.grid_x, aligned, ws.lds};
   if (lmx::launch_shrink(int(dtype), a, plan, st) != hipSuccess) return LORA_EHIP;
   if (ws.q > 0) return hip_status(lmx::launch_shrink_sk_reduce(int(dtype), a, bm, st));
   return LORA_OK;
@@ -306,10 +355,12 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
     a.x = x; a.ldx = ldx; a.K = H; a.S = 2; a.R = int(rp); a.G = 1; a.T = int(M);
     a.dense_rank = r; a.w_a_slice[0] = a_gate; a.w_a_slice[1] = a_up; a.w_a = a_gate; a.lda = H;
     a.h = xa_gu; a.ldh = 2 * rp;
-    const ShrinkWs& sp = L.s_gu;
-    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp;
+    // x is 16-byte aligned with a 16-byte row stride (checked above); A rows are H long, H % 32 == 0
+    const bool al = al16(a_gate) && al16(a_up);
+    const ShrinkWs& sp = al ? L.s_gu : L.r_gu;
+    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp; a.sk_unit = sp.unit;
     a.part = reinterpret_cast<float*>(ws + L.part);
-    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al16(x) && al16(a_gate) && al16(a_up) && (ldx * 2) % 16 == 0 && (H * 2) % 16 == 0};
+    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
     if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
     if (sp.q > 0 && (e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st)) != hipSuccess)
       return LORA_EHIP;
@@ -328,10 +379,11 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
     a.x = hmid; a.ldx = I; a.K = I; a.S = 1; a.R = int(rp); a.G = 1; a.T = int(M);
     a.dense_rank = r; a.w_a_slice[0] = a_down; a.w_a = a_down; a.lda = I;
     a.h = xa_d; a.ldh = rp;
-    const ShrinkWs& sp = L.s_d;
-    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp;
+    const bool al = al16(a_down);
+    const ShrinkWs& sp = al ? L.s_d : L.r_d;
+    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp; a.sk_unit = sp.unit;
     a.part = reinterpret_cast<float*>(ws + L.part);
-    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al16(a_down) && (I * 2) % 16 == 0};
+    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
     if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
     if (sp.q > 0 && (e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st)) != hipSuccess)
       return LORA_EHIP;

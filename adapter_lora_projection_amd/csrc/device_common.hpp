@@ -210,4 +210,29 @@ __device__ __forceinline__ f32x4_t mma_step<DT_F32>(uint4 a, uint4 b, f32x4_t ac
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// One direct-to-LDS 16-byte load per lane: the wave writes 1 KiB of LDS at byte address
+// `lds_addr` (wave-uniform; lane L at +16 L). Issued from an asm block with no register
+// outputs: the compiler does not track it, so waits on these loads are explicit (vm_wait); the
+// compiler's own waits on other loads stay correct because the counter completes in order and
+// can only over-wait.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) T*)p));
+}
+
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt
+// 6:4 and lgkmcnt 11:8 left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
+
 }  // namespace lmx

@@ -51,22 +51,6 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // (row / 4) % 4, so that the 16 lanes of each 16-byte read phase hit 16 distinct bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-// One direct-to-LDS 16-byte load per lane: the wave writes 1 KiB of LDS at byte address
-// `lds_addr` (wave-uniform; lane L at +16 L), i.e. 16 rows x 64 bytes. Issued from an asm block
-// with no register outputs: the compiler does not track it, so the pipeline's waits on these
-// loads are explicit (s_waitcnt vmcnt); the compiler's own waits on other loads stay correct
-// because the counter completes in order and can only over-wait.
-__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));
-}
-
 }  // namespace
 
 template <bool SWIGLU>

@@ -29,6 +29,10 @@ int num_expand_variants() { return int(sizeof(kExpandBM) / sizeof(int)); }
 int shrink_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kShrinkBM[variant]; }
 int shrink_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 8 : kShrinkWaves[variant]; }
 int shrink_plan_cb(int dtype, int variant) { return dtype == DT_F32 ? 1 : kShrinkCB[variant]; }
+// mirrors LMX_SHRINK_LDS_VARIANTS of shrink_lds.hpp
+static const int kShrinkLdsNCB[] = {2, 3, 4, 8, 12};
+int num_shrink_lds_variants() { return int(sizeof(kShrinkLdsNCB) / sizeof(int)); }
+int shrink_lds_ncb(int variant) { return kShrinkLdsNCB[variant]; }
 int expand_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kExpandBM[variant]; }
 int expand_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 4 : kExpandWaves[variant]; }
 int expand_max_rank(int dtype) { return 2 * (dtype == DT_F32 ? Traits<DT_F32>::kStep : Traits<DT_BF16>::kStep); }

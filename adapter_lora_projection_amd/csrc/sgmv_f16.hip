@@ -1,10 +1,12 @@
 // SGMV shrink/expand kernels instantiated for one storage type (f16); split per type so the
 // build compiles the types in parallel.
 #include "sgmv_impl.hpp"
+#include "shrink_lds.hpp"
 
 namespace lmx {
 
 hipError_t launch_shrink_f16(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st) {
+  if (plan.lds) return launch_shrink_lds_dt<DT_F16>(a, plan, st);
   return launch_shrink_dt<DT_F16>(a, plan, st);
 }
 

@@ -5,6 +5,7 @@
 namespace lmx {
 
 hipError_t launch_shrink_f32(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st) {
+  if (plan.lds) return hipErrorInvalidValue;  // 16-bit types only
   return launch_shrink_dt<DT_F32>(a, plan, st);
 }
 

@@ -296,7 +296,9 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
 }
 
 // Adds the stream-K pieces of tile blockIdx.x in workgroup order, rounds once and writes h,
-// with exact zeros in the rank padding.
+// with exact zeros in the rank padding. Workgroup y covers elements [256 y, 256 y + 256) of the
+// tile's [mlen][S*R] block, one per thread; each thread issues its plane loads eight at a time
+// before adding them in order.
 template <int DT>
 __global__ __launch_bounds__(256) void shrink_sk_reduce_kernel(ShrinkArgs p, int BM) {
   using Tr = Traits<DT>;
@@ -305,36 +307,31 @@ __global__ __launch_bounds__(256) void shrink_sk_reduce_kernel(ShrinkArgs p, int
   __shared__ int s_scan[4];
   const int t = int(blockIdx.x);
   const Tile tile = shrink_tile<256>(p, BM, t, &s_tile, s_scan);
-  if (tile.g < 0) return;
-  const int64_t nsteps = (p.K + Tr::kStep - 1) / Tr::kStep;
+  const int SR = p.S * p.R;
+  const int e = int(blockIdx.y) * 256 + int(threadIdx.x);
+  if (tile.g < 0 || e >= tile.mlen * SR) return;
+  const int64_t nsteps = (p.K + p.sk_unit - 1) / p.sk_unit;
   const int wfirst = int((int64_t(t) * nsteps) / p.sk_q);
   const int wlast = int((int64_t(t + 1) * nsteps - 1) / p.sk_q);
-  const int SR = p.S * p.R;
-  const float* base = p.part + int64_t(tile.m0) * SR;
-  const int64_t plane = int64_t(p.T) * SR;
-  S* __restrict__ h = reinterpret_cast<S*>(p.h);
-  for (int e = int(threadIdx.x); e < tile.mlen * SR; e += 256) {
-    const int m = e / SR, c = e - (e / SR) * SR;
-    const int cr = c - (c / p.R) * p.R;
-    S v = S(0);
-    if (cr < tile.r) {
-      // planes in order; eight loads are issued before their additions
-      const float* src = base + e;
-      const int np = wlast - wfirst + 1;
-      float acc = src[0];
-      int j = 1;
-      for (; j + 8 <= np; j += 8) {
-        float b[8];
+  const int np = wlast - wfirst + 1;
+  const int m = e / SR, c = e - (e / SR) * SR;
+  const int cr = c - (c / p.R) * p.R;
+  S v = S(0);
+  if (cr < tile.r) {
+    const float* src = p.part + int64_t(tile.m0) * SR + e;
+    const int64_t plane = int64_t(p.T) * SR;
+    float acc = 0.f;
+    for (int j0 = 0; j0 < np; j0 += 8) {
+      float b[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = src[(j + i) * plane];
+      for (int i = 0; i < 8; ++i) b[i] = (j0 + i < np) ? src[(j0 + i) * plane] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc += b[i];
-      }
-      for (; j < np; ++j) acc += src[j * plane];
-      v = Tr::from_f32(acc);
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i < np) acc = (j0 + i == 0) ? b[i] : acc + b[i];
     }
-    h[int64_t(tile.m0 + m) * p.ldh + c] = v;
+    v = Tr::from_f32(acc);
   }
+  reinterpret_cast<S*>(p.h)[int64_t(tile.m0 + m) * p.ldh + c] = v;
 }
 
 // ------------------------------------------------------------------------------------ expand
@@ -560,7 +557,8 @@ hipError_t launch_shrink_dt(const ShrinkArgs& a, const ShrinkPlan& plan, hipStre
 
 template <int DT>
 hipError_t launch_shrink_sk_reduce_dt(const ShrinkArgs& a, int bm, hipStream_t st) {
-  hipLaunchKernelGGL((shrink_sk_reduce_kernel<DT>), dim3(a.sk_tiles), dim3(256), 0, st, a, bm);
+  const int gy = int((int64_t(bm) * a.S * a.R + 255) / 256);
+  hipLaunchKernelGGL((shrink_sk_reduce_kernel<DT>), dim3(a.sk_tiles, gy), dim3(256), 0, st, a, bm);
   return hipGetLastError();
 }
 

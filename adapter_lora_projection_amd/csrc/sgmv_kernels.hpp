@@ -29,6 +29,7 @@ struct ShrinkArgs {
   // sorted position) and launch_shrink_sk_reduce adds them into h.
   int64_t sk_q;
   int sk_tiles, sk_mp;
+  int sk_unit;  // reduction indices per unit of work (the kernel's step)
   float* part;
 };
 
@@ -50,9 +51,10 @@ struct ExpandArgs {
 };
 
 struct ShrinkPlan {
-  int variant;   // kernel shape
+  int variant;   // kernel shape (of the register-ring kernel, or of the LDS-staged one)
   int grid_x;    // direct: tile bound ceil(T / BM) + G; stream-K: workgroups with work
   bool aligned;  // x, A bases and row strides are 16-byte aligned
+  bool lds;      // the LDS-staged kernel (16-bit types, aligned rows, K % 8 == 0)
 };
 
 struct ExpandPlan {
@@ -74,6 +76,10 @@ hipError_t launch_shrink(int dtype, const ShrinkArgs& a, const ShrinkPlan& plan,
 hipError_t launch_shrink_sk_reduce(int dtype, const ShrinkArgs& a, int bm, hipStream_t st);
 int shrink_plan_waves(int dtype, int variant);
 int shrink_plan_cb(int dtype, int variant);
+int num_shrink_lds_variants();
+int shrink_lds_ncb(int variant);          // 16-column blocks per workgroup
+constexpr int kShrinkLdsBM = 128;         // positions per tile of the LDS-staged shrink
+constexpr int kShrinkLdsUnit = 64;        // reduction indices per stage
 hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
 hipError_t launch_schedule(const int* seg_indptr, const int* weight_indices, int G, int BM,
                            int4* tiles, int* count, hipStream_t st);

@@ -191,13 +191,17 @@ lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method
                                 void* stream);
 
 /*
- * lora_tuning_override -- pins the kernel shape the library picks for an operation, for
- * measurement sweeps. op 0 = shrink (variant 0..4), op 1 = expand (variant 0..2), op 2 = expand
- * columns per workgroup (rounded up to the kernel's chunk multiple), op 3 = shrink workgroups
- * sharing the (tile, K step) work (1..65535; 0 = one workgroup per tile over all of K, no
- * second launch; the workspace query follows it); -1 or any other value restores the
- * automatic choice. Process-wide, not thread-safe; results are identical for every variant up
- * to fp32 summation order.
+ * lora_tuning_override -- pins a choice the library makes for an operation, for measurement
+ * sweeps:
+ *   op 0  shrink kernel shape (0..4, of whichever shrink kernel runs);
+ *   op 1  expand kernel shape (0..2);
+ *   op 2  expand columns per workgroup (rounded up to the kernel's chunk multiple);
+ *   op 3  shrink workgroups sharing the (tile, K step) work (1..65535), or 0 for one workgroup
+ *         per tile over all of K with no second launch; the workspace query follows it;
+ *   op 4  shrink kernel: 0 = operands loaded straight into registers, 1 = LDS-staged where the
+ *         rows are 16-byte aligned and K % 8 == 0.
+ * -1 or any other value restores the automatic choice. Process-wide, not thread-safe; results
+ * are identical for every choice up to fp32 summation order.
  */
 void lora_tuning_override(int32_t op, int32_t variant);
 

@@ -26,7 +26,7 @@ def _alp():
     return alp
 
 
-def _run_pair(c, d=None, variant=(None, None), ksplit=None):
+def _run_pair(c, d=None, variant=(None, None), ksplit=None, lds=None):
     alp = _alp()
     from adapter_lora_projection_amd import _lib
 
@@ -38,6 +38,8 @@ def _run_pair(c, d=None, variant=(None, None), ksplit=None):
             _lib.lora_tuning_override(1, variant[1])
         if ksplit is not None:
             _lib.lora_tuning_override(3, ksplit)
+        if lds is not None:
+            _lib.lora_tuning_override(4, lds)
         h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
                        d["lora_ranks"], c.S, c.R)
         y = d["y_in"].clone()
@@ -48,6 +50,7 @@ def _run_pair(c, d=None, variant=(None, None), ksplit=None):
         _lib.lora_tuning_override(0, -1)
         _lib.lora_tuning_override(1, -1)
         _lib.lora_tuning_override(3, -1)
+        _lib.lora_tuning_override(4, -1)
     return h.cpu(), y.cpu()
 
 
@@ -122,6 +125,30 @@ def test_shared_work_split(wgs, dtype):
                      slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
     print("case", c.name, wgs, flush=True)
     h, y = _run_pair(c, ksplit=wgs)
+    _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("wgs", [0, 5, 300])
+@pytest.mark.parametrize("sv", range(5))
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_lds_shrink_shapes(sv, wgs, dtype):
+    """The LDS-staged shrink in every column-block shape (2..12 blocks per workgroup, so the 6
+    blocks here are split over 3, 2, 2, 1 and 1 workgroups), one workgroup per tile or the work
+    shared over 5 or 300 workgroups; K = 1032 ends in a stage with one valid 8-element chunk;
+    tiles of 128 positions with ragged ends; rank 0, 1, 7, 17 and 32 adapters."""
+    c = li.make_sgmv(f"lds_{dtype}", seed=44, T=301, K=1032, S=3, R=32, L=5,
+                     slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
+    print("case", c.name, sv, wgs, flush=True)
+    h, y = _run_pair(c, variant=(sv, None), ksplit=wgs, lds=1)
+    _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("lds", [0, 1])
+def test_shrink_families_agree_on_prefill(lds):
+    """Both shrink kernel families on the prefill gate_up workload (8 column blocks, K = 4096)."""
+    c = li.config_prefill()[0]
+    print("case", c.name, lds, flush=True)
+    h, y = _run_pair(c, lds=lds)
     _check_pair(c, h, y)
 
 
