@@ -90,12 +90,12 @@ int shrink_lds_variant(int32_t S, int32_t R) {
 
 // Which shrink kernel to run when the LDS-staged one is eligible (rocprofv3 sweeps on MI355X):
 // it pays for its shared-work second launch when every compute unit streams a lot of x
-// (T * K at least 24 Mi elements: decode tok >= 6144, prefill down-proj, the MLP's down LoRA-A)
+// (T * K at least 16 Mi elements: decode tok >= 4096, prefill down-proj, the MLP's LoRA-A)
 // and the slices have few column blocks; the register-ring kernel is faster below that.
 bool prefer_lds(int64_t T, int64_t K, int32_t S, int32_t R) {
   if (g_lds_override >= 0) return g_lds_override == 1;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  return T * K >= (int64_t(24) << 20) && nblk <= 4;
+  return T * K >= (int64_t(16) << 20) && nblk <= 4;
 }
 
 ShrinkWs shrink_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t G, bool lds) {
@@ -326,6 +326,8 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
   if (M < 0 || H < 1 || I < 1 || r < 1) return LORA_EINVAL;
   if (r > 64 || H % 32 != 0 || I % 32 != 0) return LORA_EUNSUPPORTED;
   if (M >= INT_MAX || H >= INT_MAX / 4 || I >= INT_MAX / 4) return LORA_EUNSUPPORTED;
+  // the scaled LoRA-B copies ([2I][2 rp] and [H][rp], rp <= 64) are indexed with 32 bits
+  if (int64_t(2 * I) * 128 + int64_t(H) * 64 >= int64_t(INT_MAX)) return LORA_EUNSUPPORTED;
   if (M == 0) return LORA_OK;
   if (!x || !w_gate || !w_up || !w_down || !a_gate || !b_gate || !a_up || !b_up || !a_down ||
       !b_down || !out)
@@ -346,9 +348,13 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
   auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
   hipError_t e;
   // 1. scaled LoRA-B operands: [s B_g | 0] and [0 | s B_u] stacked, and s B_d
-  if ((e = lmx::launch_scale_lora_b(u16(b_gate), r, int(I), r, scale, lb_gu, 2 * rp, 0, st)) != hipSuccess) return LORA_EHIP;
-  if ((e = lmx::launch_scale_lora_b(u16(b_up), r, int(I), r, scale, lb_gu + I * 2 * rp, 2 * rp, int(rp), st)) != hipSuccess) return LORA_EHIP;
-  if ((e = lmx::launch_scale_lora_b(u16(b_down), r, int(H), r, scale, lb_d, rp, 0, st)) != hipSuccess) return LORA_EHIP;
+  {
+    lmx::ScaleJobs jobs{};
+    jobs.job[0] = {u16(b_gate), r, lb_gu, 2 * rp, int(I), 0};
+    jobs.job[1] = {u16(b_up), r, lb_gu + I * 2 * rp, 2 * rp, int(I), int(rp)};
+    jobs.job[2] = {u16(b_down), r, lb_d, rp, int(H), 0};
+    if ((e = lmx::launch_scale_lora_b(jobs, scale, r, st)) != hipSuccess) return LORA_EHIP;
+  }
   // 2. [xa_g | xa_u] = round(x [A_g; A_u]^T), ranks padded with zeros to rp
   {
     lmx::ShrinkArgs a{};

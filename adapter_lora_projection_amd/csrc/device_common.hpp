@@ -222,6 +222,15 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
                : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset (the
+// scalar-base addressing form), so the per-lane address needs no vector arithmetic.
+__device__ __forceinline__ void dma16_saddr(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 template <typename T>
 __device__ __forceinline__ uint32_t lds_addr(const T* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) T*)p));

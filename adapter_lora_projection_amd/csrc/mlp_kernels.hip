@@ -109,11 +109,46 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
   const uint16_t* const pB2 = p.B2;
   const int64_t plda = p.lda, plda2 = p.lda2, pldw = p.ldw, pldb2 = p.ldb2;
   const int pM = p.M, pN = p.N;
+  // Tiles inside M and N (all of them when M is a multiple of 256 and N of the column tile)
+  // address each 16-row load group as a wave-uniform base plus one loop-invariant per-lane byte
+  // offset: the lane's row inside the group (drow) and its swizzled chunk, which do not depend
+  // on the group (row % 16 == drow and swz(row, c) only reads bits 2..3 of the row).
+  const bool full = m0 + kBM <= pM && n0 + (SWIGLU ? 128 : 256) <= pN;  // uniform
+  const int swb = swz(drow, dslot) * 16;
+  const uint32_t voA = uint32_t(drow * plda * 2 + swb), voW = uint32_t(drow * pldw * 2 + swb);
+  const uint32_t voA2 = uint32_t(drow * plda2 * 2 + swb), voB2 = uint32_t(drow * pldb2 * 2 + swb);
   auto issue = [&](auto sc, int kt) {
     uint16_t* sa = stage(sc);
     uint16_t* sb = sa + kBM * kBK;
     const bool lora = kt >= nk1;
     const int koff = (lora ? kt - nk1 : kt) * kBK;
+    if (full) {
+      const char* abase = reinterpret_cast<const char*>(lora ? pA2 : pA) + int64_t(koff) * 2;
+      const int64_t lda = lora ? plda2 : plda;
+      const uint32_t voa = lora ? voA2 : voA, vow = lora ? voB2 : voW;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = w * 64 + i * 16;  // first row of the load group in the tile
+        dma16_saddr(abase + int64_t(m0 + g) * lda * 2, voa, lds_addr(sa + g * kBK));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = w * 64 + i * 16;
+        const char* wrow;
+        if (SWIGLU) {
+          const int n = n0 + (g & 127);
+          const bool up = g >= 128;
+          wrow = lora ? reinterpret_cast<const char*>(pB2) + (int64_t(up ? pN + n : n) * pldb2 + koff) * 2
+                      : reinterpret_cast<const char*>(up ? pW1 : pW0) + (int64_t(n) * pldw + koff) * 2;
+        } else {
+          const int n = n0 + g;
+          wrow = lora ? reinterpret_cast<const char*>(pB2) + (int64_t(n) * pldb2 + koff) * 2
+                      : reinterpret_cast<const char*>(pW0) + (int64_t(n) * pldw + koff) * 2;
+        }
+        dma16_saddr(wrow, vow, lds_addr(sb + g * kBK));
+      }
+      return;
+    }
     const uint16_t* abase = lora ? pA2 : pA;
     const int64_t lda = lora ? plda2 : plda;
 #pragma unroll
@@ -258,23 +293,34 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
   }
 }
 
-__global__ void scale_lora_b_kernel(const uint16_t* __restrict__ src, int64_t ld_src, int n, int r,
-                                    float scale, uint16_t* __restrict__ dst, int64_t ld_dst,
-                                    int col0) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= int64_t(n) * ld_dst) return;
-  const int row = int(i / ld_dst), j = int(i % ld_dst) - col0;
-  uint16_t v = 0;
-  if (j >= 0 && j < r)
-    v = Traits<DT_BF16>::from_f32(Traits<DT_BF16>::to_f32(src[int64_t(row) * ld_src + j]) * scale);
-  dst[i] = v;
+// The scaled LoRA-B operands of all three projections in one launch: job q writes
+// dst_q[row][c] = round(scale * src_q[row][c - col0_q]) for col0_q <= c < col0_q + r and 0
+// elsewhere in its [n_q][ld_dst_q] block; the grid covers the three blocks back to back.
+__global__ void scale_lora_b_kernel(ScaleJobs jobs, float scale, int r) {
+  // (every block has fewer than 2^31 elements: 32-bit index arithmetic)
+  int i = int(blockIdx.x) * int(blockDim.x) + int(threadIdx.x);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const ScaleJob& jb = jobs.job[q];
+    const int ld = int(jb.ld_dst);
+    const int total = jb.n * ld;
+    if (i < total) {
+      const int row = i / ld, j = i - row * ld - jb.col0;
+      uint16_t v = 0;
+      if (j >= 0 && j < r)
+        v = Traits<DT_BF16>::from_f32(Traits<DT_BF16>::to_f32(jb.src[int64_t(row) * jb.ld_src + j]) * scale);
+      jb.dst[i] = v;
+      return;
+    }
+    i -= total;
+  }
 }
 
-hipError_t launch_scale_lora_b(const uint16_t* src, int64_t ld_src, int n, int r, float scale,
-                               uint16_t* dst, int64_t ld_dst, int col0, hipStream_t st) {
-  const int64_t total = int64_t(n) * ld_dst;
+hipError_t launch_scale_lora_b(const ScaleJobs& jobs, float scale, int r, hipStream_t st) {
+  int64_t total = 0;
+  for (int q = 0; q < 3; ++q) total += int64_t(jobs.job[q].n) * jobs.job[q].ld_dst;
   hipLaunchKernelGGL(scale_lora_b_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                     src, ld_src, n, r, scale, dst, ld_dst, col0);
+                     jobs, scale, r);
   return hipGetLastError();
 }
 

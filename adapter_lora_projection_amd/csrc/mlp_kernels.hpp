@@ -27,9 +27,20 @@ struct GemmArgs {
 
 hipError_t launch_gemm_lora(const GemmArgs& a, bool swiglu, hipStream_t st);
 
-// dst[i][j] = round(scale * src[i][j]) for j < r, 0 for r <= j < ld_dst, rows i < n, written at
-// column offset `col0` of dst rows (the rest of each dst row is zeroed too).
-hipError_t launch_scale_lora_b(const uint16_t* src, int64_t ld_src, int n, int r, float scale,
-                               uint16_t* dst, int64_t ld_dst, int col0, hipStream_t st);
+// One scaled copy: dst[i][col0 + j] = round(scale * src[i][j]) for j < r, rows i < n; every
+// other column of the dst rows [0, ld_dst) is written as 0.
+struct ScaleJob {
+  const uint16_t* src;
+  int64_t ld_src;
+  uint16_t* dst;
+  int64_t ld_dst;
+  int n, col0;
+};
+struct ScaleJobs {
+  ScaleJob job[3];
+};
+
+// The three scaled copies in one launch (same scale and rank).
+hipError_t launch_scale_lora_b(const ScaleJobs& jobs, float scale, int r, hipStream_t st);
 
 }  // namespace lmx

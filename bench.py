@@ -143,7 +143,8 @@ def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
     p = [t.data_ptr() for t in w]
     call = lambda: _lib.lora_mlp_fused(_lib.LORA_BF16, c.M, c.H, c.I, c.r, c.scale, p[0], c.H,
                                        *p[1:], out.data_ptr(), c.H, ws.data_ptr(), nbytes, stream)
-    for _ in range(max(warmup, 1)):
+    # the GPU's clocks take some tens of calls of this size to settle: warm up for at least 30
+    for _ in range(max(warmup, 30)):
         call()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
