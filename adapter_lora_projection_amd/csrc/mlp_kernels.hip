@@ -20,13 +20,14 @@
 //
 // GEMM main loop: 256x256x32 block stages, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16, both
 // operands K-contiguous ([rows][K] row-major, as nn.Linear stores them) loaded straight into
-// LDS (global_load_lds_dwordx4) four stages deep, with XOR-swizzled 64-byte rows so 16-byte
+// LDS (global_load_lds_dwordx4) three stages deep, with XOR-swizzled 64-byte rows so 16-byte
 // fragment reads are bank-conflict free; fragment reads of the next k slice overlap the MFMAs.
 #include "device_common.hpp"
 #include "mlp_kernels.hpp"
 #include "sgmv_kernels.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace lmx {
 
@@ -37,7 +38,7 @@ namespace {
 constexpr int kBM = 256;  // rows of A per block
 constexpr int kBR = 256;  // rows of W per block (B operand)
 constexpr int kBK = 32;   // K per stage (64 bytes per row)
-constexpr int kStages = 4;                       // LDS buffers, all in flight
+constexpr int kStages = 3;  // LDS buffers (more in flight per compute unit measured slower)
 constexpr int kStageElems = (kBM + kBR) * kBK;  // elements per stage (32 KiB)
 
 __device__ __forceinline__ f32x16_t mma32(uint4 a, uint4 b, f32x16_t c) {
@@ -56,16 +57,10 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
   // One LDS array per pipeline stage.
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[kStageElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[kStageElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[kStageElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t stg[kStages][kStageElems];
   auto stage = [&](auto sc) -> uint16_t* {
     constexpr int s = decltype(sc)::value;
-    if constexpr (s == 0) return st0;
-    else if constexpr (s == 1) return st1;
-    else if constexpr (s == 2) return st2;
-    else return st3;
+    return stg[s];
   };
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -190,10 +185,10 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x16_t{};
 
-  // Software pipeline. Stage kt lives in buffer kt % 4. Step kt: read the fragments of its
+  // Software pipeline. Stage kt lives in buffer kt % kStages. Step kt: read the fragments of its
   // second 16-wide k slice while the MFMAs of the first run; then wait for stage kt+1's loads and
   // meet at the barrier (which also certifies every wave is done reading stage kt), refill stage
-  // kt's buffer with stage kt+4, read stage kt+1's first slice and run the MFMAs of the second.
+  // kt's buffer with stage kt+kStages, read stage kt+1's first slice and run the MFMAs of the second.
   uint4 fa0[4], fb0[4], fa1[4], fb1[4];
   auto read = [&](const uint16_t* sbase, int ks, uint4* fa, uint4* fb) {
     const uint16_t* sa = sbase;
@@ -220,39 +215,39 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
   // s_waitcnt immediate: vmcnt bits 3:0 (low) and 15:14 (high), expcnt 6:4 and lgkmcnt 11:8
   // left at their maxima.
   auto wait_stages = [&](int younger) {
-    if (younger >= 3) __builtin_amdgcn_s_waitcnt(0x4F78);       // vmcnt(24)
-    else if (younger == 2) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+    static_assert(kStages <= 5, "wait table");
+    if (younger >= 4) vm_wait<32>();
+    else if (younger == 3) vm_wait<24>();
+    else if (younger == 2) vm_wait<16>();
+    else if (younger == 1) vm_wait<8>();
+    else vm_wait<0>();
   };
 
-  // prologue: four stages in flight, stage 0 published, its first slice read
-  if (0 < nk) issue(std::integral_constant<int, 0>{}, 0);
-  if (1 < nk) issue(std::integral_constant<int, 1>{}, 1);
-  if (2 < nk) issue(std::integral_constant<int, 2>{}, 2);
-  if (3 < nk) issue(std::integral_constant<int, 3>{}, 3);
-  wait_stages(min(nk - 1, 3));
+  // prologue: all stages in flight, stage 0 published, its first slice read
+  [&]<int... ss>(std::integer_sequence<int, ss...>) {
+    ((ss < nk ? issue(std::integral_constant<int, ss>{}, ss) : void()), ...);
+  }(std::make_integer_sequence<int, kStages>{});
+  wait_stages(min(nk - 1, kStages - 1));
   __syncthreads();
-  read(st0, 0, fa0, fb0);
+  read(stg[0], 0, fa0, fb0);
 
   auto step = [&](auto sc, int kt) {
     constexpr int s = decltype(sc)::value;
     read(stage(sc), 1, fa1, fb1);
     mma_all(fa0, fb0);
     if (kt + 1 < nk) {
-      wait_stages(min(nk - 2 - kt, 2));
+      wait_stages(min(nk - 2 - kt, kStages - 2));
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
       __syncthreads();
-      if (kt + 4 < nk) issue(sc, kt + 4);
+      if (kt + kStages < nk) issue(sc, kt + kStages);
       read(stage(std::integral_constant<int, (s + 1) % kStages>{}), 0, fa0, fb0);
     }
     mma_all(fa1, fb1);
   };
   for (int kt = 0; kt < nk; kt += kStages) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
-    if (kt + 2 < nk) step(std::integral_constant<int, 2>{}, kt + 2);
-    if (kt + 3 < nk) step(std::integral_constant<int, 3>{}, kt + 3);
+    [&]<int... ss>(std::integer_sequence<int, ss...>) {
+      ((kt + ss < nk ? step(std::integral_constant<int, ss>{}, kt + ss) : void()), ...);
+    }(std::make_integer_sequence<int, kStages>{});
   }
 
   // epilogue. Output layout of a 32x32 block: lane l holds column l % 32 and rows

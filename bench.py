@@ -125,8 +125,9 @@ def mlp_flops(M: int, H: int, I: int, r: int) -> tuple[int, int]:
 
 
 def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
-    """The single-adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4),
-    timed with HIP events on the stream it is launched on; roofline against dense bf16 MFMA."""
+    """The single-adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4):
+    K calls back to back after a warm-up, timed with HIP events on the stream they are launched
+    on; roofline against dense bf16 MFMA."""
     import torch
 
     import lora_inputs as li
@@ -143,18 +144,19 @@ def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
     p = [t.data_ptr() for t in w]
     call = lambda: _lib.lora_mlp_fused(_lib.LORA_BF16, c.M, c.H, c.I, c.r, c.scale, p[0], c.H,
                                        *p[1:], out.data_ptr(), c.H, ws.data_ptr(), nbytes, stream)
-    # the GPU's clocks take some tens of calls of this size to settle: warm up for at least 30
-    for _ in range(max(warmup, 30)):
+    # the GPU's clocks take some tens of calls of this size to settle: warm up for at least 60
+    for _ in range(max(warmup, 60)):
         call()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(max(steps, 1))]
-    for a, b in evs:
-        a.record()
+    # K calls back to back between two events on the stream they run on
+    n = max(steps, 1)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
         call()
-        b.record()
+    b.record()
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = a.elapsed_time(b) / n
     base, lora = mlp_flops(c.M, c.H, c.I, c.r)
     tflops = (base + lora) / (ms * 1e-3) / 1e12
     return {"workload": f"fused LoRA+SwiGLU MLP bf16, M={c.M} H={c.H} I={c.I} r={c.r} "
