@@ -21,8 +21,8 @@ hipError_t launch_expand_f32(const ExpandArgs& a, const ExpandPlan& plan, hipStr
 static const int kShrinkBM[] = {16, 32, 64, 32, 16};
 static const int kShrinkWaves[] = {8, 4, 4, 4, 4};
 static const int kShrinkCB[] = {1, 4, 3, 3, 3};
-static const int kExpandBM[] = {16, 16, 16};
-static const int kExpandWaves[] = {4, 8, 4};
+static const int kExpandBM[] = {16, 16, 16, 16, 16};
+static const int kExpandWaves[] = {4, 8, 4, 4, 8};
 
 int num_shrink_variants() { return int(sizeof(kShrinkBM) / sizeof(int)); }
 int num_expand_variants() { return int(sizeof(kExpandBM) / sizeof(int)); }

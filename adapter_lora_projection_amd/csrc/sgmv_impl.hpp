@@ -522,7 +522,9 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
 #define LMX_EXPAND_VARIANTS(X) \
   X(0, 4, 3)                   \
   X(1, 8, 2)                   \
-  X(2, 4, 4)
+  X(2, 4, 4)                   \
+  X(3, 4, 2)                   \
+  X(4, 8, 1)
 
 template <int DT, int MT, int CB, int NW, int D>
 static hipError_t launch_shrink_t(const ShrinkArgs& a, bool aligned, int grid_x, hipStream_t st) {

@@ -194,7 +194,7 @@ lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method
  * lora_tuning_override -- pins a choice the library makes for an operation, for measurement
  * sweeps:
  *   op 0  shrink kernel shape (0..4, of whichever shrink kernel runs);
- *   op 1  expand kernel shape (0..2);
+ *   op 1  expand kernel shape (0..4);
  *   op 2  expand columns per workgroup (rounded up to the kernel's chunk multiple);
  *   op 3  shrink workgroups sharing the (tile, K step) work (1..65535), or 0 for one workgroup
  *         per tile over all of K with no second launch; the workspace query follows it;

@@ -103,7 +103,7 @@ def test_sweep(T):
 
 @pytest.mark.parametrize("direct", [False, True])
 @pytest.mark.parametrize("sv", range(5))
-@pytest.mark.parametrize("ev", range(3))
+@pytest.mark.parametrize("ev", range(5))
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_variants_small(sv, ev, dtype, direct):
     """Several tiles per segment plus ragged tails, odd ranks, K tail, unaligned slices; every
