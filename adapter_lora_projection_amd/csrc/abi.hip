@@ -47,12 +47,12 @@ int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves) {
 // the decode sweep, prefill and irregular workloads). Small token counts: one token group and
 // one 16-column block per workgroup, 8 waves splitting K. Otherwise two token groups per
 // workgroup sharing each A fragment, over 3 column blocks, or 4 when the slices have 4 or fewer
-// blocks that 3 does not divide.
+// blocks that 3 does not divide. The 2-deep operand ring measured faster than 4-deep.
 int shrink_variant(int64_t T, int32_t S, int32_t R) {
   if (g_shrink_override >= 0) return g_shrink_override;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  if (nblk % 3 == 0) return T <= 2048 ? 0 : 3;
-  return nblk <= 4 ? 1 : 3;
+  if (nblk % 3 == 0) return T <= 2048 ? 2 : 4;
+  return nblk <= 4 ? 1 : 4;
 }
 
 // Shrink launch plan and workspace: [0, sched) the standalone scheduler's tile list (only for

@@ -18,9 +18,9 @@ hipError_t launch_expand_f32(const ExpandArgs& a, const ExpandPlan& plan, hipStr
 
 // Token rows per tile (16 * token groups) and waves of each kernel shape; these tables mirror the
 // variant lists of sgmv_impl.hpp.
-static const int kShrinkBM[] = {16, 32, 64, 32, 16};
-static const int kShrinkWaves[] = {8, 4, 4, 4, 4};
-static const int kShrinkCB[] = {1, 4, 3, 3, 3};
+static const int kShrinkBM[] = {16, 32, 16, 32, 32};
+static const int kShrinkWaves[] = {8, 4, 8, 4, 4};
+static const int kShrinkCB[] = {1, 4, 1, 3, 3};
 static const int kExpandBM[] = {16, 16, 16, 16, 16};
 static const int kExpandWaves[] = {4, 8, 4, 4, 8};
 

@@ -516,9 +516,9 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
 #define LMX_SHRINK_VARIANTS(X) \
   X(0, 1, 1, 8, 4)             \
   X(1, 2, 4, 4, 4)             \
-  X(2, 4, 3, 4, 4)             \
+  X(2, 1, 1, 8, 2)             \
   X(3, 2, 3, 4, 4)             \
-  X(4, 1, 3, 4, 4)
+  X(4, 2, 3, 4, 2)
 #define LMX_EXPAND_VARIANTS(X) \
   X(0, 4, 3)                   \
   X(1, 8, 2)                   \

@@ -206,12 +206,12 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
 }
 
 // Kernel shapes of the LDS-staged shrink: (index, BMG, NCB, NS). 128 positions per tile;
-// NCB 16-column blocks per workgroup; NS stages (stage buffers of up to 32 KiB keep 4).
+// NCB 16-column blocks per workgroup; NS stages.
 #define LMX_SHRINK_LDS_VARIANTS(X) \
-  X(0, 8, 2, 4)                    \
-  X(1, 8, 3, 4)                    \
-  X(2, 8, 4, 4)                    \
-  X(3, 8, 8, 4)                    \
+  X(0, 8, 2, 3)                    \
+  X(1, 8, 3, 3)                    \
+  X(2, 8, 4, 3)                    \
+  X(3, 8, 8, 3)                    \
   X(4, 8, 12, 3)
 
 template <int DT>
