@@ -232,7 +232,7 @@ lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   if (T == 0 || G == 0) return LORA_OK;
   if (K < 1 || L < 1) return LORA_EINVAL;
   if (T >= INT_MAX || K >= INT_MAX || G >= INT_MAX / 2) return LORA_EUNSUPPORTED;
-  if (!x || !w_a || !seg_indptr || !weight_indices || !permutation || !lora_ranks || !h)
+  if (!x || !w_a || !seg_indptr || !weight_indices || !lora_ranks || !h)
     return LORA_EINVAL;
   if (ldx < K || lda < K || ldh < int64_t(S) * R) return LORA_EINVAL;
   if (int64_t(S) * R * T * 16 >= int64_t(1) << 62) return LORA_EUNSUPPORTED;
@@ -279,7 +279,7 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
   if (T == 0 || G == 0 || N == 0) return LORA_OK;
   if (L < 1) return LORA_EINVAL;
   if (T >= INT_MAX || N >= INT_MAX / 2 || G >= INT_MAX / 2) return LORA_EUNSUPPORTED;
-  if (!h || !w_b || !slice_offsets || !seg_indptr || !weight_indices || !permutation ||
+  if (!h || !w_b || !slice_offsets || !seg_indptr || !weight_indices ||
       !lora_ranks || !scalings || !y)
     return LORA_EINVAL;
   if (ldh < int64_t(S) * R || ldb < R || ldy < N) return LORA_EINVAL;

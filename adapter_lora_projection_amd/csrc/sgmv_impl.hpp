@@ -384,7 +384,8 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
   for (int v = 0; v < 4; ++v) {
     const int m = 4 * g + v;
     tok_ok[v] = m < tile.mlen;
-    yrow[v] = y + int64_t(p.permutation[tile.m0 + (tok_ok[v] ? m : 0)]) * p.ldy;
+    const int pos = tile.m0 + (tok_ok[v] ? m : 0);
+    yrow[v] = y + int64_t(p.permutation != nullptr ? p.permutation[pos] : pos) * p.ldy;
   }
   const S* bblk = wb + int64_t(a) * p.N * p.ldb;  // adapter a's rows of B
 

@@ -59,7 +59,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
 def shrink(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, S: int, R: int,
            h: torch.Tensor | None = None) -> torch.Tensor:
     """h = x[perm] A_a^T per segment (``lora_shrink``). x: [T][K] (row stride >= K),
-    w_a: [L][S*R][K]; returns h [T][S*R] in sorted order."""
+    w_a: [L][S*R][K]; returns h [T][S*R] in sorted order. permutation=None: identity."""
     _dev(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, h)
     T, K = x.shape
     ldx = _rows(x, "x")
@@ -69,7 +69,8 @@ def shrink(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, S: int, 
     G = weight_indices.numel()
     _meta(seg_indptr, G + 1, "seg_indptr")
     _meta(weight_indices, None, "weight_indices")
-    _meta(permutation, T, "permutation")
+    if permutation is not None:  # None: identity (tokens already grouped by segment)
+        _meta(permutation, T, "permutation")
     _meta(lora_ranks, w_a.shape[0], "lora_ranks")
     if h is None:
         h = torch.empty((T, S * R), dtype=x.dtype, device=x.device)
@@ -87,7 +88,7 @@ def shrink(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, S: int, 
 def expand(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks, scalings,
            y, S: int, R: int) -> torch.Tensor:
     """y[perm[i], slice] += scale_a * h B_a^T in place (``lora_expand``). h: [T][S*R] sorted
-    order, w_b: [L][N][R], y: [T][>=N] token order. Returns y."""
+    order, w_b: [L][N][R], y: [T][>=N] token order. Returns y. permutation=None: identity."""
     _dev(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks, scalings, y)
     T = h.shape[0]
     ldh = _rows(h, "h")
@@ -101,7 +102,8 @@ def expand(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_
     _meta(slice_offsets, S + 1, "slice_offsets")
     _meta(seg_indptr, G + 1, "seg_indptr")
     _meta(weight_indices, None, "weight_indices")
-    _meta(permutation, T, "permutation")
+    if permutation is not None:  # None: identity (tokens already grouped by segment)
+        _meta(permutation, T, "permutation")
     _meta(lora_ranks, w_b.shape[0], "lora_ranks")
     if scalings.dtype != torch.float32 or scalings.numel() != w_b.shape[0]:
         raise ValueError("scalings must be float32 [L]")

@@ -85,7 +85,8 @@ const char* lora_version(void);
  *   seg_indptr     device int32 [G+1]: 0 = seg_indptr[0] <= ... <= seg_indptr[G] = T.
  *   weight_indices device int32 [G], values in [0, L).
  *   permutation    device int32 [T], a bijection of [0, T): sorted position i reads token row
- *                  permutation[i].
+ *                  permutation[i]; NULL means the identity (tokens already grouped by segment:
+ *                  the non-chunked LoRA-A product of the prefill path).
  *   lora_ranks     device int32 [L], values in [0, R].
  *   h              device [T][ldh], ldh >= S*R; row i is sorted position i. Columns >= S*R are
  *                  not written.
@@ -115,7 +116,8 @@ size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_
  * with an fp32 accumulation and one rounding to `dtype` per stored element. Entries of y outside
  * the slices, and every row of a rank-0 adapter, are neither read nor written.
  *
- *   T, S, L, G     as for lora_shrink.
+ *   T, S, L, G     as for lora_shrink; permutation as for lora_shrink (NULL: identity, the
+ *                  non-chunked LoRA-B product of the prefill path).
  *   R              padded rank, 1 <= R <= 64 (bf16, fp16) or 32 (fp32).
  *   N              columns covered by the slices; slice_offsets[S] == N.
  *   h              device [T][ldh], ldh >= S*R, sorted order (the output of lora_shrink).

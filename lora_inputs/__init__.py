@@ -256,6 +256,57 @@ def config_mlp(seed: int = 4, M: int = 4096, H: int = 4096, I: int = 12288, r: i
                    a_down=a_down, b_down=b_down)
 
 
+@dataclass
+class QkvCase:
+    """Single-adapter LoRA attention projections of one x (nn.Linear [out][in] layouts)."""
+
+    name: str
+    dtype: str
+    M: int
+    H: int
+    Nq: int
+    Nkv: int
+    r: int
+    scale: float
+    x: torch.Tensor  # [M][H]
+    w_q: torch.Tensor  # [Nq][H]
+    w_k: torch.Tensor  # [Nkv][H]
+    w_v: torch.Tensor  # [Nkv][H]
+    a_q: torch.Tensor  # [r][H]
+    b_q: torch.Tensor  # [Nq][r]
+    a_k: torch.Tensor
+    b_k: torch.Tensor  # [Nkv][r]
+    a_v: torch.Tensor
+    b_v: torch.Tensor
+    w_o: torch.Tensor  # [H][Nq] (output projection, reads the attention output)
+    a_o: torch.Tensor  # [r][Nq]
+    b_o: torch.Tensor  # [H][r]
+
+
+def config_qkv(seed: int = 5, M: int = 4096, H: int = 4096, Nq: int = 4096, Nkv: int = 1024,
+               r: int = 16, scale: float = 4.0, dtype: str = "bf16") -> QkvCase:
+    """Single-adapter LoRA Q/K/V and O projections (Qwen3-8B-shaped attention by default:
+    32 query heads and 8 key/value heads of 128): x~N(0,1) [M][H]; frozen W and LoRA A/B
+    ~N(0,0.02); scale alpha/r = 4; dropout 0."""
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (M, H), 1.0, dtype)
+    w_q = _normal(rng, (Nq, H), 0.02, dtype)
+    w_k = _normal(rng, (Nkv, H), 0.02, dtype)
+    w_v = _normal(rng, (Nkv, H), 0.02, dtype)
+    a_q = _normal(rng, (r, H), 0.02, dtype)
+    b_q = _normal(rng, (Nq, r), 0.02, dtype)
+    a_k = _normal(rng, (r, H), 0.02, dtype)
+    b_k = _normal(rng, (Nkv, r), 0.02, dtype)
+    a_v = _normal(rng, (r, H), 0.02, dtype)
+    b_v = _normal(rng, (Nkv, r), 0.02, dtype)
+    w_o = _normal(rng, (H, Nq), 0.02, dtype)
+    a_o = _normal(rng, (r, Nq), 0.02, dtype)
+    b_o = _normal(rng, (H, r), 0.02, dtype)
+    return QkvCase(name=f"qkv_{dtype}_M{M}_H{H}_Nq{Nq}_Nkv{Nkv}_r{r}", dtype=dtype, M=M, H=H,
+                   Nq=Nq, Nkv=Nkv, r=r, scale=scale, x=x, w_q=w_q, w_k=w_k, w_v=w_v, a_q=a_q,
+                   b_q=b_q, a_k=a_k, b_k=b_k, a_v=a_v, b_v=b_v, w_o=w_o, a_o=a_o, b_o=b_o)
+
+
 def sweep_case(T: int) -> SgmvCase:
     """One point of the decode-QKV token sweep (same generator and seed as the tok=50 case)."""
     return config_decode_qkv(T=T, seed=1)

@@ -10,8 +10,9 @@ Sources (pages as titled):
   changes: chunked-SGMV shrink/expand driven by seg_indptr, an index range (weight_indices), a
   token permutation and a slice offset table; one segment per adapter.
 * "Add optional fast lora path for qwen2/qwen3 on npu" (ms-swift pull request 9754), What this PR
-  does and Compatibility checks: the single-adapter LoRA MLP with fused SwiGLU, dropout 0, no
-  bias, not merged.
+  does and Compatibility checks: the single-adapter LoRA MLP with fused SwiGLU, and the
+  single-adapter LoRA attention projections (query/key/value and output), dropout 0, no bias,
+  not merged.
 
 Readings where the pages are silent are listed in each function's docstring.
 
@@ -22,8 +23,10 @@ inputs, hand-worked fixtures, closed forms, invariants and library casts); none 
 from .rounding import rho, DTYPE_FORMATS
 from .sgmv import shrink, expand, tile_list, slice_blocks, validate_metadata
 from .mlp import silu, lora_mlp, lora_mlp_rows
+from .linear import lora_linear, lora_qkv, lora_linear_rows
 
 __all__ = [
     "rho", "DTYPE_FORMATS", "shrink", "expand", "tile_list", "slice_blocks",
-    "validate_metadata", "silu", "lora_mlp", "lora_mlp_rows",
+    "validate_metadata", "silu", "lora_mlp", "lora_mlp_rows", "lora_linear", "lora_qkv",
+    "lora_linear_rows",
 ]

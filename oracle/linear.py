@@ -1,0 +1,52 @@
+"""fp64 oracle of the single-adapter LoRA linear projections (attention Q, K, V and O).
+
+Test infrastructure only (see the package docstring).
+
+Source: "Add optional fast lora path for qwen2/qwen3 on npu" (ms-swift pull request 9754). What
+this PR does: the fast path patches the Qwen2/Qwen3 attention forward as well as the MLP, with
+the fast LoRA projection logic; the review thread names the projection helpers for the fused
+query/key/value projection and for the output projection, under the same compatibility checks
+(dropout 0, one active adapter, no trainable base bias, unmerged weights). With nn.Linear
+layouts ``[out][in]`` each projection is
+
+    y = x W^T + s (x A^T) B^T.
+
+Reading of the rounding points (the pages do not state them), as for the MLP: the LoRA-A product
+that feeds the second matrix product is stored in the storage dtype, and the output is stored
+once. The query, key and value projections read the same x; each has its own W, A and B.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .rounding import rho
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        import torch
+
+        return a.detach().to(torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def lora_linear(x, w, a, b, scale: float, out_dtype: str):
+    """y = rho(x W^T + s * xa B^T) with xa = rho(x A^T) (``out_dtype`` 'f64' rounds nothing)."""
+    x = _f64(x)
+    xa = rho(x @ _f64(a).T, out_dtype)
+    return rho(x @ _f64(w).T + float(scale) * (xa @ _f64(b).T), out_dtype)
+
+
+def lora_qkv(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, scale: float, out_dtype: str):
+    """(q, k, v): the three projections of the same x, each ``lora_linear``."""
+    return (lora_linear(x, w_q, a_q, b_q, scale, out_dtype),
+            lora_linear(x, w_k, a_k, b_k, scale, out_dtype),
+            lora_linear(x, w_v, a_v, b_v, scale, out_dtype))
+
+
+def lora_linear_rows(rows, x, w, a, b, scale: float, out_dtype: str):
+    """``lora_linear`` restricted to the given rows of x (each output row depends on its own
+    input row only), for sampled checks at full size."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return lora_linear(_f64(x)[rows], w, a, b, scale, out_dtype)

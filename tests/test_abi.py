@@ -64,7 +64,6 @@ def _expand(**kw):
     (dict(R=2048), _lib.LORA_EUNSUPPORTED),
     (dict(K=0), _lib.LORA_EINVAL),
     (dict(x=None), _lib.LORA_EINVAL),
-    (dict(permutation=None), _lib.LORA_EINVAL),
     (dict(h=None), _lib.LORA_EINVAL),
     (dict(ldx=15), _lib.LORA_EINVAL),
     (dict(lda=8), _lib.LORA_EINVAL),

@@ -152,6 +152,31 @@ def test_shrink_families_agree_on_prefill(lds):
     _check_pair(c, h, y)
 
 
+@pytest.mark.parametrize("lds", [0, 1])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_identity_permutation_null(dtype, lds):
+    """The non-chunked ops: permutation NULL means the identity. Checked against the oracle
+    with an identity permutation (tokens already grouped by segment)."""
+    c = li.make_sgmv(f"nochunk_{dtype}", seed=45, T=333, K=520, S=2, R=16, L=4,
+                     slice_offsets=[0, 200, 264], dtype=dtype, identity_perm=True)
+    assert torch.equal(c.permutation, torch.arange(c.T, dtype=torch.int32))
+    d = to_dev(c)
+    alp = _alp()
+    from adapter_lora_projection_amd import _lib
+
+    try:
+        _lib.lora_tuning_override(4, lds)
+        h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], None,
+                       d["lora_ranks"], c.S, c.R)
+        y = d["y_in"].clone()
+        alp.expand(h, d["B"], d["slice_offsets"], d["seg_indptr"], d["weight_indices"], None,
+                   d["lora_ranks"], d["scalings"], y, c.S, c.R)
+        torch.cuda.synchronize()
+    finally:
+        _lib.lora_tuning_override(4, -1)
+    _check_pair(c, h.cpu(), y.cpu())
+
+
 # ------------------------------------------------------------------ edge cases
 
 def test_empty_and_zero_sizes():

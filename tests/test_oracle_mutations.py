@@ -13,6 +13,7 @@ import pytest
 
 import oracle.sgmv as sgmv_mod
 import oracle.mlp as mlp_mod
+import oracle.linear as linear_mod
 import lora_inputs as li
 from oracle import rho
 
@@ -83,4 +84,26 @@ def test_mlp_mutation_is_caught(old, new):
     good = mlp_mod.lora_mlp(*_args(c), c.scale, "f64")
     assert np.allclose(good, ref, rtol=1e-11, atol=1e-13)
     bad = _mutant(mlp_mod, old, new).lora_mlp(*_args(c), c.scale, "f64")
+    assert not np.allclose(bad, ref, rtol=1e-11, atol=1e-13)
+
+
+LINEAR_MUTATIONS = [
+    ("rho(x @ _f64(w).T + float(scale) * (xa @ _f64(b).T), out_dtype)",
+     "rho(x @ _f64(w).T + (xa @ _f64(b).T), out_dtype)"),  # dropped scaling
+    ("rho(x @ _f64(w).T + float(scale) * (xa @ _f64(b).T), out_dtype)",
+     "rho(x @ _f64(w).T - float(scale) * (xa @ _f64(b).T), out_dtype)"),  # sign
+    ("xa = rho(x @ _f64(a).T, out_dtype)", "xa = rho(x @ _f64(a)[::-1].T, out_dtype)"),  # rank order
+    ("rho(x @ _f64(w).T + float(scale)", "rho(float(scale)"),  # dropped base product
+]
+
+
+@pytest.mark.parametrize("old,new", LINEAR_MUTATIONS)
+def test_linear_mutation_is_caught(old, new):
+    from tests.test_oracle_linear import _brute, _tiny
+
+    c = _tiny(2)
+    ref = _brute(c.x, c.w_q, c.a_q, c.b_q, c.scale, "f64")
+    good = linear_mod.lora_linear(c.x, c.w_q, c.a_q, c.b_q, c.scale, "f64")
+    assert np.allclose(good, ref, rtol=1e-11, atol=1e-13)
+    bad = _mutant(linear_mod, old, new).lora_linear(c.x, c.w_q, c.a_q, c.b_q, c.scale, "f64")
     assert not np.allclose(bad, ref, rtol=1e-11, atol=1e-13)
