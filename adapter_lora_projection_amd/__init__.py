@@ -1,5 +1,6 @@
-"""MI355X (gfx950) multi-adapter LoRA projection: chunked-SGMV shrink/expand and the fused
-single-adapter LoRA+SwiGLU MLP, as hand-written HIP kernels behind a C ABI.
+"""MI355X (gfx950) multi-adapter LoRA projection: chunked-SGMV shrink/expand, the fused
+single-adapter LoRA+SwiGLU MLP and the single-adapter LoRA attention projections, as hand-written
+HIP kernels behind a C ABI.
 
 ``_lib`` mirrors the C entry points one to one; ``ops`` adds tensor-level helpers that infer
 sizes and strides from torch tensors, allocate outputs and workspaces, and pass the current
@@ -7,6 +8,7 @@ stream. Every step runs in the HIP library; there is no CPU path.
 """
 
 from ._lib import LoraError, lib, lora_version
-from .ops import expand, mlp_fused, schedule_tiles, shrink
+from .ops import expand, linear_fused, mlp_fused, qkv_fused, schedule_tiles, shrink
 
-__all__ = ["LoraError", "lib", "lora_version", "shrink", "expand", "schedule_tiles", "mlp_fused"]
+__all__ = ["LoraError", "lib", "lora_version", "shrink", "expand", "schedule_tiles", "mlp_fused",
+           "linear_fused", "qkv_fused"]

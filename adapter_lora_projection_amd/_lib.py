@@ -33,6 +33,13 @@ SIGNATURES = {
     "lora_mlp_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
     "lora_mlp_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
+    "lora_linear_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
+                                 _vp, _vp, _i64, _vp, _sz, _vp]),
+    "lora_linear_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
+    "lora_qkv_fused": (_i32, [_i32, _i64, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp,
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                              _i64, _vp, _sz, _vp]),
+    "lora_qkv_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i64, _i32]),
 }
 
 
@@ -128,3 +135,27 @@ def lora_mlp_workspace_size(dtype, M, H, I, r) -> int:
 
 def lora_tuning_override(op: int, variant: int) -> None:
     lib().lora_tuning_override(op, variant)
+
+
+def lora_linear_fused(dtype, M, K, N, r, scale, x, ldx, w, a, b, out, ldo, workspace,
+                      workspace_bytes, stream) -> None:
+    st = lib().lora_linear_fused(dtype, M, K, N, r, scale, _p(x), ldx, _p(w), _p(a), _p(b),
+                                 _p(out), ldo, _p(workspace), workspace_bytes, stream)
+    _check("lora_linear_fused", st)
+
+
+def lora_linear_workspace_size(dtype, M, K, N, r) -> int:
+    return int(lib().lora_linear_workspace_size(dtype, M, K, N, r))
+
+
+def lora_qkv_fused(dtype, M, K, Nq, Nkv, r, scale, x, ldx, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v,
+                   b_v, q, ldq, k, ldk, v, ldv, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_qkv_fused(dtype, M, K, Nq, Nkv, r, scale, _p(x), ldx, _p(w_q), _p(w_k),
+                              _p(w_v), _p(a_q), _p(b_q), _p(a_k), _p(b_k), _p(a_v), _p(b_v),
+                              _p(q), ldq, _p(k), ldk, _p(v), ldv, _p(workspace), workspace_bytes,
+                              stream)
+    _check("lora_qkv_fused", st)
+
+
+def lora_qkv_workspace_size(dtype, M, K, Nq, Nkv, r) -> int:
+    return int(lib().lora_qkv_workspace_size(dtype, M, K, Nq, Nkv, r))

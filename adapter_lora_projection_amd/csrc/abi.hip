@@ -179,6 +179,101 @@ MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   return L;
 }
 
+// Workspace of the LoRA linear projections (P = 1 or 3 projections of one x): byte offsets of
+// [xa [M][P rp]], the scaled LoRA-B copies [N_p][rp] and the shrink partials.
+struct LinearLayout {
+  int64_t rp;
+  int P;
+  ShrinkWs s, r;  // LoRA-A product plans: LDS-staged / register-ring (unaligned A pointers)
+  size_t xa, lb[3], part, total;
+};
+
+LinearLayout linear_layout(int64_t M, int64_t K, const int64_t* N, int P, int32_t r) {
+  LinearLayout L{};
+  L.rp = cdiv(r, 32) * 32;
+  L.P = P;
+  L.s = shrink_ws(LORA_BF16, M, K, P, int(L.rp), 0, prefer_lds(M, K, P, int(L.rp)));
+  L.r = shrink_ws(LORA_BF16, M, K, P, int(L.rp), 0, false);
+  size_t off = 0;
+  L.xa = off; off += align256(size_t(M) * P * L.rp * 2);
+  for (int p = 0; p < P; ++p) { L.lb[p] = off; off += align256(size_t(N[p]) * L.rp * 2); }
+  L.part = off;
+  off += align256(std::max(L.s.total - L.s.part, L.r.total - L.r.part));
+  L.total = off;
+  return L;
+}
+
+// The shared body of lora_linear_fused (P = 1) and lora_qkv_fused (P = 3).
+lora_status linear_fused(lora_dtype dtype, int64_t M, int64_t K, const int64_t* N, int P,
+                         int32_t r, float scale, const void* x, int64_t ldx, const void* const* w,
+                         const void* const* a, const void* const* b, void* const* out,
+                         const int64_t* ldo, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
+  if (M < 0 || K < 1 || r < 1) return LORA_EINVAL;
+  for (int p = 0; p < P; ++p)
+    if (N[p] < 1) return LORA_EINVAL;
+  if (r > 64 || K % 32 != 0) return LORA_EUNSUPPORTED;
+  if (M >= INT_MAX || K >= INT_MAX / 4) return LORA_EUNSUPPORTED;
+  for (int p = 0; p < P; ++p)
+    if (N[p] >= INT_MAX / 4) return LORA_EUNSUPPORTED;
+  if (M == 0) return LORA_OK;
+  if (!x) return LORA_EINVAL;
+  for (int p = 0; p < P; ++p)
+    if (!w[p] || !a[p] || !b[p] || !out[p]) return LORA_EINVAL;
+  if (ldx < K) return LORA_EINVAL;
+  for (int p = 0; p < P; ++p)
+    if (ldo[p] < N[p]) return LORA_EINVAL;
+  if (!al16(x) || (ldx * 2) % 16 != 0) return LORA_EUNSUPPORTED;
+  for (int p = 0; p < P; ++p)
+    if (!al16(w[p])) return LORA_EUNSUPPORTED;
+  int64_t ntot = 0;
+  for (int p = 0; p < P; ++p) ntot += N[p];
+  if (ntot * 64 >= int64_t(INT_MAX)) return LORA_EUNSUPPORTED;  // the scaled-B copies
+  const LinearLayout L = linear_layout(M, K, N, P, r);
+  if (workspace == nullptr || workspace_bytes < L.total || !al16(workspace)) return LORA_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* xa = reinterpret_cast<uint16_t*>(ws + L.xa);
+  const int64_t rp = L.rp;
+  auto u16 = [](const void* q) { return static_cast<const uint16_t*>(q); };
+  // 1. scaled LoRA-B operands s * B_p, zero padded to rp columns
+  {
+    lmx::ScaleJobs jobs{};
+    for (int p = 0; p < P; ++p)
+      jobs.job[p] = {u16(b[p]), r, reinterpret_cast<uint16_t*>(ws + L.lb[p]), rp, int(N[p]), 0};
+    if (lmx::launch_scale_lora_b(jobs, scale, r, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 2. [xa_0 | .. | xa_{P-1}] = round(x [A_0; ..]^T) in one pass over x (dense shrink, P slices)
+  {
+    bool al = true;
+    for (int p = 0; p < P; ++p) al = al && al16(a[p]);
+    const ShrinkWs& sp = al ? L.s : L.r;
+    lmx::ShrinkArgs sa{};
+    sa.x = x; sa.ldx = ldx; sa.K = K; sa.S = P; sa.R = int(rp); sa.G = 1; sa.T = int(M);
+    sa.dense_rank = r; sa.w_a = a[0]; sa.lda = K;
+    for (int p = 0; p < P; ++p) sa.w_a_slice[p] = a[p];
+    sa.h = xa; sa.ldh = P * rp;
+    sa.sk_q = sp.q; sa.sk_tiles = int(sp.bound); sa.sk_mp = sp.mp; sa.sk_unit = sp.unit;
+    sa.part = reinterpret_cast<float*>(ws + L.part);
+    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
+    if (lmx::launch_shrink(LORA_BF16, sa, plan, st) != hipSuccess) return LORA_EHIP;
+    if (sp.q > 0 && lmx::launch_shrink_sk_reduce(LORA_BF16, sa, sp.bm, st) != hipSuccess)
+      return LORA_EHIP;
+  }
+  // 3. out_p = round(x W_p^T + s xa_p B_p^T): one GEMM per projection with LoRA in K
+  for (int p = 0; p < P; ++p) {
+    lmx::GemmArgs g{};
+    g.A = u16(x); g.lda = ldx; g.W0 = u16(w[p]); g.W1 = u16(w[p]); g.ldw = K;
+    g.A2 = xa + p * rp; g.lda2 = P * rp;
+    g.B2 = reinterpret_cast<const uint16_t*>(ws + L.lb[p]); g.ldb2 = rp;
+    g.C = static_cast<uint16_t*>(out[p]); g.ldc = ldo[p];
+    g.M = int(M); g.N = int(N[p]); g.K = int(K); g.K2 = int(rp);
+    if (lmx::launch_gemm_lora(g, false, st) != hipSuccess) return LORA_EHIP;
+  }
+  return LORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -408,6 +503,49 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
     if ((e = lmx::launch_gemm_lora(g, false, st)) != hipSuccess) return LORA_EHIP;
   }
   return LORA_OK;
+}
+
+size_t lora_linear_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r) {
+  (void)dtype;
+  if (M <= 0 || K <= 0 || N <= 0 || r <= 0) return 0;
+  const int64_t n[1] = {N};
+  return linear_layout(M, K, n, 1, r).total;
+}
+
+lora_status lora_linear_fused(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r,
+                              float scale, const void* x, int64_t ldx, const void* w,
+                              const void* a, const void* b, void* out, int64_t ldo,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t n[1] = {N}, ld[1] = {ldo};
+  const void* ws[1] = {w};
+  const void* as[1] = {a};
+  const void* bs[1] = {b};
+  void* os[1] = {out};
+  return linear_fused(dtype, M, K, n, 1, r, scale, x, ldx, ws, as, bs, os, ld, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t lora_qkv_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,
+                               int32_t r) {
+  (void)dtype;
+  if (M <= 0 || K <= 0 || Nq <= 0 || Nkv <= 0 || r <= 0) return 0;
+  const int64_t n[3] = {Nq, Nkv, Nkv};
+  return linear_layout(M, K, n, 3, r).total;
+}
+
+lora_status lora_qkv_fused(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,
+                           int32_t r, float scale, const void* x, int64_t ldx, const void* w_q,
+                           const void* w_k, const void* w_v, const void* a_q, const void* b_q,
+                           const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                           void* q, int64_t ldq, void* k, int64_t ldk, void* v, int64_t ldv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t n[3] = {Nq, Nkv, Nkv}, ld[3] = {ldq, ldk, ldv};
+  const void* ws[3] = {w_q, w_k, w_v};
+  const void* as[3] = {a_q, a_k, a_v};
+  const void* bs[3] = {b_q, b_k, b_v};
+  void* os[3] = {q, k, v};
+  return linear_fused(dtype, M, K, n, 3, r, scale, x, ldx, ws, as, bs, os, ld, workspace,
+                      workspace_bytes, stream);
 }
 
 lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method,

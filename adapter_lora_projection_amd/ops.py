@@ -157,3 +157,51 @@ def mlp_fused(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_dow
                         a_gate, b_gate, a_up, b_up, a_down, b_down, out, ldo, workspace,
                         workspace.numel(), _stream())
     return out
+
+
+def _bf16_mat(t, shape, name):
+    if tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+
+
+def linear_fused(x, w, a, b, scale: float, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """out = x W^T + s (x A^T) B^T with one adapter (``lora_linear_fused``). x: [M][K] bf16;
+    w: [N][K]; a: [r][K]; b: [N][r]."""
+    _dev(x, w, a, b, out, workspace)
+    M, K = x.shape
+    N, r = w.shape[0], a.shape[0]
+    for t, shape, name in ((w, (N, K), "w"), (a, (r, K), "a"), (b, (N, r), "b")):
+        _bf16_mat(t, shape, name)
+    ldx = _rows(x, "x")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    nbytes = _lib.lora_linear_workspace_size(_lib.LORA_BF16, M, K, N, r)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _lib.lora_linear_fused(_lib.LORA_BF16, M, K, N, r, float(scale), x, ldx, w, a, b, out,
+                           _rows(out, "out"), workspace, workspace.numel(), _stream())
+    return out
+
+
+def qkv_fused(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, scale: float,
+              workspace: torch.Tensor | None = None):
+    """(q, k, v) projections of one x with one adapter each (``lora_qkv_fused``)."""
+    _dev(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, workspace)
+    M, K = x.shape
+    Nq, Nkv, r = w_q.shape[0], w_k.shape[0], a_q.shape[0]
+    for t, shape, name in ((w_q, (Nq, K), "w_q"), (w_k, (Nkv, K), "w_k"), (w_v, (Nkv, K), "w_v"),
+                           (a_q, (r, K), "a_q"), (a_k, (r, K), "a_k"), (a_v, (r, K), "a_v"),
+                           (b_q, (Nq, r), "b_q"), (b_k, (Nkv, r), "b_k"), (b_v, (Nkv, r), "b_v")):
+        _bf16_mat(t, shape, name)
+    ldx = _rows(x, "x")
+    q = torch.empty((M, Nq), dtype=x.dtype, device=x.device)
+    k = torch.empty((M, Nkv), dtype=x.dtype, device=x.device)
+    v = torch.empty((M, Nkv), dtype=x.dtype, device=x.device)
+    nbytes = _lib.lora_qkv_workspace_size(_lib.LORA_BF16, M, K, Nq, Nkv, r)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _lib.lora_qkv_fused(_lib.LORA_BF16, M, K, Nq, Nkv, r, float(scale), x, ldx, w_q, w_k, w_v,
+                        a_q, b_q, a_k, b_k, a_v, b_v, q, Nq, k, Nkv, v, Nkv, workspace,
+                        workspace.numel(), _stream())
+    return q, k, v

@@ -13,8 +13,9 @@ per call as: x rows + valid rank rows of A of the adapters used + valid h entrie
 valid h entries + valid rank columns of B of the adapters used + y read and written (expand);
 plus the int32 metadata.
 
-The single adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4) is timed
-in the same run and reported in its own object when the library provides it.
+The single-adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4) and the
+single-adapter LoRA attention projections (q/k/v and o of the same layer shape) are timed in the
+same run and reported in their own objects.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-mlp]
 """
@@ -168,6 +169,63 @@ def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
                          "kernel": "lora_mlp_fused (all seven launches of one call)"}}
 
 
+def attention_object(steps: int, warmup: int) -> dict:
+    """The single-adapter LoRA attention projections (bf16, Qwen3-8B shape: M=4096, H=4096,
+    32 query and 8 key/value heads of 128, r=16, scale 4): lora_qkv_fused then lora_linear_fused
+    for the output projection, K pairs back to back after a warm-up, HIP events on their stream;
+    roofline against dense bf16 MFMA."""
+    import torch
+
+    import lora_inputs as li
+    from adapter_lora_projection_amd import _lib
+
+    c = li.config_qkv()
+    g = lambda t: t.to("cuda").contiguous()
+    d = {k: g(getattr(c, k)) for k in ("x", "w_q", "w_k", "w_v", "a_q", "b_q", "a_k", "b_k", "a_v",
+                                       "b_v", "w_o", "a_o", "b_o")}
+    q = torch.empty((c.M, c.Nq), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((c.M, c.Nkv), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((c.M, c.Nkv), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((c.M, c.H), dtype=torch.bfloat16, device="cuda")
+    nq = _lib.lora_qkv_workspace_size(_lib.LORA_BF16, c.M, c.H, c.Nq, c.Nkv, c.r)
+    no = _lib.lora_linear_workspace_size(_lib.LORA_BF16, c.M, c.Nq, c.H, c.r)
+    ws = torch.empty(max(nq, no, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    P = {kk: t.data_ptr() for kk, t in d.items()}
+
+    def call():
+        _lib.lora_qkv_fused(_lib.LORA_BF16, c.M, c.H, c.Nq, c.Nkv, c.r, c.scale, P["x"], c.H,
+                            P["w_q"], P["w_k"], P["w_v"], P["a_q"], P["b_q"], P["a_k"], P["b_k"],
+                            P["a_v"], P["b_v"], q.data_ptr(), c.Nq, k.data_ptr(), c.Nkv,
+                            v.data_ptr(), c.Nkv, ws.data_ptr(), ws.numel(), stream)
+        _lib.lora_linear_fused(_lib.LORA_BF16, c.M, c.Nq, c.H, c.r, c.scale, q.data_ptr(), c.Nq,
+                               P["w_o"], P["a_o"], P["b_o"], o.data_ptr(), c.H, ws.data_ptr(),
+                               ws.numel(), stream)
+
+    for _ in range(max(warmup, 60)):
+        call()
+    torch.cuda.synchronize()
+    n = max(steps, 1)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    nqkv = c.Nq + 2 * c.Nkv
+    flops = (2 * c.M * c.H * nqkv + 2 * c.M * c.r * (3 * c.H + nqkv)  # q, k, v
+             + 2 * c.M * c.Nq * c.H + 2 * c.M * c.r * (c.Nq + c.H))   # o
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"LoRA q/k/v + o projections bf16, M={c.M} H={c.H} Nq={c.Nq} Nkv={c.Nkv} "
+                        f"r={c.r} scale={c.scale:g}", "ms_per_call": round(ms, 4),
+            "flops_per_call": int(flops), "value": round(tflops, 1), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "lora_qkv_fused + lora_linear_fused (all launches)"}}
+
+
 def cpu_baseline(min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload (host cores): passes
     over the sweep's token counts in order, until at least min_seconds of oracle time."""
@@ -216,7 +274,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-mlp", action="store_true", help="leave out the fused MLP object")
+    ap.add_argument("--no-mlp", action="store_true",
+                    help="leave out the fused MLP and attention-projection objects")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
@@ -380,6 +439,8 @@ def main() -> int:
     if not args.no_mlp:
         print("[bench] timing the fused LoRA+SwiGLU MLP", file=sys.stderr, flush=True)
         out["mlp"] = mlp_object(args.steps, args.warmup, traffic_table)
+        print("[bench] timing the LoRA attention projections", file=sys.stderr, flush=True)
+        out["attention_projections"] = attention_object(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()

@@ -11,6 +11,8 @@
  *   - lora_mlp_fused: the single-adapter LoRA MLP with fused SwiGLU of "Add optional fast lora
  *     path for qwen2/qwen3 on npu" (ms-swift pull request 9754), What this PR does and
  *     Compatibility checks (dropout 0, one adapter, no bias, unmerged weights).
+ *   - lora_linear_fused / lora_qkv_fused: the single-adapter LoRA attention projections (output,
+ *     and query/key/value of one x) of the same fast path (pull request 9754).
  *   - lora_schedule_tiles: export of the device segment schedule (the on-device segment scheduler
  *     named in the Summary of pull request 550) for checking.
  *   - lora_check_metadata: the value checks that pull request 550 (Behaviour changes) moves out of
@@ -170,6 +172,53 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
                            void* workspace, size_t workspace_bytes, void* stream);
 
 size_t lora_mlp_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r);
+
+/*
+ * lora_linear_fused -- single-adapter LoRA linear projection (bf16): the attention output
+ * projection of the fast LoRA path of "Add optional fast lora path for qwen2/qwen3 on npu" (What
+ * this PR does: the attention forward with fast LoRA projections; Compatibility checks as for
+ * the MLP).
+ *
+ *   out = round( x W^T + scale * xa B^T ),   xa = round( x A^T ),
+ * with fp32 accumulation and round-to-nearest-even to bf16 at xa and out only. The scale is
+ * folded into a bf16 copy of B (exact for a power-of-two scale, as for the MLP).
+ *
+ *   M, K, N        rows of x, input features (K % 32 == 0), output features.
+ *   r              LoRA rank, 1 <= r <= 64.
+ *   x              device [M][ldx] bf16, ldx >= K, 16-byte aligned rows.
+ *   w              device [N][K] bf16, contiguous, 16-byte aligned.
+ *   a, b           device [r][K] and [N][r] bf16, contiguous.
+ *   out            device [M][ldo] bf16, ldo >= N (a new tensor; not accumulated into).
+ *   workspace      device scratch of lora_linear_workspace_size(...) bytes, 16-byte aligned.
+ * Returns LORA_EUNSUPPORTED for another dtype, K % 32 != 0, r > 64 or unaligned x / w.
+ */
+lora_status lora_linear_fused(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r,
+                              float scale, const void* x, int64_t ldx, const void* w,
+                              const void* a, const void* b, void* out, int64_t ldo,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+size_t lora_linear_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r);
+
+/*
+ * lora_qkv_fused -- the query, key and value projections of one x, each a single-adapter LoRA
+ * linear projection as in lora_linear_fused (same page and section). The three LoRA-A products
+ * are formed in one pass over x; each projection then runs one matrix product with its LoRA
+ * term folded into the reduction.
+ *
+ *   q = round( x W_q^T + scale * round(x A_q^T) B_q^T ),  k and v likewise,
+ *   x [M][ldx]; W_q [Nq][K], W_k and W_v [Nkv][K]; A_* [r][K]; B_q [Nq][r], B_k, B_v [Nkv][r];
+ *   q [M][ldq >= Nq], k [M][ldk >= Nkv], v [M][ldv >= Nkv]. Other requirements as for
+ *   lora_linear_fused; workspace of lora_qkv_workspace_size(...) bytes.
+ */
+lora_status lora_qkv_fused(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,
+                           int32_t r, float scale, const void* x, int64_t ldx, const void* w_q,
+                           const void* w_k, const void* w_v, const void* a_q, const void* b_q,
+                           const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                           void* q, int64_t ldq, void* k, int64_t ldk, void* v, int64_t ldv,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+size_t lora_qkv_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,
+                               int32_t r);
 
 /*
  * lora_schedule_tiles -- the segment schedule the compute kernels use, exported for checking.

@@ -153,3 +153,45 @@ def test_mlp_workspace_size_covers_hmid():
     M, H, I = 4096, 4096, 12288
     n = _lib.lora_mlp_workspace_size(1, M, H, I, 16)
     assert n >= M * I * 2 and n < M * I * 2 + 64 * (1 << 20)
+
+
+def _linear(**kw):
+    args = dict(dtype=1, M=8, K=64, N=32, r=16, scale=2.0, x=0x1000, ldx=64, w=0x2000, a=0x3000,
+                b=0x4000, out=0x5000, ldo=32, workspace=0x100000, workspace_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    return _lib.lib().lora_linear_fused(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), _lib.LORA_EUNSUPPORTED),
+    (dict(K=48, ldx=48), _lib.LORA_EUNSUPPORTED),   # K % 32 != 0
+    (dict(r=65), _lib.LORA_EUNSUPPORTED),
+    (dict(r=0), _lib.LORA_EINVAL),
+    (dict(N=0), _lib.LORA_EINVAL),
+    (dict(x=None), _lib.LORA_EINVAL),
+    (dict(b=None), _lib.LORA_EINVAL),
+    (dict(ldx=32), _lib.LORA_EINVAL),
+    (dict(ldo=31), _lib.LORA_EINVAL),
+    (dict(x=0x1002), _lib.LORA_EUNSUPPORTED),       # unaligned rows
+    (dict(workspace_bytes=16), _lib.LORA_EWORKSPACE),
+    (dict(M=0, x=None), _lib.LORA_OK),
+])
+def test_linear_host_validation(kw, code):
+    assert _linear(**kw) == code
+
+
+def test_qkv_host_validation():
+    # every call below is rejected on the host before anything is enqueued (the addresses are
+    # placeholders, never dereferenced)
+    L = _lib.lib()
+    base = [1, 8, 64, 32, 16, 8, 2.0, 0x1000, 64, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000,
+            0x8000, 0x9000, 0xA000, 0xB000, 32, 0xC000, 16, 0xD000, 16, 0x100000, 1 << 30, None]
+    bad = list(base); bad[11] = None  # w_v
+    assert L.lora_qkv_fused(*bad) == _lib.LORA_EINVAL
+    bad = list(base); bad[23] = 15  # ldv < Nkv
+    assert L.lora_qkv_fused(*bad) == _lib.LORA_EINVAL
+    bad = list(base); bad[25] = 64  # workspace too small
+    assert L.lora_qkv_fused(*bad) == _lib.LORA_EWORKSPACE
+    assert _lib.lora_qkv_workspace_size(1, 8, 64, 32, 16, 8) > 0
+    assert _lib.lora_linear_workspace_size(1, 0, 64, 32, 16) == 0
