@@ -307,6 +307,62 @@ def config_qkv(seed: int = 5, M: int = 4096, H: int = 4096, Nq: int = 4096, Nkv:
                    b_q=b_q, a_k=a_k, b_k=b_k, a_v=a_v, b_v=b_v, w_o=w_o, a_o=a_o, b_o=b_o)
 
 
+@dataclass
+class EmbeddingCase:
+    """Multi-adapter embedding LoRA-A problem: token ids, stacked A [L][R][V], segments."""
+
+    name: str
+    dtype: str
+    T: int
+    V: int
+    R: int
+    L: int
+    input_ids: torch.Tensor  # int32 [T] (token order)
+    A: torch.Tensor  # [L][R][V]
+    seg_indptr: torch.Tensor
+    weight_indices: torch.Tensor
+    permutation: torch.Tensor
+    lora_ranks: torch.Tensor
+
+    @property
+    def G(self) -> int:
+        return int(self.weight_indices.numel())
+
+
+def make_embedding(name: str, *, seed: int, T: int, V: int, R: int, L: int, dtype: str,
+                   lengths: str = "uniform", ranks=None, identity_perm: bool = False,
+                   fixed_indptr=None, fixed_weight_indices=None) -> EmbeddingCase:
+    """Seeded embedding LoRA-A inputs: segment lengths, weight_indices and permutation as for
+    make_sgmv, then token ids uniform over the vocabulary (with ids 0 and V-1 forced in), then
+    A ~ N(0, 0.02) with the rows past each adapter's rank zeroed."""
+    rng = np.random.default_rng(seed)
+    if fixed_indptr is not None:
+        indptr = np.asarray(fixed_indptr, dtype=np.int64)
+        widx = np.asarray(fixed_weight_indices, dtype=np.int64)
+    else:
+        G = T if lengths == "ones" else L
+        if lengths == "ones":
+            lens = np.ones(T, dtype=np.int64)
+            widx = rng.integers(0, L, size=G)
+        else:
+            cuts = np.sort(rng.integers(0, T + 1, size=G - 1))
+            lens = np.diff(np.concatenate([[0], cuts, [T]]))
+            widx = rng.permutation(L)[:G]
+        indptr = np.concatenate([[0], np.cumsum(lens)])
+    perm = np.arange(T) if identity_perm else rng.permutation(T)
+    ids = rng.integers(0, V, size=T)
+    if T >= 2:
+        ids[0], ids[-1] = 0, V - 1
+    ranks = np.full(L, R, dtype=np.int64) if ranks is None else np.asarray(ranks, dtype=np.int64)
+    A = _normal(rng, (L, R, V), 0.02, dtype)
+    for a in range(L):
+        A[a, int(ranks[a]):] = 0
+    i32 = lambda v: torch.from_numpy(np.asarray(v, dtype=np.int32))
+    return EmbeddingCase(name=name, dtype=dtype, T=T, V=V, R=R, L=L, input_ids=i32(ids), A=A,
+                         seg_indptr=i32(indptr), weight_indices=i32(widx), permutation=i32(perm),
+                         lora_ranks=i32(ranks))
+
+
 def sweep_case(T: int) -> SgmvCase:
     """One point of the decode-QKV token sweep (same generator and seed as the tok=50 case)."""
     return config_decode_qkv(T=T, seed=1)

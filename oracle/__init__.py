@@ -24,9 +24,10 @@ from .rounding import rho, DTYPE_FORMATS
 from .sgmv import shrink, expand, tile_list, slice_blocks, validate_metadata
 from .mlp import silu, lora_mlp, lora_mlp_rows
 from .linear import lora_linear, lora_qkv, lora_linear_rows
+from .embedding import embedding_lora_a
 
 __all__ = [
     "rho", "DTYPE_FORMATS", "shrink", "expand", "tile_list", "slice_blocks",
     "validate_metadata", "silu", "lora_mlp", "lora_mlp_rows", "lora_linear", "lora_qkv",
-    "lora_linear_rows",
+    "lora_linear_rows", "embedding_lora_a",
 ]

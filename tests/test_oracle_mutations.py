@@ -14,6 +14,7 @@ import pytest
 import oracle.sgmv as sgmv_mod
 import oracle.mlp as mlp_mod
 import oracle.linear as linear_mod
+import oracle.embedding as emb_mod
 import lora_inputs as li
 from oracle import rho
 
@@ -107,3 +108,25 @@ def test_linear_mutation_is_caught(old, new):
     assert np.allclose(good, ref, rtol=1e-11, atol=1e-13)
     bad = _mutant(linear_mod, old, new).lora_linear(c.x, c.w_q, c.a_q, c.b_q, c.scale, "f64")
     assert not np.allclose(bad, ref, rtol=1e-11, atol=1e-13)
+
+
+EMB_MUTATIONS = [
+    ("cols = ids[perm[i0:i1]]", "cols = ids[i0:i1]"),            # forgot the permutation
+    ("h[i0:i1, :r] = A[a, :r][:, cols].T", "h[i0:i1, :r] = A[a, :r][:, cols][::-1].T"),  # rank order
+    ("a = int(widx[g])", "a = g % A.shape[0]"),                  # adapter of the segment ignored
+    ("h[i0:i1, r:] = 0.0", "pass"),                                # rank padding not zeroed
+]
+
+
+@pytest.mark.parametrize("old,new", EMB_MUTATIONS)
+def test_embedding_mutation_is_caught(old, new):
+    from tests.test_oracle_embedding import HERE as H
+
+    with open(os.path.join(H, "golden", "embedding_handworked.json")) as f:
+        d = json.load(f)
+    A = np.array([[[float(e) for e in r] for r in b] for b in d["A"]])
+    args = (d["input_ids"], A, d["seg_indptr"], d["weight_indices"], d["permutation"], d["lora_ranks"], d["R"])
+    exp = np.array(d["h_expected"], dtype=float)
+    assert np.array_equal(emb_mod.embedding_lora_a(*args), exp)
+    got = _mutant(emb_mod, old, new).embedding_lora_a(*args)
+    assert not np.array_equal(got, exp, equal_nan=True)
