@@ -8,7 +8,8 @@ stream. Every step runs in the HIP library; there is no CPU path.
 """
 
 from ._lib import LoraError, lib, lora_version
-from .ops import expand, linear_fused, mlp_fused, qkv_fused, schedule_tiles, shrink
+from .ops import (embedding_a, expand, linear_fused, mlp_fused, qkv_fused, schedule_tiles,
+                  shrink)
 
 __all__ = ["LoraError", "lib", "lora_version", "shrink", "expand", "schedule_tiles", "mlp_fused",
-           "linear_fused", "qkv_fused"]
+           "linear_fused", "qkv_fused", "embedding_a"]

@@ -40,6 +40,8 @@ SIGNATURES = {
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
                               _i64, _vp, _sz, _vp]),
     "lora_qkv_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i64, _i32]),
+    "lora_embedding_a": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _i64, _i64, _i64,
+                                _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
 }
 
 
@@ -159,3 +161,11 @@ def lora_qkv_fused(dtype, M, K, Nq, Nkv, r, scale, x, ldx, w_q, w_k, w_v, a_q, b
 
 def lora_qkv_workspace_size(dtype, M, K, Nq, Nkv, r) -> int:
     return int(lib().lora_qkv_workspace_size(dtype, M, K, Nq, Nkv, r))
+
+
+def lora_embedding_a(dtype, T, V, R, L, G, input_ids, w_a, stride_l, stride_r, stride_v,
+                     seg_indptr, weight_indices, permutation, lora_ranks, h, ldh, stream) -> None:
+    st = lib().lora_embedding_a(dtype, T, V, R, L, G, _p(input_ids), _p(w_a), stride_l, stride_r,
+                                stride_v, _p(seg_indptr), _p(weight_indices), _p(permutation),
+                                _p(lora_ranks), _p(h), ldh, stream)
+    _check("lora_embedding_a", st)

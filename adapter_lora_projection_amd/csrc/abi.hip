@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "../../include/lora_mi355x.h"
+#include "embedding.hpp"
 #include "mlp_kernels.hpp"
 #include "sgmv_kernels.hpp"
 
@@ -546,6 +547,31 @@ lora_status lora_qkv_fused(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, i
   void* os[3] = {q, k, v};
   return linear_fused(dtype, M, K, n, 3, r, scale, x, ldx, ws, as, bs, os, ld, workspace,
                       workspace_bytes, stream);
+}
+
+lora_status lora_embedding_a(lora_dtype dtype, int64_t T, int64_t V, int32_t R, int32_t L,
+                             int32_t G, const int32_t* input_ids, const void* w_a,
+                             int64_t stride_l, int64_t stride_r, int64_t stride_v,
+                             const int32_t* seg_indptr, const int32_t* weight_indices,
+                             const int32_t* permutation, const int32_t* lora_ranks, void* h,
+                             int64_t ldh, void* stream) {
+  if (!valid_dtype(dtype)) return LORA_EUNSUPPORTED;
+  if (T < 0 || G < 0 || R < 1 || V < 1) return LORA_EINVAL;
+  if (R > kMaxRank) return LORA_EUNSUPPORTED;
+  if (T == 0 || G == 0) return LORA_OK;
+  if (L < 1) return LORA_EINVAL;
+  if (T > INT_MAX - 512 || G >= INT_MAX || V >= INT_MAX) return LORA_EUNSUPPORTED;
+  if (!input_ids || !w_a || !seg_indptr || !weight_indices || !lora_ranks || !h) return LORA_EINVAL;
+  if (stride_l < 0 || stride_r < 1 || stride_v < 1 || ldh < R) return LORA_EINVAL;
+  lmx::EmbeddingArgs a{};
+  a.input_ids = input_ids; a.w_a = w_a; a.seg_indptr = seg_indptr; a.weight_indices = weight_indices;
+  a.permutation = permutation; a.lora_ranks = lora_ranks; a.h = h;
+  a.stride_l = stride_l; a.stride_r = stride_r; a.stride_v = stride_v; a.ldh = ldh;
+  a.T = int(T); a.R = R; a.G = G; a.L = L; a.V = int(V);
+  const int es = esize(dtype), ve = 16 / es;
+  const bool vec = stride_r == 1 && R % ve == 0 && ldh % ve == 0 && stride_v % ve == 0 &&
+                   stride_l % ve == 0 && al16(w_a) && al16(h);
+  return hip_status(lmx::launch_embedding_a(a, es, vec, reinterpret_cast<hipStream_t>(stream)));
 }
 
 lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method,

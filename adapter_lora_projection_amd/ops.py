@@ -205,3 +205,32 @@ def qkv_fused(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, scale: float,
                         a_q, b_q, a_k, b_k, a_v, b_v, q, Nq, k, Nkv, v, Nkv, workspace,
                         workspace.numel(), _stream())
     return q, k, v
+
+
+def embedding_a(input_ids, w_a, seg_indptr, weight_indices, permutation, lora_ranks,
+                h: torch.Tensor | None = None) -> torch.Tensor:
+    """h[i] = column input_ids[perm[i]] of the segment's adapter A, rank-padded with zeros
+    (``lora_embedding_a``). input_ids: int32 [T]; w_a: [L][R][V], any strides (a transposed view
+    of [L][V][R] storage is the faster layout); returns h [T][R] in sorted order.
+    permutation=None: identity."""
+    _dev(input_ids, w_a, seg_indptr, weight_indices, permutation, lora_ranks, h)
+    T = input_ids.numel()
+    _meta(input_ids, T, "input_ids")
+    if w_a.dim() != 3 or min(w_a.stride()) < 0 or w_a.stride(1) < 1 or w_a.stride(2) < 1:
+        raise ValueError("w_a must be a [L][R][V] tensor with positive rank and vocabulary strides")
+    L, R, V = w_a.shape
+    G = weight_indices.numel()
+    _meta(seg_indptr, G + 1, "seg_indptr")
+    _meta(weight_indices, None, "weight_indices")
+    if permutation is not None:
+        _meta(permutation, T, "permutation")
+    _meta(lora_ranks, L, "lora_ranks")
+    if h is None:
+        h = torch.empty((T, R), dtype=w_a.dtype, device=w_a.device)
+    dt = dtype_code(w_a)
+    if h.dtype != w_a.dtype:
+        raise TypeError("w_a and h must share a dtype")
+    sl, sr, sv = w_a.stride()
+    _lib.lora_embedding_a(dt, T, V, R, L, G, input_ids, w_a, sl, sr, sv, seg_indptr,
+                          weight_indices, permutation, lora_ranks, h, _rows(h, "h"), _stream())
+    return h

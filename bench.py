@@ -226,6 +226,65 @@ def attention_object(steps: int, warmup: int) -> dict:
                          "kernel": "lora_qkv_fused + lora_linear_fused (all launches)"}}
 
 
+def embedding_object(steps: int, warmup: int) -> dict:
+    """The embedding LoRA-A product (lora_embedding_a) on 16,384 one-token segments (bf16,
+    vocabulary 151,936, 8 adapters of rank 16), A stored [L][V][R] (unit rank stride; the
+    [L][R][V] storage is timed beside it). Algorithmic bytes per call: per token its id and
+    permutation entry (8 B), r values of A read and R values of h written, plus seg_indptr,
+    weight_indices and lora_ranks. K calls back to back after a warm-up, HIP events on the
+    launch stream; roofline against HBM peak."""
+    import torch
+
+    import lora_inputs as li
+    from adapter_lora_projection_amd import _lib
+
+    c = li.make_embedding("emb_16384x1", seed=12, T=16384, V=151936, R=16, L=8, dtype="bf16",
+                          lengths="ones")
+    g = lambda t: t.to("cuda").contiguous()
+    ids, ip, wi, pm, rk = (g(t) for t in (c.input_ids, c.seg_indptr, c.weight_indices,
+                                          c.permutation, c.lora_ranks))
+    a_rv = g(c.A)
+    a_vr = g(c.A.permute(0, 2, 1))  # [L][V][R] storage
+    h = torch.empty((c.T, c.R), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    V, R = c.V, c.R
+    strides = {"vr": (V * R, 1, R), "rv": (R * V, V, 1)}
+    ptrs = {"vr": a_vr.data_ptr(), "rv": a_rv.data_ptr()}
+    ranks = c.lora_ranks.numpy().astype(np.int64)
+    r_tok = ranks[c.weight_indices.numpy()]  # one token per segment
+    algo = int(c.T * 8 + 2 * int(r_tok.sum()) + 2 * c.T * c.R + 4 * (2 * c.G + 1) + 4 * c.L)
+
+    def run(layout):
+        sl, sr, sv = strides[layout]
+
+        def call():
+            _lib.lora_embedding_a(_lib.LORA_BF16, c.T, V, R, c.L, c.G, ids.data_ptr(),
+                                  ptrs[layout], sl, sr, sv, ip.data_ptr(), wi.data_ptr(),
+                                  pm.data_ptr(), rk.data_ptr(), h.data_ptr(), R, stream)
+
+        for _ in range(max(warmup, 20)):
+            call()
+        torch.cuda.synchronize()
+        n = max(steps, 1) * 10
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    us = {lay: run(lay) * 1e3 for lay in ("vr", "rv")}
+    gbps = algo / (us["vr"] * 1e-6) / 1e9
+    return {"workload": "embedding LoRA-A bf16, 16384 one-token segments, V=151936, 8 adapters "
+                        "r16, A stored [L][V][R]",
+            "us_per_call": round(us["vr"], 2), "us_per_call_A_stored_LRV": round(us["rv"], 2),
+            "algorithmic_bytes_per_call": algo, "value": round(gbps, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "embedding_a_kernel (one launch)"}}
+
+
 def cpu_baseline(min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload (host cores): passes
     over the sweep's token counts in order, until at least min_seconds of oracle time."""
@@ -441,6 +500,8 @@ def main() -> int:
         out["mlp"] = mlp_object(args.steps, args.warmup, traffic_table)
         print("[bench] timing the LoRA attention projections", file=sys.stderr, flush=True)
         out["attention_projections"] = attention_object(args.steps, args.warmup)
+        print("[bench] timing the embedding LoRA-A product", file=sys.stderr, flush=True)
+        out["embedding_a"] = embedding_object(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()

@@ -13,6 +13,8 @@
  *     Compatibility checks (dropout 0, one adapter, no bias, unmerged weights).
  *   - lora_linear_fused / lora_qkv_fused: the single-adapter LoRA attention projections (output,
  *     and query/key/value of one x) of the same fast path (pull request 9754).
+ *   - lora_embedding_a: the embedding LoRA-A product of the same LoRA op family (pull request
+ *     550), sized without a longest-segment bound.
  *   - lora_schedule_tiles: export of the device segment schedule (the on-device segment scheduler
  *     named in the Summary of pull request 550) for checking.
  *   - lora_check_metadata: the value checks that pull request 550 (Behaviour changes) moves out of
@@ -219,6 +221,37 @@ lora_status lora_qkv_fused(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, i
 
 size_t lora_qkv_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,
                                int32_t r);
+
+/*
+ * lora_embedding_a -- the LoRA-A product of an embedding layer (the embedding LoRA-A forward of
+ * "Decode LoRA kernels are optimized", Summary and Behaviour changes; the page does not print
+ * the arithmetic, this is its reading): for segment g (adapter a, rank r = lora_ranks[a]) and
+ * sorted position i in it,
+ *     h[i][j] = A[a][j][input_ids[permutation[i]]]   for j < r,   0 for r <= j < R,
+ * the column of the adapter's A at the token's vocabulary id (one-hot row times A^T), copied
+ * bit for bit. No longest-segment bound is needed: the launch is sized from T and G on the host
+ * and no call reads device memory on the host. Rows of h that no segment covers are not written.
+ *
+ *   dtype          element type of A and h.
+ *   T, V, R, L, G  tokens, vocabulary size, padded rank (1 <= R <= 1024), adapters, segments.
+ *   input_ids      device int32 [T] in token order. An id outside [0, V) is a caller error: its
+ *                  row of h gets zeros and A is not read for it.
+ *   w_a            device; A[a][j][v] is the element at a*stride_l + j*stride_r + v*stride_v
+ *                  (element strides; stride_l >= 0, stride_r >= 1, stride_v >= 1). [L][R][V]
+ *                  storage has stride_v = 1; [L][V][R] storage (stride_r = 1) makes each token's
+ *                  values one contiguous run, the faster layout. Elements with j >= lora_ranks[a]
+ *                  are never read. The strides must keep every read inside the caller's buffer.
+ *   seg_indptr, weight_indices, permutation (NULL: identity), lora_ranks: as for lora_shrink
+ *                  (an adapter index or permutation entry out of range also gives a zero row).
+ *   h              device [T][ldh], ldh >= R, sorted order.
+ * One kernel launch of ceil(T / 256) workgroups; no workspace for any segment count.
+ */
+lora_status lora_embedding_a(lora_dtype dtype, int64_t T, int64_t V, int32_t R, int32_t L,
+                             int32_t G, const int32_t* input_ids, const void* w_a,
+                             int64_t stride_l, int64_t stride_r, int64_t stride_v,
+                             const int32_t* seg_indptr, const int32_t* weight_indices,
+                             const int32_t* permutation, const int32_t* lora_ranks, void* h,
+                             int64_t ldh, void* stream);
 
 /*
  * lora_schedule_tiles -- the segment schedule the compute kernels use, exported for checking.

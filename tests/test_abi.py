@@ -195,3 +195,38 @@ def test_qkv_host_validation():
     assert L.lora_qkv_fused(*bad) == _lib.LORA_EWORKSPACE
     assert _lib.lora_qkv_workspace_size(1, 8, 64, 32, 16, 8) > 0
     assert _lib.lora_linear_workspace_size(1, 0, 64, 32, 16) == 0
+
+
+def _emb(**kw):
+    args = dict(dtype=1, T=8, V=100, R=16, L=2, G=2, input_ids=0x1000, w_a=0x2000,
+                stride_l=1600, stride_r=100, stride_v=1, seg_indptr=0x3000, weight_indices=0x4000, permutation=0x5000, lora_ranks=0x6000,
+                h=0x7000, ldh=16, stream=None)
+    args.update(kw)
+    return _lib.lib().lora_embedding_a(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), _lib.LORA_EUNSUPPORTED),
+    (dict(T=-1), _lib.LORA_EINVAL),
+    (dict(R=0), _lib.LORA_EINVAL),
+    (dict(R=2048), _lib.LORA_EUNSUPPORTED),
+    (dict(V=0), _lib.LORA_EINVAL),
+    (dict(L=0), _lib.LORA_EINVAL),
+    (dict(input_ids=None), _lib.LORA_EINVAL),
+    (dict(w_a=None), _lib.LORA_EINVAL),
+    (dict(h=None), _lib.LORA_EINVAL),
+    (dict(stride_l=-1), _lib.LORA_EINVAL),
+    (dict(stride_r=0), _lib.LORA_EINVAL),
+    (dict(stride_v=0), _lib.LORA_EINVAL),
+    (dict(ldh=15), _lib.LORA_EINVAL),
+    (dict(T=(1 << 31) - 100), _lib.LORA_EUNSUPPORTED),
+])
+def test_embedding_host_validation(kw, code):
+    # rejected on the host before anything is enqueued (the addresses are placeholders)
+    assert _emb(**kw) == code
+
+
+def test_embedding_empty_calls_are_no_ops():
+    # nothing to do: returns before touching any pointer
+    assert _emb(T=0) == _lib.LORA_OK
+    assert _emb(G=0) == _lib.LORA_OK
