@@ -256,6 +256,13 @@ def config_mlp(seed: int = 4, M: int = 4096, H: int = 4096, I: int = 12288, r: i
                    a_down=a_down, b_down=b_down)
 
 
+def mlp_dout(seed: int = 4, M: int = 4096, H: int = 4096, dtype: str = "bf16") -> torch.Tensor:
+    """Seeded upstream gradient of the MLP output for the backward, dout ~ N(0,1) [M][H], drawn
+    from its own stream (seed, 1) so the forward inputs of the same seed are unchanged."""
+    rng = np.random.default_rng([seed, 1])
+    return _normal(rng, (M, H), 1.0, dtype)
+
+
 @dataclass
 class QkvCase:
     """Single-adapter LoRA attention projections of one x (nn.Linear [out][in] layouts)."""

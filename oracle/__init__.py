@@ -12,7 +12,8 @@ Sources (pages as titled):
 * "Add optional fast lora path for qwen2/qwen3 on npu" (ms-swift pull request 9754), What this PR
   does and Compatibility checks: the single-adapter LoRA MLP with fused SwiGLU, and the
   single-adapter LoRA attention projections (query/key/value and output), dropout 0, no bias,
-  not merged.
+  not merged; review thread and Verification advice: the MLP backward (saved X and gate/up
+  projections, SwiGLU backward, dX, LoRA weight gradients).
 
 Readings where the pages are silent are listed in each function's docstring.
 
@@ -22,12 +23,13 @@ inputs, hand-worked fixtures, closed forms, invariants and library casts); none 
 
 from .rounding import rho, DTYPE_FORMATS
 from .sgmv import shrink, expand, tile_list, slice_blocks, validate_metadata
-from .mlp import silu, lora_mlp, lora_mlp_rows
+from .mlp import silu, lora_mlp, lora_mlp_rows, sigmoid, silu_grad, lora_mlp_saved, lora_mlp_backward
 from .linear import lora_linear, lora_qkv, lora_linear_rows
 from .embedding import embedding_lora_a
 
 __all__ = [
     "rho", "DTYPE_FORMATS", "shrink", "expand", "tile_list", "slice_blocks",
-    "validate_metadata", "silu", "lora_mlp", "lora_mlp_rows", "lora_linear", "lora_qkv",
+    "validate_metadata", "silu", "lora_mlp", "lora_mlp_rows", "sigmoid", "silu_grad",
+    "lora_mlp_saved", "lora_mlp_backward", "lora_linear", "lora_qkv",
     "lora_linear_rows", "embedding_lora_a",
 ]
