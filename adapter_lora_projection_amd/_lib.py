@@ -33,6 +33,15 @@ SIGNATURES = {
     "lora_mlp_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
     "lora_mlp_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
+    "lora_mlp_fused_train": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                                    _i64, _vp, _sz, _vp]),
+    "lora_mlp_prepare_backward": (_i32, [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "lora_mlp_backward": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
+                                 _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lora_mlp_backward_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
+    "lora_mlp_backward_intermediates": (_i32, [_i64, _i64, _i64, _i32, _vp]),
     "lora_linear_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
                                  _vp, _vp, _i64, _vp, _sz, _vp]),
     "lora_linear_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
@@ -135,6 +144,37 @@ def lora_mlp_workspace_size(dtype, M, H, I, r) -> int:
     return int(lib().lora_mlp_workspace_size(dtype, M, H, I, r))
 
 
+def lora_mlp_fused_train(dtype, M, H, I, r, scale, x, ldx, w_gate, w_up, w_down, a_gate, b_gate,
+                         a_up, b_up, a_down, b_down, out, ldo, e, v, lde, workspace,
+                         workspace_bytes, stream) -> None:
+    st = lib().lora_mlp_fused_train(dtype, M, H, I, r, scale, _p(x), ldx, _p(w_gate), _p(w_up),
+                                    _p(w_down), _p(a_gate), _p(b_gate), _p(a_up), _p(b_up),
+                                    _p(a_down), _p(b_down), _p(out), ldo, _p(e), _p(v), lde,
+                                    _p(workspace), workspace_bytes, stream)
+    _check("lora_mlp_fused_train", st)
+
+
+def lora_mlp_prepare_backward(dtype, H, I, w_gate, w_up, w_down, w_gu_t, w_down_t, stream) -> None:
+    st = lib().lora_mlp_prepare_backward(dtype, H, I, _p(w_gate), _p(w_up), _p(w_down), _p(w_gu_t),
+                                         _p(w_down_t), stream)
+    _check("lora_mlp_prepare_backward", st)
+
+
+def lora_mlp_backward(dtype, M, H, I, r, scale, x, ldx, e, v, lde, dout, lddo, w_gu_t, w_down_t,
+                      a_gate, b_gate, a_up, b_up, a_down, b_down, dx, lddx, da_gate, db_gate,
+                      da_up, db_up, da_down, db_down, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_mlp_backward(dtype, M, H, I, r, scale, _p(x), ldx, _p(e), _p(v), lde, _p(dout),
+                                 lddo, _p(w_gu_t), _p(w_down_t), _p(a_gate), _p(b_gate), _p(a_up),
+                                 _p(b_up), _p(a_down), _p(b_down), _p(dx), lddx, _p(da_gate),
+                                 _p(db_gate), _p(da_up), _p(db_up), _p(da_down), _p(db_down),
+                                 _p(workspace), workspace_bytes, stream)
+    _check("lora_mlp_backward", st)
+
+
+def lora_mlp_backward_workspace_size(dtype, M, H, I, r) -> int:
+    return int(lib().lora_mlp_backward_workspace_size(dtype, M, H, I, r))
+
+
 def lora_tuning_override(op: int, variant: int) -> None:
     lib().lora_tuning_override(op, variant)
 
@@ -169,3 +209,10 @@ def lora_embedding_a(dtype, T, V, R, L, G, input_ids, w_a, stride_l, stride_r, s
                                 stride_v, _p(seg_indptr), _p(weight_indices), _p(permutation),
                                 _p(lora_ranks), _p(h), ldh, stream)
     _check("lora_embedding_a", st)
+
+
+def lora_mlp_backward_intermediates(M, H, I, r) -> tuple[int, list[int]]:
+    """(rp, byte offsets of hmid, [de|dv], [xa_g|xa_u], xa_d, dxa_d, [dxa_g|dxa_u])."""
+    offs = (ctypes.c_size_t * 6)()
+    rp = int(lib().lora_mlp_backward_intermediates(M, H, I, r, offs))
+    return rp, [int(o) for o in offs]

@@ -204,6 +204,92 @@ LinearLayout linear_layout(int64_t M, int64_t K, const int64_t* N, int P, int32_
   return L;
 }
 
+lora_status mlp_forward(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r, float scale,
+                        const void* x, int64_t ldx, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* a_gate, const void* b_gate,
+                        const void* a_up, const void* b_up, const void* a_down,
+                        const void* b_down, void* out, int64_t ldo, void* e_save, void* v_save,
+                        int64_t lde, void* workspace, size_t workspace_bytes, void* stream);
+
+// Workspace of the LoRA MLP backward: byte offsets of the transposed / scaled LoRA operands, the
+// recomputed LoRA-A products, the gradient intermediates and the partial sums.
+struct MlpBwdLayout {
+  int64_t rp;
+  ShrinkWs s_x, r_x;   // [xa_g | xa_u] from x (plans for aligned / unaligned A)
+  ShrinkWs s_w;        // products against operands in the workspace (always aligned): K = H
+  ShrinkWs s_i, r_i;   // products over K = I (xa_d from hmid; dxa_g, dxa_u from de, dv)
+  lmx::ColJobs cj;     // geometry of the sums over tokens (pointers set at call time)
+  size_t sbdt, sbgt, sbut, adt, agut, xa_gu, dxa_d, xa_d, dxa_gu, hmid, dedv, part, colpart, total;
+};
+
+lmx::ColJobs mlp_bwd_coljobs(int64_t M, int64_t H, int64_t I, int32_t r) {
+  lmx::ColJobs j{};
+  j.n = 6;
+  j.M = int(M);
+  const int64_t C[6] = {H, H, I, I, I, H};
+  int64_t blocks = 0;
+  for (int q = 0; q < 6; ++q) {
+    j.job[q].C = int(C[q]);
+    j.job[q].nq = r;
+    blocks += cdiv(C[q], 1024);
+  }
+  const int64_t jb = cdiv(r, 16);
+  // about 512 workgroups, chunks of at least 64 rows
+  j.chunks = int(std::max<int64_t>(1, std::min<int64_t>(cdiv(512, blocks * jb), M / 64)));
+  return j;
+}
+
+MlpBwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
+  MlpBwdLayout L{};
+  L.rp = cdiv(r, 32) * 32;
+  const int rp = int(L.rp);
+  L.s_x = shrink_ws(LORA_BF16, M, H, 2, rp, 0, prefer_lds(M, H, 2, rp));
+  L.r_x = shrink_ws(LORA_BF16, M, H, 2, rp, 0, false);
+  L.s_w = shrink_ws(LORA_BF16, M, H, 1, rp, 0, prefer_lds(M, H, 1, rp));
+  L.s_i = shrink_ws(LORA_BF16, M, I, 1, rp, 0, prefer_lds(M, I, 1, rp));
+  L.r_i = shrink_ws(LORA_BF16, M, I, 1, rp, 0, false);
+  L.cj = mlp_bwd_coljobs(M, H, I, r);
+  size_t off = 0;
+  L.sbdt = off; off += align256(size_t(r) * H * 2);
+  L.sbgt = off; off += align256(size_t(r) * I * 2);
+  L.sbut = off; off += align256(size_t(r) * I * 2);
+  L.adt = off; off += align256(size_t(I) * L.rp * 2);
+  L.agut = off; off += align256(size_t(H) * 2 * L.rp * 2);
+  L.xa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
+  L.dxa_d = off; off += align256(size_t(M) * L.rp * 2);
+  L.xa_d = off; off += align256(size_t(M) * L.rp * 2);
+  L.dxa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
+  L.hmid = off; off += align256(size_t(M) * I * 2);
+  L.dedv = off; off += align256(size_t(M) * 2 * I * 2);
+  size_t sp = 0;
+  for (const ShrinkWs* w : {&L.s_x, &L.r_x, &L.s_w, &L.s_i, &L.r_i}) sp = std::max(sp, w->total - w->part);
+  L.part = off; off += align256(sp);
+  L.colpart = off; off += align256(lmx::colred_partial_floats(L.cj) * 4);
+  L.total = off;
+  return L;
+}
+
+// One dense LoRA-A product h = round(x A^T) (one segment; S slices of padded rank rp, true rank
+// r): the LDS-staged plan when A is aligned, else the register-ring plan.
+hipError_t dense_shrink(const void* x, int64_t ldx, int64_t K, int S, const void* const* A,
+                        int64_t lda, int64_t M, int rp, int r, void* h, int64_t ldh,
+                        const ShrinkWs& s_al, const ShrinkWs& s_un, void* part, hipStream_t st) {
+  bool al = true;
+  for (int q = 0; q < S; ++q) al = al && al16(A[q]);
+  const ShrinkWs& sp = al ? s_al : s_un;
+  lmx::ShrinkArgs a{};
+  a.x = x; a.ldx = ldx; a.K = K; a.S = S; a.R = rp; a.G = 1; a.T = int(M);
+  a.dense_rank = r; a.w_a = A[0]; a.lda = lda;
+  for (int q = 0; q < S; ++q) a.w_a_slice[q] = A[q];
+  a.h = h; a.ldh = ldh;
+  a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp; a.sk_unit = sp.unit;
+  a.part = static_cast<float*>(part);
+  lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
+  hipError_t e = lmx::launch_shrink(LORA_BF16, a, plan, st);
+  if (e == hipSuccess && sp.q > 0) e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st);
+  return e;
+}
+
 // The shared body of lora_linear_fused (P = 1) and lora_qkv_fused (P = 3).
 lora_status linear_fused(lora_dtype dtype, int64_t M, int64_t K, const int64_t* N, int P,
                          int32_t r, float scale, const void* x, int64_t ldx, const void* const* w,
@@ -270,7 +356,7 @@ lora_status linear_fused(lora_dtype dtype, int64_t M, int64_t K, const int64_t* 
     g.B2 = reinterpret_cast<const uint16_t*>(ws + L.lb[p]); g.ldb2 = rp;
     g.C = static_cast<uint16_t*>(out[p]); g.ldc = ldo[p];
     g.M = int(M); g.N = int(N[p]); g.K = int(K); g.K2 = int(rp);
-    if (lmx::launch_gemm_lora(g, false, st) != hipSuccess) return LORA_EHIP;
+    if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;
   }
   return LORA_OK;
 }
@@ -422,7 +508,35 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
                            const void* b_gate, const void* a_up, const void* b_up,
                            const void* a_down, const void* b_down, void* out, int64_t ldo,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (dtype != LORA_BF16) return valid_dtype(dtype) ? LORA_EUNSUPPORTED : LORA_EUNSUPPORTED;
+  return mlp_forward(dtype, M, H, I, r, scale, x, ldx, w_gate, w_up, w_down, a_gate, b_gate, a_up,
+                     b_up, a_down, b_down, out, ldo, nullptr, nullptr, 0, workspace,
+                     workspace_bytes, stream);
+}
+
+lora_status lora_mlp_fused_train(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r,
+                                 float scale, const void* x, int64_t ldx, const void* w_gate,
+                                 const void* w_up, const void* w_down, const void* a_gate,
+                                 const void* b_gate, const void* a_up, const void* b_up,
+                                 const void* a_down, const void* b_down, void* out, int64_t ldo,
+                                 void* e, void* v, int64_t lde, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (M > 0 && (!e || !v)) return LORA_EINVAL;
+  if (M > 0 && lde < I) return LORA_EINVAL;
+  return mlp_forward(dtype, M, H, I, r, scale, x, ldx, w_gate, w_up, w_down, a_gate, b_gate, a_up,
+                     b_up, a_down, b_down, out, ldo, e, v, lde, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+lora_status mlp_forward(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r, float scale,
+                        const void* x, int64_t ldx, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* a_gate, const void* b_gate,
+                        const void* a_up, const void* b_up, const void* a_down,
+                        const void* b_down, void* out, int64_t ldo, void* e_save, void* v_save,
+                        int64_t lde, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
   if (M < 0 || H < 1 || I < 1 || r < 1) return LORA_EINVAL;
   if (r > 64 || H % 32 != 0 || I % 32 != 0) return LORA_EUNSUPPORTED;
   if (M >= INT_MAX || H >= INT_MAX / 4 || I >= INT_MAX / 4) return LORA_EUNSUPPORTED;
@@ -477,7 +591,9 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
     g.A = u16(x); g.lda = ldx; g.W0 = u16(w_gate); g.W1 = u16(w_up); g.ldw = H;
     g.A2 = xa_gu; g.lda2 = 2 * rp; g.B2 = lb_gu; g.ldb2 = 2 * rp;
     g.C = hmid; g.ldc = I; g.M = int(M); g.N = int(I); g.K = int(H); g.K2 = int(2 * rp);
-    if ((e = lmx::launch_gemm_lora(g, true, st)) != hipSuccess) return LORA_EHIP;
+    g.E = static_cast<uint16_t*>(e_save); g.V = static_cast<uint16_t*>(v_save); g.lde = lde;
+    const int mode = e_save != nullptr ? lmx::kGemmSwigluSave : lmx::kGemmSwiglu;
+    if ((e = lmx::launch_gemm_lora(g, mode, st)) != hipSuccess) return LORA_EHIP;
   }
   // 4. xa_d = round(hmid A_d^T)
   {
@@ -501,7 +617,165 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
     g.A2 = xa_d; g.lda2 = rp; g.B2 = lb_d; g.ldb2 = rp;
     g.C = static_cast<uint16_t*>(out); g.ldc = ldo; g.M = int(M); g.N = int(H); g.K = int(I);
     g.K2 = int(rp);
-    if ((e = lmx::launch_gemm_lora(g, false, st)) != hipSuccess) return LORA_EHIP;
+    if ((e = lmx::launch_gemm_lora(g, lmx::kGemmPlain, st)) != hipSuccess) return LORA_EHIP;
+  }
+  return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status lora_mlp_prepare_backward(lora_dtype dtype, int64_t H, int64_t I, const void* w_gate,
+                                      const void* w_up, const void* w_down, void* w_gu_t,
+                                      void* w_down_t, void* stream) {
+  if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
+  if (H < 1 || I < 1) return LORA_EINVAL;
+  if (H >= INT_MAX / 4 || I >= INT_MAX / 4) return LORA_EUNSUPPORTED;
+  if (H > 65535 * 64 || I > 65535 * 64) return LORA_EUNSUPPORTED;  // transpose grid rows
+  if (!w_gate || !w_up || !w_down || !w_gu_t || !w_down_t) return LORA_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  uint16_t* gu = static_cast<uint16_t*>(w_gu_t);
+  // [W_g^T | W_u^T] as [H][2I], and W_d^T as [I][H]
+  if (lmx::launch_transpose(u16(w_gate), H, gu, 2 * I, int(I), int(H), st) != hipSuccess ||
+      lmx::launch_transpose(u16(w_up), H, gu + I, 2 * I, int(I), int(H), st) != hipSuccess ||
+      lmx::launch_transpose(u16(w_down), I, static_cast<uint16_t*>(w_down_t), H, int(H), int(I),
+                            st) != hipSuccess)
+    return LORA_EHIP;
+  return LORA_OK;
+}
+
+int32_t lora_mlp_backward_intermediates(int64_t M, int64_t H, int64_t I, int32_t r,
+                                        size_t* offsets) {
+  if (M <= 0 || H <= 0 || I <= 0 || r <= 0 || r > 64 || offsets == nullptr) return 0;
+  const MlpBwdLayout L = mlp_bwd_layout(M, H, I, r);
+  offsets[0] = L.hmid;
+  offsets[1] = L.dedv;
+  offsets[2] = L.xa_gu;
+  offsets[3] = L.xa_d;
+  offsets[4] = L.dxa_d;
+  offsets[5] = L.dxa_gu;
+  return int32_t(L.rp);
+}
+
+size_t lora_mlp_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I,
+                                        int32_t r) {
+  (void)dtype;
+  if (M <= 0 || H <= 0 || I <= 0 || r <= 0 || r > 64) return 0;
+  return mlp_bwd_layout(M, H, I, r).total;
+}
+
+lora_status lora_mlp_backward(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r,
+                              float scale, const void* x, int64_t ldx, const void* e_saved,
+                              const void* v_saved, int64_t lde, const void* dout, int64_t lddo,
+                              const void* w_gu_t, const void* w_down_t, const void* a_gate,
+                              const void* b_gate, const void* a_up, const void* b_up,
+                              const void* a_down, const void* b_down, void* dx, int64_t lddx,
+                              void* da_gate, void* db_gate, void* da_up, void* db_up,
+                              void* da_down, void* db_down, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
+  if (M < 0 || H < 1 || I < 1 || r < 1) return LORA_EINVAL;
+  if (r > 64 || H % 32 != 0 || I % 32 != 0) return LORA_EUNSUPPORTED;
+  if (M >= INT_MAX || H >= INT_MAX / 8 || I >= INT_MAX / 8) return LORA_EUNSUPPORTED;
+  if (M == 0) return LORA_OK;
+  if (!x || !e_saved || !v_saved || !dout || !w_gu_t || !w_down_t || !a_gate || !b_gate || !a_up ||
+      !b_up || !a_down || !b_down || !dx || !da_gate || !db_gate || !da_up || !db_up || !da_down ||
+      !db_down)
+    return LORA_EINVAL;
+  if (ldx < H || lde < I || lddo < H || lddx < H) return LORA_EINVAL;
+  if (dx == x || dx == dout) return LORA_EINVAL;  // the saved input is never overwritten
+  if (!al16(x) || (ldx * 2) % 16 != 0 || !al16(dout) || (lddo * 2) % 16 != 0 || !al16(w_gu_t) ||
+      !al16(w_down_t))
+    return LORA_EUNSUPPORTED;
+  const MlpBwdLayout L = mlp_bwd_layout(M, H, I, r);
+  if (workspace == nullptr || workspace_bytes < L.total || !al16(workspace)) return LORA_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto W = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  const int rp = int(L.rp);
+  uint16_t *sbdt = W(L.sbdt), *sbgt = W(L.sbgt), *sbut = W(L.sbut), *adt = W(L.adt);
+  uint16_t *agut = W(L.agut), *xa_gu = W(L.xa_gu), *dxa_d = W(L.dxa_d), *xa_d = W(L.xa_d);
+  uint16_t *dxa_gu = W(L.dxa_gu), *hmid = W(L.hmid), *dedv = W(L.dedv);
+  void* part = ws + L.part;
+  // 1. operands: s B_d^T [r][H], s B_g^T, s B_u^T [r][I]; A_d^T [I][rp]; [A_g^T | A_u^T] [H][2 rp]
+  {
+    lmx::TJobs t{};
+    t.n = 6;
+    t.job[0] = {u16(b_down), r, sbdt, H, r, int(H), 0, int(H), scale};
+    t.job[1] = {u16(b_gate), r, sbgt, I, r, int(I), 0, int(I), scale};
+    t.job[2] = {u16(b_up), r, sbut, I, r, int(I), 0, int(I), scale};
+    t.job[3] = {u16(a_down), I, adt, rp, int(I), rp, 0, r, 1.0f};
+    t.job[4] = {u16(a_gate), H, agut, 2 * rp, int(H), rp, 0, r, 1.0f};
+    t.job[5] = {u16(a_up), H, agut + rp, 2 * rp, int(H), rp, 0, r, 1.0f};
+    if (lmx::launch_small_transposes(t, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 2. [xa_g | xa_u] = round(x [A_g; A_u]^T)
+  {
+    const void* A[2] = {a_gate, a_up};
+    if (dense_shrink(x, ldx, H, 2, A, H, M, rp, r, xa_gu, 2 * rp, L.s_x, L.r_x, part, st) != hipSuccess)
+      return LORA_EHIP;
+  }
+  // 3. dxa_d = round(dout (s B_d))
+  {
+    const void* A[1] = {sbdt};
+    if (dense_shrink(dout, lddo, H, 1, A, H, M, rp, r, dxa_d, rp, L.s_w, L.s_w, part, st) != hipSuccess)
+      return LORA_EHIP;
+  }
+  // 4. dhmid = dout W_d + dxa_d A_d with the SwiGLU backward in the epilogue:
+  //    hmid = round(silu(e) v), de = round(dhmid v silu'(e)), dv = round(dhmid silu(e))
+  {
+    lmx::GemmArgs g{};
+    g.A = u16(dout); g.lda = lddo; g.W0 = u16(w_down_t); g.W1 = u16(w_down_t); g.ldw = H;
+    g.A2 = dxa_d; g.lda2 = rp; g.B2 = adt; g.ldb2 = rp;
+    g.C = hmid; g.ldc = I;
+    g.E = const_cast<uint16_t*>(u16(e_saved)); g.V = const_cast<uint16_t*>(u16(v_saved)); g.lde = lde;
+    g.D = dedv; g.ldd = 2 * I;
+    g.M = int(M); g.N = int(I); g.K = int(H); g.K2 = rp;
+    if (lmx::launch_gemm_lora(g, lmx::kGemmSwigluBwd, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 5. xa_d = round(hmid A_d^T)
+  {
+    const void* A[1] = {a_down};
+    if (dense_shrink(hmid, I, I, 1, A, I, M, rp, r, xa_d, rp, L.s_i, L.r_i, part, st) != hipSuccess)
+      return LORA_EHIP;
+  }
+  // 6. dxa_g = round(de (s B_g)), dxa_u = round(dv (s B_u))
+  {
+    const void* Ag[1] = {sbgt};
+    const void* Au[1] = {sbut};
+    if (dense_shrink(dedv, 2 * I, I, 1, Ag, I, M, rp, r, dxa_gu, 2 * rp, L.s_i, L.s_i, part, st) != hipSuccess ||
+        dense_shrink(dedv + I, 2 * I, I, 1, Au, I, M, rp, r, dxa_gu + rp, 2 * rp, L.s_i, L.s_i, part, st) != hipSuccess)
+      return LORA_EHIP;
+  }
+  // 7. LoRA weight gradients (sums over the M tokens)
+  {
+    lmx::ColJobs j = L.cj;
+    auto set = [&](int q, const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, void* out,
+                   int64_t osc, int64_t osj, float sc) {
+      j.job[q].P = P; j.job[q].ldp = ldp; j.job[q].Q = Q; j.job[q].ldq = ldq;
+      j.job[q].out = static_cast<uint16_t*>(out); j.job[q].osc = osc; j.job[q].osj = osj;
+      j.job[q].scale = sc;
+    };
+    set(0, u16(x), ldx, dxa_gu, 2 * rp, da_gate, 1, H, 1.0f);          // dA_g = dxa_g^T x
+    set(1, u16(x), ldx, dxa_gu + rp, 2 * rp, da_up, 1, H, 1.0f);       // dA_u = dxa_u^T x
+    set(2, dedv, 2 * I, xa_gu, 2 * rp, db_gate, r, 1, scale);          // dB_g = s de^T xa_g
+    set(3, dedv + I, 2 * I, xa_gu + rp, 2 * rp, db_up, r, 1, scale);   // dB_u = s dv^T xa_u
+    set(4, hmid, I, dxa_d, rp, da_down, 1, I, 1.0f);                   // dA_d = dxa_d^T hmid
+    set(5, u16(dout), lddo, xa_d, rp, db_down, r, 1, scale);           // dB_d = s dout^T xa_d
+    if (lmx::launch_colred(j, reinterpret_cast<float*>(ws + L.colpart), st) != hipSuccess)
+      return LORA_EHIP;
+  }
+  // 8. dx = round(de W_g + dv W_u + dxa_g A_g + dxa_u A_u)
+  {
+    lmx::GemmArgs g{};
+    g.A = dedv; g.lda = 2 * I; g.W0 = u16(w_gu_t); g.W1 = u16(w_gu_t); g.ldw = 2 * I;
+    g.A2 = dxa_gu; g.lda2 = 2 * rp; g.B2 = agut; g.ldb2 = 2 * rp;
+    g.C = static_cast<uint16_t*>(dx); g.ldc = lddx;
+    g.M = int(M); g.N = int(H); g.K = int(2 * I); g.K2 = 2 * rp;
+    if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;
   }
   return LORA_OK;
 }

@@ -54,8 +54,9 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 
 }  // namespace
 
-template <bool SWIGLU>
+template <int MODE>
 __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
+  constexpr bool SWIGLU = MODE == kGemmSwiglu || MODE == kGemmSwigluSave;
   // One LDS array per pipeline stage.
   __shared__ __attribute__((aligned(1024))) uint16_t stg[kStages][kStageElems];
   auto stage = [&](auto sc) -> uint16_t* {
@@ -266,10 +267,40 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
         for (int v = 0; v < 16; ++v) {
           const int row = rbase + 8 * (v >> 2) + rq + (v & 3);
           const float g = acc[rb][cb][v], u = acc[rb][cb + 2][v];
-          if (row < p.M) p.C[int64_t(row) * p.ldc + n] = Traits<DT_BF16>::from_f32(silu(g) * u);
+          if (row < p.M) {
+            p.C[int64_t(row) * p.ldc + n] = Traits<DT_BF16>::from_f32(silu(g) * u);
+            if constexpr (MODE == kGemmSwigluSave) {
+              p.E[int64_t(row) * p.lde + n] = Traits<DT_BF16>::from_f32(g);
+              p.V[int64_t(row) * p.lde + n] = Traits<DT_BF16>::from_f32(u);
+            }
+          }
         }
       }
     }
+  } else if constexpr (MODE == kGemmSwigluBwd) {
+    // acc = dhmid; e, v = saved pre-activations; f = silu(e) = e sigmoid(e),
+    // silu'(e) = sigmoid(e) (1 + e (1 - sigmoid(e))). The element loop is expanded at compile
+    // time (the unroller declines this body, and a runtime index would move acc to scratch).
+    auto elem = [&](auto rbc, auto cbc, auto vc) {
+      constexpr int rb = decltype(rbc)::value, cb = decltype(cbc)::value, v = decltype(vc)::value;
+      const int n = col_base + cb * 32 + lr;
+      const int row = m0 + wi * 128 + rb * 32 + 8 * (v >> 2) + rq + (v & 3);
+      if (n >= p.N || row >= p.M) return;
+      const float dh = acc[rb][cb][v];
+      const float z = Traits<DT_BF16>::to_f32(p.E[int64_t(row) * p.lde + n]);
+      const float u = Traits<DT_BF16>::to_f32(p.V[int64_t(row) * p.lde + n]);
+      const float ex = __expf(-z);
+      const float sg = 1.0f / (1.0f + ex);
+      const float f = z / (1.0f + ex);
+      p.C[int64_t(row) * p.ldc + n] = Traits<DT_BF16>::from_f32(f * u);
+      p.D[int64_t(row) * p.ldd + n] =
+          Traits<DT_BF16>::from_f32(dh * u * (sg * (1.0f + z * (1.0f - sg))));
+      p.D[int64_t(row) * p.ldd + p.N + n] = Traits<DT_BF16>::from_f32(dh * f);
+    };
+    [&]<int... ii>(std::integer_sequence<int, ii...>) {
+      (elem(std::integral_constant<int, ii / 64>{}, std::integral_constant<int, (ii / 16) % 4>{},
+            std::integral_constant<int, ii % 16>{}), ...);
+    }(std::make_integer_sequence<int, 256>{});
   } else {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -319,14 +350,22 @@ hipError_t launch_scale_lora_b(const ScaleJobs& jobs, float scale, int r, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_lora(const GemmArgs& a, bool swiglu, hipStream_t st) {
+hipError_t launch_gemm_lora(const GemmArgs& a, int mode, hipStream_t st) {
+  const bool swiglu = mode == kGemmSwiglu || mode == kGemmSwigluSave;
   const int nbm = (a.M + kBM - 1) / kBM;
   const int nbn = swiglu ? (a.N + 127) / 128 : (a.N + 255) / 256;
   dim3 grid(nbm * nbn);
-  if (swiglu)
-    hipLaunchKernelGGL(gemm_lora_kernel<true>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(gemm_lora_kernel<false>, grid, dim3(256), 0, st, a);
+  switch (mode) {
+    case kGemmPlain: hipLaunchKernelGGL(gemm_lora_kernel<kGemmPlain>, grid, dim3(256), 0, st, a); break;
+    case kGemmSwiglu: hipLaunchKernelGGL(gemm_lora_kernel<kGemmSwiglu>, grid, dim3(256), 0, st, a); break;
+    case kGemmSwigluSave:
+      hipLaunchKernelGGL(gemm_lora_kernel<kGemmSwigluSave>, grid, dim3(256), 0, st, a);
+      break;
+    case kGemmSwigluBwd:
+      hipLaunchKernelGGL(gemm_lora_kernel<kGemmSwigluBwd>, grid, dim3(256), 0, st, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -159,6 +159,115 @@ def mlp_fused(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_dow
     return out
 
 
+def _mlp_shapes(x, w_gate, a_gate):
+    M, H = x.shape
+    return M, H, w_gate.shape[0], a_gate.shape[0]
+
+
+def mlp_fused_train(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_down,
+                    scale: float, workspace: torch.Tensor | None = None):
+    """The training forward (``lora_mlp_fused_train``): returns (out, e, v) where e and v are the
+    gate and up pre-activations (bf16 [M][I]) the backward reads."""
+    _dev(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_down, workspace)
+    M, H, I, r = _mlp_shapes(x, w_gate, a_gate)
+    for t, shape, name in ((w_gate, (I, H), "w_gate"), (w_up, (I, H), "w_up"), (w_down, (H, I), "w_down"),
+                           (a_gate, (r, H), "a_gate"), (a_up, (r, H), "a_up"), (a_down, (r, I), "a_down"),
+                           (b_gate, (I, r), "b_gate"), (b_up, (I, r), "b_up"), (b_down, (H, r), "b_down")):
+        _bf16_mat(t, shape, name)
+    out = torch.empty((M, H), dtype=x.dtype, device=x.device)
+    e = torch.empty((M, I), dtype=x.dtype, device=x.device)
+    v = torch.empty((M, I), dtype=x.dtype, device=x.device)
+    nbytes = _lib.lora_mlp_workspace_size(_lib.LORA_BF16, M, H, I, r)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _lib.lora_mlp_fused_train(_lib.LORA_BF16, M, H, I, r, float(scale), x, _rows(x, "x"), w_gate,
+                              w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_down, out, H, e,
+                              v, I, workspace, workspace.numel(), _stream())
+    return out, e, v
+
+
+def mlp_prepare_backward(w_gate, w_up, w_down):
+    """The frozen weights as the backward reads them (``lora_mlp_prepare_backward``): returns
+    (w_gu_t [H][2I] = [W_g^T | W_u^T], w_down_t [I][H] = W_d^T). Done once per layer."""
+    _dev(w_gate, w_up, w_down)
+    I, H = w_gate.shape
+    _bf16_mat(w_gate, (I, H), "w_gate")
+    _bf16_mat(w_up, (I, H), "w_up")
+    _bf16_mat(w_down, (H, I), "w_down")
+    w_gu_t = torch.empty((H, 2 * I), dtype=torch.bfloat16, device=w_gate.device)
+    w_down_t = torch.empty((I, H), dtype=torch.bfloat16, device=w_gate.device)
+    _lib.lora_mlp_prepare_backward(_lib.LORA_BF16, H, I, w_gate, w_up, w_down, w_gu_t, w_down_t,
+                                   _stream())
+    return w_gu_t, w_down_t
+
+
+def mlp_backward(x, e, v, dout, w_gu_t, w_down_t, a_gate, b_gate, a_up, b_up, a_down, b_down,
+                 scale: float, workspace: torch.Tensor | None = None,
+                 return_intermediates: bool = False):
+    """Gradients of the LoRA MLP (``lora_mlp_backward``): dict with dx [M][H], da_gate, da_up
+    [r][H], db_gate, db_up [I][r], da_down [r][I], db_down [H][r] (bf16). x must not be the
+    storage of any output (it is only read). return_intermediates: also return the stored
+    intermediates (views into the workspace, ``lora_mlp_backward_intermediates``)."""
+    _dev(x, e, v, dout, w_gu_t, w_down_t, a_gate, b_gate, a_up, b_up, a_down, b_down, workspace)
+    M, H = x.shape
+    I, r = w_down_t.shape[0], a_gate.shape[0]
+    for t, shape, name in ((w_gu_t, (H, 2 * I), "w_gu_t"), (w_down_t, (I, H), "w_down_t"),
+                           (a_gate, (r, H), "a_gate"), (a_up, (r, H), "a_up"), (a_down, (r, I), "a_down"),
+                           (b_gate, (I, r), "b_gate"), (b_up, (I, r), "b_up"), (b_down, (H, r), "b_down"),
+                           (e, (M, I), "e"), (v, (M, I), "v"), (dout, (M, H), "dout")):
+        _bf16_mat(t, shape, name)
+    dev, bf = x.device, torch.bfloat16
+    g = {"dx": torch.empty((M, H), dtype=bf, device=dev),
+         "da_gate": torch.empty((r, H), dtype=bf, device=dev),
+         "db_gate": torch.empty((I, r), dtype=bf, device=dev),
+         "da_up": torch.empty((r, H), dtype=bf, device=dev),
+         "db_up": torch.empty((I, r), dtype=bf, device=dev),
+         "da_down": torch.empty((r, I), dtype=bf, device=dev),
+         "db_down": torch.empty((H, r), dtype=bf, device=dev)}
+    nbytes = _lib.lora_mlp_backward_workspace_size(_lib.LORA_BF16, M, H, I, r)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _lib.lora_mlp_backward(_lib.LORA_BF16, M, H, I, r, float(scale), x, _rows(x, "x"), e, v, I,
+                           dout, H, w_gu_t, w_down_t, a_gate, b_gate, a_up, b_up, a_down, b_down,
+                           g["dx"], H, g["da_gate"], g["db_gate"], g["da_up"], g["db_up"],
+                           g["da_down"], g["db_down"], workspace, workspace.numel(), _stream())
+    if not return_intermediates:
+        return g
+    rp, offs = _lib.lora_mlp_backward_intermediates(M, H, I, r)
+
+    def view(k, cols):
+        return workspace[offs[k]: offs[k] + M * cols * 2].view(torch.bfloat16).view(M, cols)
+
+    dedv, xa_gu, dxa_gu = view(1, 2 * I), view(2, 2 * rp), view(5, 2 * rp)
+    inter = {"hmid": view(0, I), "de": dedv[:, :I], "dv": dedv[:, I:],
+             "xa_g": xa_gu[:, :r], "xa_u": xa_gu[:, rp:rp + r], "xa_d": view(3, rp)[:, :r],
+             "dxa_d": view(4, rp)[:, :r], "dxa_g": dxa_gu[:, :r], "dxa_u": dxa_gu[:, rp:rp + r]}
+    return g, inter
+
+
+class LoraMlpFunction(torch.autograd.Function):
+    """autograd wrapper of the LoRA MLP: forward = lora_mlp_fused_train (saving x, e, v),
+    backward = lora_mlp_backward. The frozen weights take no gradient; their backward layout
+    (from mlp_prepare_backward) is passed in. x is saved and never written."""
+
+    @staticmethod
+    def forward(ctx, x, a_gate, b_gate, a_up, b_up, a_down, b_down, w_gate, w_up, w_down, w_gu_t,
+                w_down_t, scale):
+        out, e, v = mlp_fused_train(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down,
+                                    b_down, scale)
+        ctx.save_for_backward(x, e, v, a_gate, b_gate, a_up, b_up, a_down, b_down, w_gu_t, w_down_t)
+        ctx.scale = scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, e, v, a_gate, b_gate, a_up, b_up, a_down, b_down, w_gu_t, w_down_t = ctx.saved_tensors
+        g = mlp_backward(x, e, v, dout.contiguous(), w_gu_t, w_down_t, a_gate, b_gate, a_up, b_up,
+                         a_down, b_down, ctx.scale)
+        return (g["dx"], g["da_gate"], g["db_gate"], g["da_up"], g["db_up"], g["da_down"],
+                g["db_down"], None, None, None, None, None, None)
+
+
 def _bf16_mat(t, shape, name):
     if tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != torch.bfloat16:
         raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")

@@ -8,6 +8,8 @@
  *     GEMM whose epilogue applies the adapter scaling and the per-slice column offsets, driven by
  *     seg_indptr / weight_indices / permutation / slice offsets. The weight operand is stored
  *     [out][in] row-major, as in the masked operand load shown in that page's review thread.
+ *   - lora_mlp_fused_train / lora_mlp_prepare_backward / lora_mlp_backward: the training
+ *     forward (storing the gate and up pre-activations) and the gradients of the same MLP.
  *   - lora_mlp_fused: the single-adapter LoRA MLP with fused SwiGLU of "Add optional fast lora
  *     path for qwen2/qwen3 on npu" (ms-swift pull request 9754), What this PR does and
  *     Compatibility checks (dropout 0, one adapter, no bias, unmerged weights).
@@ -174,6 +176,86 @@ lora_status lora_mlp_fused(lora_dtype dtype, int64_t M, int64_t H, int64_t I, in
                            void* workspace, size_t workspace_bytes, void* stream);
 
 size_t lora_mlp_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r);
+
+/*
+ * lora_mlp_fused_train -- lora_mlp_fused that also stores what the backward needs: the gate and
+ * up pre-activations e = round(g), v = round(u) (bf16 [M][lde], lde >= I), the saved gate and up
+ * projections of the fast path's backward ("Add optional fast lora path for qwen2/qwen3 on npu",
+ * review thread: the backward reads the saved X and gate/up projections). out is computed exactly
+ * as by lora_mlp_fused; the same workspace size applies. Errors as lora_mlp_fused, plus
+ * LORA_EINVAL for a NULL e or v or lde < I.
+ */
+lora_status lora_mlp_fused_train(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r,
+                                 float scale, const void* x, int64_t ldx, const void* w_gate,
+                                 const void* w_up, const void* w_down, const void* a_gate,
+                                 const void* b_gate, const void* a_up, const void* b_up,
+                                 const void* a_down, const void* b_down, void* out, int64_t ldo,
+                                 void* e, void* v, int64_t lde, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * lora_mlp_prepare_backward -- the frozen weights in the layout the backward reads, written once
+ * per layer (the weights take no gradient): w_gu_t = [W_g^T | W_u^T] as bf16 [H][2I] and
+ * w_down_t = W_d^T as bf16 [I][H], both packed and 16-byte aligned, from the nn.Linear weights
+ * w_gate, w_up [I][H] and w_down [H][I] (packed). The backward's products then reduce over
+ * contiguous rows as the forward's do. Errors: LORA_EUNSUPPORTED for a dtype other than bf16,
+ * LORA_EINVAL for a NULL pointer or H, I < 1.
+ */
+lora_status lora_mlp_prepare_backward(lora_dtype dtype, int64_t H, int64_t I, const void* w_gate,
+                                      const void* w_up, const void* w_down, void* w_gu_t,
+                                      void* w_down_t, void* stream);
+
+/*
+ * lora_mlp_backward -- gradients of the single-adapter LoRA MLP with SwiGLU (bf16) for the fast
+ * path's backward ("Add optional fast lora path for qwen2/qwen3 on npu", review thread and
+ * Verification advice: SwiGLU backward from the saved gate/up projections, dX from df and the
+ * weights, LoRA A/B gradients, X never overwritten; the page shows fragments only, this is its
+ * reading). With d = dout, f = silu(e):
+ *
+ *   hmid = round(f v), xa_g = round(x A_g^T), xa_u = round(x A_u^T), xa_d = round(hmid A_d^T),
+ *   dxa_d = round(s d B_d),   dhmid = d W_d + dxa_d A_d   (fp32, not stored),
+ *   de = round(dhmid v silu'(e)),  dv = round(dhmid f),
+ *   dxa_g = round(s de B_g),  dxa_u = round(s dv B_u),
+ *   dx = round(de W_g + dv W_u + dxa_g A_g + dxa_u A_u),
+ *   da_down = round(dxa_d^T hmid), db_down = round(s d^T xa_d),
+ *   da_gate = round(dxa_g^T x),    db_gate = round(s de^T xa_g),  (up likewise)
+ *
+ * silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))); fp32 accumulation; s is folded into bf16
+ * copies of B (exact for a power of two). The frozen W take no gradient.
+ *
+ *   x [M][ldx], dout [M][lddo]: 16-byte aligned rows. e, v [M][lde] from lora_mlp_fused_train.
+ *   w_gu_t, w_down_t: from lora_mlp_prepare_backward. a_*, b_* as for lora_mlp_fused.
+ *   dx [M][lddx] (must not be x or dout); da_gate, da_up [r][H]; db_gate, db_up [I][r];
+ *   da_down [r][I]; db_down [H][r]: all bf16, packed, written (not accumulated).
+ *   workspace    device, >= lora_mlp_backward_workspace_size(...) bytes, 16-byte aligned.
+ * Requires H and I multiples of 32 and 1 <= r <= 64 (else LORA_EUNSUPPORTED). Nothing is read on
+ * the host; every launch is on `stream`.
+ */
+lora_status lora_mlp_backward(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r,
+                              float scale, const void* x, int64_t ldx, const void* e,
+                              const void* v, int64_t lde, const void* dout, int64_t lddo,
+                              const void* w_gu_t, const void* w_down_t, const void* a_gate,
+                              const void* b_gate, const void* a_up, const void* b_up,
+                              const void* a_down, const void* b_down, void* dx, int64_t lddx,
+                              void* da_gate, void* db_gate, void* da_up, void* db_up,
+                              void* da_down, void* db_down, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+size_t lora_mlp_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I,
+                                        int32_t r);
+
+/*
+ * lora_mlp_backward_intermediates -- where lora_mlp_backward leaves its stored intermediates in
+ * its workspace (valid until the workspace is reused), for inspection and step-by-step checks:
+ * byte offsets (16-byte aligned) of bf16 row-major arrays, written to offsets[0..5]:
+ *   [0] hmid [M][I]   [1] [de | dv] [M][2I]   [2] [xa_g | xa_u] [M][2 rp]   [3] xa_d [M][rp]
+ *   [4] dxa_d [M][rp] [5] [dxa_g | dxa_u] [M][2 rp]
+ * where rp, the rank rounded up to 32, is the return value (columns r..rp-1 of each rp block
+ * hold zeros). Returns 0 (and writes nothing) for sizes lora_mlp_backward rejects or a NULL
+ * offsets pointer.
+ */
+int32_t lora_mlp_backward_intermediates(int64_t M, int64_t H, int64_t I, int32_t r,
+                                        size_t* offsets);
 
 /*
  * lora_linear_fused -- single-adapter LoRA linear projection (bf16): the attention output

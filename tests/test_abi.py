@@ -230,3 +230,62 @@ def test_embedding_empty_calls_are_no_ops():
     # nothing to do: returns before touching any pointer
     assert _emb(T=0) == _lib.LORA_OK
     assert _emb(G=0) == _lib.LORA_OK
+
+
+def _mlp_bwd(**kw):
+    args = dict(dtype=1, M=8, H=64, I=96, r=16, scale=2.0, x=0x1000, ldx=64, e=0x2000, v=0x3000,
+                lde=96, dout=0x4000, lddo=64, w_gu_t=0x5000, w_down_t=0x6000, a_gate=0x7000,
+                b_gate=0x8000, a_up=0x9000, b_up=0xA000, a_down=0xB000, b_down=0xC000, dx=0xD000,
+                lddx=64, da_gate=0xE000, db_gate=0xF000, da_up=0x10000, db_up=0x11000,
+                da_down=0x12000, db_down=0x13000, workspace=0x100000, workspace_bytes=16,
+                stream=None)
+    args.update(kw)
+    return _lib.lib().lora_mlp_backward(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), _lib.LORA_EUNSUPPORTED),
+    (dict(dtype=2), _lib.LORA_EUNSUPPORTED),
+    (dict(M=-1), _lib.LORA_EINVAL),
+    (dict(r=0), _lib.LORA_EINVAL),
+    (dict(r=65), _lib.LORA_EUNSUPPORTED),
+    (dict(H=48, ldx=48, lddo=48, lddx=48), _lib.LORA_EUNSUPPORTED),
+    (dict(I=100, lde=100), _lib.LORA_EUNSUPPORTED),
+    (dict(e=None), _lib.LORA_EINVAL),
+    (dict(db_down=None), _lib.LORA_EINVAL),
+    (dict(w_gu_t=None), _lib.LORA_EINVAL),
+    (dict(lde=95), _lib.LORA_EINVAL),
+    (dict(lddo=32), _lib.LORA_EINVAL),
+    (dict(dx=0x1000), _lib.LORA_EINVAL),             # dx would overwrite the saved x
+    (dict(dx=0x4000), _lib.LORA_EINVAL),             # ... or dout
+    (dict(x=0x1002), _lib.LORA_EUNSUPPORTED),        # unaligned rows
+    (dict(workspace=None), _lib.LORA_EWORKSPACE),
+    (dict(workspace_bytes=16), _lib.LORA_EWORKSPACE),
+])
+def test_mlp_backward_host_validation(kw, code):
+    # every call is rejected on the host before anything is enqueued (placeholder addresses)
+    assert _mlp_bwd(**kw) == code
+
+
+def test_mlp_backward_empty_and_workspace_size():
+    assert _mlp_bwd(M=0) == _lib.LORA_OK
+    n = _lib.lora_mlp_backward_workspace_size(1, 4096, 4096, 12288, 16)
+    # at least hmid [M][I] and [de | dv] [M][2I] in bf16
+    assert n >= 3 * 4096 * 12288 * 2
+    assert _lib.lora_mlp_backward_workspace_size(1, 0, 64, 96, 16) == 0
+    assert _lib.lora_mlp_backward_workspace_size(1, 8, 64, 96, 65) == 0
+
+
+def test_mlp_train_and_prepare_host_validation():
+    L = _lib.lib()
+    base = [1, 8, 64, 96, 16, 2.0, 0x1000, 64, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000,
+            0x8000, 0x9000, 0xA000, 0xB000, 64, 0xC000, 0xD000, 96, 0x100000, 16, None]
+    bad = list(base); bad[19] = None  # e
+    assert L.lora_mlp_fused_train(*bad) == _lib.LORA_EINVAL
+    bad = list(base); bad[21] = 95  # lde < I
+    assert L.lora_mlp_fused_train(*bad) == _lib.LORA_EINVAL
+    bad = list(base); bad[23] = 16  # workspace too small
+    assert L.lora_mlp_fused_train(*bad) == _lib.LORA_EWORKSPACE
+    assert L.lora_mlp_prepare_backward(0, 64, 96, 0x1, 0x2, 0x3, 0x4, 0x5, None) == _lib.LORA_EUNSUPPORTED
+    assert L.lora_mlp_prepare_backward(1, 0, 96, 0x1, 0x2, 0x3, 0x4, 0x5, None) == _lib.LORA_EINVAL
+    assert L.lora_mlp_prepare_backward(1, 64, 96, 0x1, None, 0x3, 0x4, 0x5, None) == _lib.LORA_EINVAL

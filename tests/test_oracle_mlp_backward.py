@@ -171,6 +171,26 @@ def test_silu_grad_closed_forms():
     assert np.allclose(silu_grad(z), fd, rtol=1e-8, atol=1e-10)
 
 
+def test_given_intermediates_are_used_downstream():
+    c, dout = _case(6, M=5, H=16, I=20, r=3)
+    e, v = lora_mlp_saved(c.x, c.w_gate, c.w_up, c.a_gate, c.b_gate, c.a_up, c.b_up, c.scale, "bf16")
+    g0, inter = lora_mlp_backward(c.x, e, v, dout, *_w(c), c.scale, "bf16", return_intermediates=True)
+    given = {k: inter[k] for k in ("hmid", "xa_g", "xa_u", "xa_d", "dxa_d", "de", "dv", "dxa_g", "dxa_u")}
+    g1, inter1 = lora_mlp_backward(c.x, e, v, dout, *_w(c), c.scale, "bf16",
+                                   return_intermediates=True, given=given)
+    for k in NAMES:
+        assert np.array_equal(g0[k], g1[k]), k
+    for k in given:
+        assert np.array_equal(inter[k], inter1[k]), k
+    # a changed de reaches dx, db_gate and dxa_g (computed from the given de), not de itself
+    bumped = dict(given, de=given["de"] * 2.0)
+    g2, inter2 = lora_mlp_backward(c.x, e, v, dout, *_w(c), c.scale, "bf16",
+                                   return_intermediates=True, given=bumped)
+    assert np.array_equal(inter2["de"], inter["de"])
+    assert not np.array_equal(inter2["dxa_g"], inter["dxa_g"])
+    assert not np.array_equal(g2["dx"], g0["dx"]) and not np.array_equal(g2["db_gate"], g0["db_gate"])
+
+
 def test_saved_preactivations_match_the_forward():
     c, _ = _case(4)
     e, v = lora_mlp_saved(c.x, c.w_gate, c.w_up, c.a_gate, c.b_gate, c.a_up, c.b_up, c.scale, "f64")
@@ -181,17 +201,17 @@ def test_saved_preactivations_match_the_forward():
 
 
 BWD_MUTATIONS = [
-    ("return sg * (1.0 + z * (1.0 - sg))", "return sg * (1.0 + z * sg)"),     # wrong silu'
-    ("de = rnd(dhmid * v * silu_grad(e))", "de = rnd(dhmid * silu_grad(e))"),  # dropped v
-    ("dv = rnd(dhmid * f)", "dv = rnd(dhmid * e)"),                              # silu dropped
-    ("dxa_d = rnd(s * (d @ Bd))", "dxa_d = rnd(d @ Bd)"),                        # dropped scale
-    ("dhmid = d @ Wd + dxa_d @ Ad", "dhmid = d @ Wd"),                           # LoRA term lost
-    ("+ dxa_g @ Ag + dxa_u @ Au)", "+ dxa_g @ Ag + dxa_u @ Ag)"),                # wrong A
-    ('"db_gate": rnd(s * (de.T @ xa_g))', '"db_gate": rnd(s * (de.T @ xa_u))'),  # wrong operand
-    ('"da_up": rnd(dxa_u.T @ x)', '"da_up": rnd(dxa_g.T @ x)'),                  # swapped
-    ('"db_down": rnd(s * (d.T @ xa_d))', '"db_down": rnd(d.T @ xa_d)'),          # dropped scale
-    ("de = rnd(dhmid * v * silu_grad(e))", "de = dhmid * v * silu_grad(e)"),     # rounding point
-    ("hmid = rnd(f * v)\n    xa_g", "hmid = f * v\n    xa_g"),                    # rounding point
+    ("return sg * (1.0 + z * (1.0 - sg))", "return sg * (1.0 + z * sg)"),           # wrong silu'
+    ("rnd(dhmid * v * silu_grad(e))", "rnd(dhmid * silu_grad(e))"),                  # dropped v
+    ('use("dv", rnd(dhmid * f))', 'use("dv", rnd(dhmid * e))'),                      # silu dropped
+    ("rnd(s * (d @ Bd))", "rnd(d @ Bd)"),                                            # dropped scale
+    ("dhmid = d @ Wd + dxa_d @ Ad", "dhmid = d @ Wd"),                               # LoRA term lost
+    ("+ dxa_g @ Ag + dxa_u @ Au)", "+ dxa_g @ Ag + dxa_u @ Ag)"),                    # wrong A
+    ('"db_gate": rnd(s * (de.T @ xa_g))', '"db_gate": rnd(s * (de.T @ xa_u))'),      # wrong operand
+    ('"da_up": rnd(dxa_u.T @ x)', '"da_up": rnd(dxa_g.T @ x)'),                      # swapped
+    ('"db_down": rnd(s * (d.T @ xa_d))', '"db_down": rnd(d.T @ xa_d)'),              # dropped scale
+    ('use("de", rnd(dhmid * v * silu_grad(e)))', 'use("de", dhmid * v * silu_grad(e))'),  # rounding
+    ('use("hmid", rnd(f * v))', 'use("hmid", f * v)'),                               # rounding point
 ]
 
 
@@ -209,3 +229,15 @@ def test_backward_mutation_is_caught(old, new):
     ref = _brute(c, dout, "bf16")
     caught |= any(np.mean(got[k] == ref[k]) < 0.95 for k in NAMES)
     assert caught
+
+
+def test_ignoring_given_intermediates_is_caught():
+    from tests.test_oracle_mutations import _mutant
+
+    m = _mutant(mlp_mod, "return _f64(given[name])", "return value")
+    c, dout = _case(6, M=5, H=16, I=20, r=3)
+    e, v = lora_mlp_saved(c.x, c.w_gate, c.w_up, c.a_gate, c.b_gate, c.a_up, c.b_up, c.scale, "bf16")
+    g0, inter = m.lora_mlp_backward(c.x, e, v, dout, *_w(c), c.scale, "bf16", return_intermediates=True)
+    bumped = {"de": inter["de"] * 2.0}
+    g2 = m.lora_mlp_backward(c.x, e, v, dout, *_w(c), c.scale, "bf16", given=bumped)
+    assert np.array_equal(g2["dx"], g0["dx"])  # the mutant ignores the given de: the pin above fails
