@@ -687,7 +687,7 @@ lora_status lora_mlp_backward(lora_dtype dtype, int64_t M, int64_t H, int64_t I,
   if (ldx < H || lde < I || lddo < H || lddx < H) return LORA_EINVAL;
   if (dx == x || dx == dout) return LORA_EINVAL;  // the saved input is never overwritten
   if (!al16(x) || (ldx * 2) % 16 != 0 || !al16(dout) || (lddo * 2) % 16 != 0 || !al16(w_gu_t) ||
-      !al16(w_down_t))
+      !al16(w_down_t) || !al16(e_saved) || !al16(v_saved) || (lde * 2) % 16 != 0)
     return LORA_EUNSUPPORTED;
   const MlpBwdLayout L = mlp_bwd_layout(M, H, I, r);
   if (workspace == nullptr || workspace_bytes < L.total || !al16(workspace)) return LORA_EWORKSPACE;

@@ -224,10 +224,16 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset (the
 // scalar-base addressing form), so the per-lane address needs no vector arithmetic.
+// The base must be wave-uniform; it is passed through readfirstlane so that it sits in SGPRs
+// even where the compiler's uniformity analysis cannot prove it (free when it already does).
 __device__ __forceinline__ void dma16_saddr(const void* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32));
+  const void* sb = reinterpret_cast<const void*>((uint64_t(hi) << 32) | lo);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "v"(voff), "s"(sb), "s"(lds_addr)
                : "memory", "m0");
 }
 

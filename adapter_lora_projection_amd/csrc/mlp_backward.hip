@@ -75,13 +75,17 @@ hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int
 // ---- sums over tokens --------------------------------------------------------------------
 // Workgroup (x = column block of 1024 columns of one job, y = chunk of rows, z = block of 16 of
 // the nq columns of Q): each thread owns 4 adjacent columns of P and the 16 Q columns, so it
-// keeps 64 fp32 sums and reads P with 8-byte loads (a wave covers 512 contiguous bytes of a row);
-// the Q values of a row are the same for the whole workgroup. The partial sums of the chunk go
-// to part[job][(chunk * JB + z) * C + c][16]; a second kernel adds the chunks in order.
+// keeps 64 fp32 sums and reads P with 8-byte loads (a wave covers 512 contiguous bytes of a row).
+// The Q values of 256 rows at a time are staged once in LDS as fp32 and read back as broadcasts;
+// P rows are loaded 8 at a time, two groups in flight, so the loads of one group overlap the FMAs
+// of the previous one. The partial sums of the chunk go to part[job][(chunk * JB + z) * C + c][16];
+// a second kernel adds the chunks in order.
 namespace {
 constexpr int kColThreads = 256;
 constexpr int kColPerThread = 4;
 constexpr int kColBlock = kColThreads * kColPerThread;  // 1024 columns per workgroup
+constexpr int kColRows = 256;                            // Q rows staged in LDS at a time
+constexpr int kColGroup = 8;                             // P rows per load group
 
 struct ColGeom {
   int blk0[7];       // first column block of each job (prefix)
@@ -103,6 +107,7 @@ ColGeom col_geom(const ColJobs& j) {
 size_t colred_partial_floats(const ColJobs& jobs) { return size_t(col_geom(jobs).part0[jobs.n]); }
 
 __global__ __launch_bounds__(kColThreads) void colred_kernel(ColJobs jobs, ColGeom geo, float* part) {
+  __shared__ __align__(16) float qs[kColRows][16];
   // this workgroup's job (uniform; constant-index selection keeps the job table in registers)
   int q = 0;
 #pragma unroll
@@ -116,11 +121,16 @@ __global__ __launch_bounds__(kColThreads) void colred_kernel(ColJobs jobs, ColGe
     if (q == k) { jb = jobs.job[k]; blk0 = geo.blk0[k]; part0 = geo.part0[k]; }
   const int JB = (jb.nq + 15) / 16;
   const int zb = int(blockIdx.z);
-  if (zb >= JB) return;
-  const int c = (int(blockIdx.x) - blk0) * kColBlock + int(threadIdx.x) * kColPerThread;
+  if (zb >= JB) return;  // uniform over the workgroup
+  const int tid = int(threadIdx.x);
+  const int c = (int(blockIdx.x) - blk0) * kColBlock + tid * kColPerThread;
+  const bool active = c < jb.C;
+  const int cc = active ? c : 0;  // inactive threads read column 0 (never stored)
   const int rows_per = (jobs.M + jobs.chunks - 1) / jobs.chunks;
   const int m0 = int(blockIdx.y) * rows_per, m1 = min(jobs.M, m0 + rows_per);
   const int nvalid = min(16, jb.nq - 16 * zb);  // Q columns of this block (uniform)
+  const uint16_t* __restrict__ P = jb.P + cc;
+  const uint16_t* __restrict__ Q = jb.Q + 16 * zb;
 
   float acc[kColPerThread][16];
 #pragma unroll
@@ -128,25 +138,58 @@ __global__ __launch_bounds__(kColThreads) void colred_kernel(ColJobs jobs, ColGe
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[a][j] = 0.f;
 
-  if (c < jb.C) {
-    const uint16_t* __restrict__ P = jb.P + c;
-    const uint16_t* __restrict__ Q = jb.Q + 16 * zb;
-#pragma unroll 4
-    for (int m = m0; m < m1; ++m) {
-      const uint2 pv = *reinterpret_cast<const uint2*>(P + int64_t(m) * jb.ldp);
-      float pf[4];
-      pf[0] = __uint_as_float(pv.x << 16);
-      pf[1] = __uint_as_float(pv.x & 0xffff0000u);
-      pf[2] = __uint_as_float(pv.y << 16);
-      pf[3] = __uint_as_float(pv.y & 0xffff0000u);
-      const uint16_t* qrow = Q + int64_t(m) * jb.ldq;
+  auto load_group = [&](uint2* dst, int mg, int mend) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float qv = j < nvalid ? Traits<DT_BF16>::to_f32(qrow[j]) : 0.f;
+    for (int i = 0; i < kColGroup; ++i) {
+      const int m = min(mg + i, mend - 1);  // past the end: a valid row, never added
+      dst[i] = *reinterpret_cast<const uint2*>(P + int64_t(m) * jb.ldp);
+    }
+  };
+  auto add_group = [&](const uint2* src, int mg, int mend, int sb) {
 #pragma unroll
-        for (int a = 0; a < kColPerThread; ++a) acc[a][j] = fmaf(pf[a], qv, acc[a][j]);
+    for (int i = 0; i < kColGroup; ++i) {
+      if (mg + i < mend) {  // uniform
+        float pf[4];
+        pf[0] = __uint_as_float(src[i].x << 16);
+        pf[1] = __uint_as_float(src[i].x & 0xffff0000u);
+        pf[2] = __uint_as_float(src[i].y << 16);
+        pf[3] = __uint_as_float(src[i].y & 0xffff0000u);
+        const float4* qr = reinterpret_cast<const float4*>(qs[mg + i - sb]);
+        float qv[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 t = qr[k];
+          qv[4 * k] = t.x; qv[4 * k + 1] = t.y; qv[4 * k + 2] = t.z; qv[4 * k + 3] = t.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+          for (int a = 0; a < kColPerThread; ++a) acc[a][j] = fmaf(pf[a], qv[j], acc[a][j]);
       }
     }
+  };
+
+  for (int sb = m0; sb < m1; sb += kColRows) {
+    const int se = min(m1, sb + kColRows);
+    // stage the Q rows [sb, se) as fp32 (zeros past the block's valid columns)
+    __syncthreads();  // the previous rows' reads of qs are done
+    if (sb + tid < se) {
+      const uint16_t* qrow = Q + int64_t(sb + tid) * jb.ldq;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qs[tid][j] = j < nvalid ? Traits<DT_BF16>::to_f32(qrow[j]) : 0.f;
+    }
+    __syncthreads();
+    uint2 ga[kColGroup], gb[kColGroup];
+    load_group(ga, sb, se);
+    for (int mg = sb; mg < se; mg += 2 * kColGroup) {
+      load_group(gb, mg + kColGroup, se);
+      add_group(ga, mg, se, sb);
+      load_group(ga, mg + 2 * kColGroup, se);
+      add_group(gb, mg + kColGroup, se, sb);
+    }
+  }
+
+  if (active) {
     float* dst = part + part0 + ((int64_t(blockIdx.y) * JB + zb) * jb.C + c) * 16;
 #pragma unroll
     for (int a = 0; a < kColPerThread; ++a)

@@ -169,6 +169,87 @@ def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
                          "kernel": "lora_mlp_fused (all seven launches of one call)"}}
 
 
+def mlp_backward_flops(M: int, H: int, I: int, r: int) -> tuple[int, int]:
+    """(frozen-weight flops, LoRA flops) of the gradient arithmetic of one LoRA MLP backward:
+    dhmid = d W_d (2 M I H) and dx = de W_g + dv W_u (4 M H I); the LoRA terms dxa_d, dxa_g,
+    dxa_u, their products in dhmid and dx, and the six weight gradients. Recomputed forward
+    quantities (hmid, xa_*) are overhead and not counted."""
+    base = 2 * M * I * H + 2 * M * (2 * I) * H
+    lora = (2 * M * H * r + 2 * M * I * r            # dxa_d, dxa_d A_d
+            + 2 * 2 * M * I * r + 2 * M * H * 2 * r  # dxa_g, dxa_u and their A products
+            + 2 * 2 * r * M * H + 2 * 2 * I * M * r  # dA_g, dA_u, dB_g, dB_u
+            + 2 * r * M * I + 2 * H * M * r)         # dA_d, dB_d
+    return base, lora
+
+
+def mlp_backward_object(steps: int, warmup: int) -> dict:
+    """The LoRA MLP backward (lora_mlp_backward, bf16, M=4096, H=4096, I=12288, r=16, scale 4)
+    after one training forward (lora_mlp_fused_train, timed beside it): K calls back to back
+    after a warm-up, HIP events on their stream; roofline against dense bf16 MFMA."""
+    import torch
+
+    import lora_inputs as li
+    from adapter_lora_projection_amd import _lib
+
+    c = li.config_mlp()
+    dout = li.mlp_dout().to("cuda")
+    g = lambda t: t.to("cuda").contiguous()
+    x, wg, wu, wd = g(c.x), g(c.w_gate), g(c.w_up), g(c.w_down)
+    lo = [g(getattr(c, k)) for k in ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")]
+    bf = torch.bfloat16
+    out = torch.empty((c.M, c.H), dtype=bf, device="cuda")
+    e = torch.empty((c.M, c.I), dtype=bf, device="cuda")
+    v = torch.empty((c.M, c.I), dtype=bf, device="cuda")
+    w_gu_t = torch.empty((c.H, 2 * c.I), dtype=bf, device="cuda")
+    w_down_t = torch.empty((c.I, c.H), dtype=bf, device="cuda")
+    grads = [torch.empty(sh, dtype=bf, device="cuda") for sh in
+             ((c.M, c.H), (c.r, c.H), (c.I, c.r), (c.r, c.H), (c.I, c.r), (c.r, c.I), (c.H, c.r))]
+    nf = _lib.lora_mlp_workspace_size(_lib.LORA_BF16, c.M, c.H, c.I, c.r)
+    nb = _lib.lora_mlp_backward_workspace_size(_lib.LORA_BF16, c.M, c.H, c.I, c.r)
+    wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    L = [P(t) for t in lo]
+    _lib.lora_mlp_prepare_backward(_lib.LORA_BF16, c.H, c.I, P(wg), P(wu), P(wd), P(w_gu_t),
+                                   P(w_down_t), stream)
+    fwd = lambda: _lib.lora_mlp_fused_train(_lib.LORA_BF16, c.M, c.H, c.I, c.r, c.scale, P(x), c.H,
+                                            P(wg), P(wu), P(wd), *L, P(out), c.H, P(e), P(v), c.I,
+                                            P(wsf), nf, stream)
+    bwd = lambda: _lib.lora_mlp_backward(_lib.LORA_BF16, c.M, c.H, c.I, c.r, c.scale, P(x), c.H,
+                                         P(e), P(v), c.I, P(dout), c.H, P(w_gu_t), P(w_down_t), *L,
+                                         P(grads[0]), c.H, *[P(t) for t in grads[1:]], P(wsb), nb,
+                                         stream)
+
+    def timed(call):
+        for _ in range(max(warmup, 40)):
+            call()
+        torch.cuda.synchronize()
+        n = max(steps, 1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms_f = timed(fwd)
+    ms_b = timed(bwd)
+    base, lora = mlp_backward_flops(c.M, c.H, c.I, c.r)
+    fb, fl = mlp_flops(c.M, c.H, c.I, c.r)
+    tflops = (base + lora) / (ms_b * 1e-3) / 1e12
+    return {"workload": f"LoRA+SwiGLU MLP backward bf16, M={c.M} H={c.H} I={c.I} r={c.r} "
+                        f"scale={c.scale:g}", "ms_per_call": round(ms_b, 4),
+            "flops_per_call": int(base + lora), "value": round(tflops, 1), "unit": "TFLOP/s",
+            "train_forward_ms": round(ms_f, 4),
+            "train_forward_tflops": round((fb + fl) / (ms_f * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "lora_mlp_backward (all launches of one call)"}}
+
+
 def attention_object(steps: int, warmup: int) -> dict:
     """The single-adapter LoRA attention projections (bf16, Qwen3-8B shape: M=4096, H=4096,
     32 query and 8 key/value heads of 128, r=16, scale 4): lora_qkv_fused then lora_linear_fused
@@ -334,7 +415,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mlp", action="store_true",
-                    help="leave out the fused MLP and attention-projection objects")
+                    help="leave out every object beside the shrink+expand sweep")
+    ap.add_argument("--extras", default="mlp,attention,backward,embedding",
+                    help="comma list of the objects timed after the sweep (mlp, attention, "
+                         "backward, embedding); counter runs keep only mlp, so that every GEMM "
+                         "launch of the run belongs to the fused MLP")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
@@ -495,11 +580,17 @@ def main() -> int:
                      "traffic": traffic, "kernel": dom_name, "avg_launch_us": round(dom_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(dom_bytes)},
     }
-    if not args.no_mlp:
+    extras = set() if args.no_mlp else {e.strip() for e in args.extras.split(",") if e.strip()}
+    if "mlp" in extras:
         print("[bench] timing the fused LoRA+SwiGLU MLP", file=sys.stderr, flush=True)
         out["mlp"] = mlp_object(args.steps, args.warmup, traffic_table)
+    if "attention" in extras:
         print("[bench] timing the LoRA attention projections", file=sys.stderr, flush=True)
         out["attention_projections"] = attention_object(args.steps, args.warmup)
+    if "backward" in extras:
+        print("[bench] timing the LoRA MLP training forward and backward", file=sys.stderr, flush=True)
+        out["mlp_backward"] = mlp_backward_object(args.steps, args.warmup)
+    if "embedding" in extras:
         print("[bench] timing the embedding LoRA-A product", file=sys.stderr, flush=True)
         out["embedding_a"] = embedding_object(args.steps, args.warmup)
     if not args.no_cpu_baseline:

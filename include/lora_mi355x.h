@@ -223,7 +223,8 @@ lora_status lora_mlp_prepare_backward(lora_dtype dtype, int64_t H, int64_t I, co
  * silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))); fp32 accumulation; s is folded into bf16
  * copies of B (exact for a power of two). The frozen W take no gradient.
  *
- *   x [M][ldx], dout [M][lddo]: 16-byte aligned rows. e, v [M][lde] from lora_mlp_fused_train.
+ *   x [M][ldx], dout [M][lddo]: 16-byte aligned rows. e, v [M][lde] from lora_mlp_fused_train
+ *   (16-byte aligned rows).
  *   w_gu_t, w_down_t: from lora_mlp_prepare_backward. a_*, b_* as for lora_mlp_fused.
  *   dx [M][lddx] (must not be x or dout); da_gate, da_up [r][H]; db_gate, db_up [I][r];
  *   da_down [r][I]; db_down [H][r]: all bf16, packed, written (not accumulated).

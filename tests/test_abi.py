@@ -259,6 +259,8 @@ def _mlp_bwd(**kw):
     (dict(dx=0x1000), _lib.LORA_EINVAL),             # dx would overwrite the saved x
     (dict(dx=0x4000), _lib.LORA_EINVAL),             # ... or dout
     (dict(x=0x1002), _lib.LORA_EUNSUPPORTED),        # unaligned rows
+    (dict(e=0x2002), _lib.LORA_EUNSUPPORTED),
+    (dict(lde=100), _lib.LORA_EUNSUPPORTED),         # 200-byte rows: not 16-byte aligned
     (dict(workspace=None), _lib.LORA_EWORKSPACE),
     (dict(workspace_bytes=16), _lib.LORA_EWORKSPACE),
 ])
