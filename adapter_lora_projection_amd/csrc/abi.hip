@@ -348,14 +348,28 @@ lora_status linear_fused(lora_dtype dtype, int64_t M, int64_t K, const int64_t* 
     if (sp.q > 0 && lmx::launch_shrink_sk_reduce(LORA_BF16, sa, sp.bm, st) != hipSuccess)
       return LORA_EHIP;
   }
-  // 3. out_p = round(x W_p^T + s xa_p B_p^T): one GEMM per projection with LoRA in K
-  for (int p = 0; p < P; ++p) {
+  // 3. out_p = round(x W_p^T + s xa_p B_p^T) with LoRA in K: one launch over the P column
+  //    groups (query, key and value share the pass over x and fill the chip together)
+  {
     lmx::GemmArgs g{};
-    g.A = u16(x); g.lda = ldx; g.W0 = u16(w[p]); g.W1 = u16(w[p]); g.ldw = K;
-    g.A2 = xa + p * rp; g.lda2 = P * rp;
-    g.B2 = reinterpret_cast<const uint16_t*>(ws + L.lb[p]); g.ldb2 = rp;
-    g.C = static_cast<uint16_t*>(out[p]); g.ldc = ldo[p];
-    g.M = int(M); g.N = int(N[p]); g.K = int(K); g.K2 = int(rp);
+    g.A = u16(x); g.lda = ldx; g.W0 = u16(w[0]); g.W1 = u16(w[0]); g.ldw = K;
+    g.A2 = xa; g.lda2 = P * rp;
+    g.B2 = reinterpret_cast<const uint16_t*>(ws + L.lb[0]); g.ldb2 = rp;
+    g.C = static_cast<uint16_t*>(out[0]); g.ldc = ldo[0];
+    g.M = int(M); g.N = int(N[0]); g.K = int(K); g.K2 = int(rp);
+    if (P > 1) {
+      g.ngroups = P;
+      g.gblk[0] = 0;
+      for (int p = 0; p < P; ++p) {
+        g.gW[p] = u16(w[p]);
+        g.gB2[p] = reinterpret_cast<const uint16_t*>(ws + L.lb[p]);
+        g.ga2[p] = p * rp;
+        g.gC[p] = static_cast<uint16_t*>(out[p]);
+        g.gldc[p] = ldo[p];
+        g.gN[p] = int(N[p]);
+        g.gblk[p + 1] = g.gblk[p] + int(cdiv(N[p], 256));
+      }
+    }
     if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;
   }
   return LORA_OK;

@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
   // super-tiles, the 32 workgroups an XCD runs together form a 4 x 8 sub-grid of one
   // super-tile, so each K slice of an A tile is read by 8 of its CUs and each slice of a W tile
   // by 4 out of the XCD's L2. Otherwise column blocks walk fastest inside groups of 8 row blocks.
-  const int nbn = SWIGLU ? (p.N + 127) / 128 : (p.N + 255) / 256;
+  const bool grouped = MODE == kGemmPlain && p.ngroups > 1;  // uniform
+  const int nbn = SWIGLU ? (p.N + 127) / 128 : (grouped ? p.gblk[p.ngroups] : (p.N + 255) / 256);
   const int nbm = (p.M + kBM - 1) / kBM;
   int bm, bn;
   if (nbm % 16 == 0 && nbn % 16 == 0) {
@@ -87,6 +88,28 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
     bm = first_m + local % gsize;
     bn = local / gsize;
   }
+  // column group of this block (constant-index selection keeps the tables out of scratch)
+  const uint16_t* gW0 = p.W0;
+  const uint16_t* gB2 = p.B2;
+  const uint16_t* gA2 = p.A2;
+  uint16_t* gC = p.C;
+  int64_t gldc = p.ldc;
+  int gN = p.N;
+  if constexpr (MODE == kGemmPlain) {
+    if (grouped) {
+      int sel = 0;
+#pragma unroll
+      for (int g = 1; g < 3; ++g)
+        if (g < p.ngroups && bn >= p.gblk[g]) sel = g;
+#pragma unroll
+      for (int g = 0; g < 3; ++g) {
+        if (sel == g) {
+          gW0 = p.gW[g]; gB2 = p.gB2[g]; gA2 = p.A2 + p.ga2[g]; gC = p.gC[g]; gldc = p.gldc[g];
+          gN = p.gN[g]; bn -= p.gblk[g];
+        }
+      }
+    }
+  }
   const int m0 = bm * kBM;
   const int n0 = SWIGLU ? bn * 128 : bn * 256;
 
@@ -99,12 +122,12 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
   // kernel arguments as values (selecting between argument fields per lane would load them
   // through vector memory)
   const uint16_t* const pA = p.A;
-  const uint16_t* const pA2 = p.A2;
-  const uint16_t* const pW0 = p.W0;
+  const uint16_t* const pA2 = gA2;
+  const uint16_t* const pW0 = gW0;
   const uint16_t* const pW1 = p.W1;
-  const uint16_t* const pB2 = p.B2;
+  const uint16_t* const pB2 = gB2;
   const int64_t plda = p.lda, plda2 = p.lda2, pldw = p.ldw, pldb2 = p.ldb2;
-  const int pM = p.M, pN = p.N;
+  const int pM = p.M, pN = gN;
   // Tiles inside M and N (all of them when M is a multiple of 256 and N of the column tile)
   // address each 16-row load group as a wave-uniform base plus one loop-invariant per-lane byte
   // offset: the lane's row inside the group (drow) and its swizzled chunk, which do not depend
@@ -353,11 +376,11 @@ __global__ __launch_bounds__(256) void gemm_lora_kernel(GemmArgs p) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int n = col_base + cb * 32 + lr;
-        if (n >= p.N) continue;
+        if (n >= gN) continue;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = rbase + 8 * (v >> 2) + rq + (v & 3);
-          if (row < p.M) p.C[int64_t(row) * p.ldc + n] = Traits<DT_BF16>::from_f32(acc[rb][cb][v]);
+          if (row < p.M) gC[int64_t(row) * gldc + n] = Traits<DT_BF16>::from_f32(acc[rb][cb][v]);
         }
       }
     }
@@ -398,7 +421,8 @@ hipError_t launch_scale_lora_b(const ScaleJobs& jobs, float scale, int r, hipStr
 hipError_t launch_gemm_lora(const GemmArgs& a, int mode, hipStream_t st) {
   const bool swiglu = mode == kGemmSwiglu || mode == kGemmSwigluSave;
   const int nbm = (a.M + kBM - 1) / kBM;
-  const int nbn = swiglu ? (a.N + 127) / 128 : (a.N + 255) / 256;
+  const int nbn = swiglu ? (a.N + 127) / 128
+                         : (mode == kGemmPlain && a.ngroups > 1 ? a.gblk[a.ngroups] : (a.N + 255) / 256);
   dim3 grid(nbm * nbn);
   switch (mode) {
     case kGemmPlain: hipLaunchKernelGGL(gemm_lora_kernel<kGemmPlain>, grid, dim3(256), 0, st, a); break;

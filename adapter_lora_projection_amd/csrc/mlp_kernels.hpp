@@ -31,6 +31,18 @@ struct GemmArgs {
   int64_t lde;
   uint16_t* D;
   int64_t ldd;
+  // Plain mode only: up to 3 column groups in one launch (the query/key/value projections of
+  // one x). Group g owns column blocks [gblk[g], gblk[g + 1]) of 256 columns and replaces W0 by
+  // gW[g], B2 by gB2[g], A2 by A2 + ga2[g], C by gC[g], ldc by gldc[g] and N by gN[g].
+  // ngroups <= 1: one group, the fields above.
+  int ngroups;
+  int gblk[4];
+  const uint16_t* gW[3];
+  const uint16_t* gB2[3];
+  int64_t ga2[3];
+  uint16_t* gC[3];
+  int64_t gldc[3];
+  int gN[3];
 };
 
 // Epilogue modes of the GEMM: plain store; SwiGLU of the gate/up pair; the same also storing the
