@@ -8,9 +8,10 @@ stream. Every step runs in the HIP library; there is no CPU path.
 """
 
 from ._lib import LoraError, lib, lora_version
-from .ops import (LoraMlpFunction, embedding_a, expand, linear_fused, mlp_backward, mlp_fused,
+from .ops import (LoraMlpFunction, check_metadata, embedding_a, expand, linear_fused, mlp_backward,
+                  mlp_fused,
                   mlp_fused_train, mlp_prepare_backward, qkv_fused, schedule_tiles, shrink)
 
 __all__ = ["LoraError", "lib", "lora_version", "shrink", "expand", "schedule_tiles", "mlp_fused",
            "linear_fused", "qkv_fused", "embedding_a", "mlp_fused_train", "mlp_prepare_backward",
-           "mlp_backward", "LoraMlpFunction"]
+           "mlp_backward", "LoraMlpFunction", "check_metadata"]

@@ -42,6 +42,9 @@ SIGNATURES = {
                                  _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lora_mlp_backward_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
     "lora_mlp_backward_intermediates": (_i32, [_i64, _i64, _i64, _i32, _vp]),
+    "lora_check_metadata": (_i32, [_i64, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _sz, _vp]),
+    "lora_check_metadata_workspace_size": (_sz, [_i64]),
     "lora_linear_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
                                  _vp, _vp, _i64, _vp, _sz, _vp]),
     "lora_linear_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
@@ -216,3 +219,19 @@ def lora_mlp_backward_intermediates(M, H, I, r) -> tuple[int, list[int]]:
     offs = (ctypes.c_size_t * 6)()
     rp = int(lib().lora_mlp_backward_intermediates(M, H, I, r, offs))
     return rp, [int(o) for o in offs]
+
+
+def lora_check_metadata(T, G, L, R, S, N, seg_indptr, weight_indices, permutation, lora_ranks,
+                        slice_offsets, workspace, workspace_bytes, stream) -> int:
+    """Rule number broken (0 = valid); argument errors raise."""
+    rule = ctypes.c_int32(0)
+    st = lib().lora_check_metadata(T, G, L, R, S, N, _p(seg_indptr), _p(weight_indices),
+                                   _p(permutation), _p(lora_ranks), _p(slice_offsets),
+                                   ctypes.byref(rule), _p(workspace), workspace_bytes, stream)
+    if st not in (LORA_OK, LORA_EVALUE):
+        _check("lora_check_metadata", st)
+    return int(rule.value)
+
+
+def lora_check_metadata_workspace_size(T) -> int:
+    return int(lib().lora_check_metadata_workspace_size(T))

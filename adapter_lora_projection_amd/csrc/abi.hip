@@ -8,6 +8,7 @@
 
 #include "../../include/lora_mi355x.h"
 #include "embedding.hpp"
+#include "metadata_check.hpp"
 #include "mlp_kernels.hpp"
 #include "sgmv_kernels.hpp"
 
@@ -860,6 +861,43 @@ lora_status lora_embedding_a(lora_dtype dtype, int64_t T, int64_t V, int32_t R, 
   const bool vec = stride_r == 1 && R % ve == 0 && ldh % ve == 0 && stride_v % ve == 0 &&
                    stride_l % ve == 0 && al16(w_a) && al16(h);
   return hip_status(lmx::launch_embedding_a(a, es, vec, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t lora_check_metadata_workspace_size(int64_t T) {
+  return T < 0 ? 0 : 256 + size_t(T) * 4;
+}
+
+lora_status lora_check_metadata(int64_t T, int32_t G, int32_t L, int32_t R, int32_t S, int64_t N,
+                                const int32_t* seg_indptr, const int32_t* weight_indices,
+                                const int32_t* permutation, const int32_t* lora_ranks,
+                                const int32_t* slice_offsets, int32_t* rule, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (rule != nullptr) *rule = 0;
+  if (T < 0 || G < 0 || L < 0 || R < 0 || S < 0 || N < 0) return LORA_EINVAL;
+  if (T >= INT_MAX || G >= INT_MAX - 1 || S >= INT_MAX - 1 || N >= INT_MAX) return LORA_EUNSUPPORTED;
+  if (!seg_indptr || (G > 0 && !weight_indices) || (L > 0 && !lora_ranks)) return LORA_EINVAL;
+  if (workspace == nullptr || workspace_bytes < lora_check_metadata_workspace_size(T) ||
+      !al16(workspace))
+    return LORA_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  lmx::MetaArgs a{};
+  a.seg_indptr = seg_indptr; a.weight_indices = weight_indices; a.permutation = permutation;
+  a.lora_ranks = lora_ranks; a.slice_offsets = slice_offsets; a.N = N;
+  a.T = int(T); a.G = G; a.L = L; a.R = R; a.S = S;
+  int* flag = static_cast<int*>(workspace);
+  int* counts = reinterpret_cast<int*>(static_cast<char*>(workspace) + 256);
+  if (lmx::launch_metadata_check(a, flag, counts, st) != hipSuccess) return LORA_EHIP;
+  int bits = 0;
+  if (hipMemcpyAsync(&bits, flag, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return LORA_EHIP;
+  for (int k = 1; k <= 5; ++k) {
+    if (bits & (1 << k)) {
+      if (rule != nullptr) *rule = k;
+      return LORA_EVALUE;
+    }
+  }
+  return LORA_OK;
 }
 
 lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method,

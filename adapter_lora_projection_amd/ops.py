@@ -343,3 +343,24 @@ def embedding_a(input_ids, w_a, seg_indptr, weight_indices, permutation, lora_ra
     _lib.lora_embedding_a(dt, T, V, R, L, G, input_ids, w_a, sl, sr, sv, seg_indptr,
                           weight_indices, permutation, lora_ranks, h, _rows(h, "h"), _stream())
     return h
+
+
+def check_metadata(seg_indptr, weight_indices, lora_ranks, R: int, T: int, permutation=None,
+                   slice_offsets=None, N: int = 0) -> int:
+    """The metadata value checks (``lora_check_metadata``, synchronizing): the number of the
+    first rule broken, 0 when valid. permutation / slice_offsets None: not checked."""
+    _dev(seg_indptr, weight_indices, lora_ranks, permutation, slice_offsets)
+    G = weight_indices.numel()
+    _meta(seg_indptr, G + 1, "seg_indptr")
+    _meta(weight_indices, None, "weight_indices")
+    _meta(lora_ranks, None, "lora_ranks")
+    if permutation is not None:
+        _meta(permutation, T, "permutation")
+    S = 0
+    if slice_offsets is not None:
+        _meta(slice_offsets, None, "slice_offsets")
+        S = slice_offsets.numel() - 1
+    nbytes = _lib.lora_check_metadata_workspace_size(T)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=seg_indptr.device)
+    return _lib.lora_check_metadata(T, G, lora_ranks.numel(), R, S, N, seg_indptr, weight_indices,
+                                    permutation, lora_ranks, slice_offsets, ws, nbytes, _stream())

@@ -337,6 +337,29 @@ lora_status lora_embedding_a(lora_dtype dtype, int64_t T, int64_t V, int32_t R, 
                              int64_t ldh, void* stream);
 
 /*
+ * lora_check_metadata -- the value checks of the LoRA metadata that "Decode LoRA kernels are
+ * optimized" (Behaviour changes) takes off the fast path, as an explicit call that waits for its
+ * own result (it synchronizes `stream`; not for capture). Rules, reported as the first one broken:
+ *   1 seg_indptr [G+1]: starts at 0, never decreases, ends at T;
+ *   2 weight_indices [G]: inside [0, L);
+ *   3 lora_ranks [L]: inside [0, R];
+ *   4 permutation [T] (NULL: not checked, the identity): every value in [0, T) exactly once;
+ *   5 slice_offsets [S+1] (NULL: not checked): start >= 0, never decrease, end at N.
+ * Returns LORA_OK, or LORA_EVALUE with *rule (host int, may be NULL) set to the rule number (0
+ * when valid). Every device access is bounded by the sizes, so any values are safe to check.
+ * workspace: device, >= lora_check_metadata_workspace_size(T) bytes, 16-byte aligned.
+ * Errors: LORA_EINVAL (negative size, NULL seg_indptr, or NULL weight_indices / lora_ranks with
+ * G / L > 0), LORA_EWORKSPACE, LORA_EHIP.
+ */
+lora_status lora_check_metadata(int64_t T, int32_t G, int32_t L, int32_t R, int32_t S, int64_t N,
+                                const int32_t* seg_indptr, const int32_t* weight_indices,
+                                const int32_t* permutation, const int32_t* lora_ranks,
+                                const int32_t* slice_offsets, int32_t* rule, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+size_t lora_check_metadata_workspace_size(int64_t T);
+
+/*
  * lora_schedule_tiles -- the segment schedule the compute kernels use, exported for checking.
  *
  * Each non-empty segment g is cut into row tiles of at most BM sorted positions starting at

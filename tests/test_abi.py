@@ -291,3 +291,20 @@ def test_mlp_train_and_prepare_host_validation():
     assert L.lora_mlp_prepare_backward(0, 64, 96, 0x1, 0x2, 0x3, 0x4, 0x5, None) == _lib.LORA_EUNSUPPORTED
     assert L.lora_mlp_prepare_backward(1, 0, 96, 0x1, 0x2, 0x3, 0x4, 0x5, None) == _lib.LORA_EINVAL
     assert L.lora_mlp_prepare_backward(1, 64, 96, 0x1, None, 0x3, 0x4, 0x5, None) == _lib.LORA_EINVAL
+
+
+def test_check_metadata_host_validation():
+    # rejected before anything is enqueued (placeholder addresses)
+    L = _lib.lib()
+    args = [8, 2, 2, 16, 1, 32, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None, 0x100000, 1 << 20, None]
+    bad = list(args); bad[0] = -1
+    assert L.lora_check_metadata(*bad) == _lib.LORA_EINVAL
+    bad = list(args); bad[6] = None  # seg_indptr
+    assert L.lora_check_metadata(*bad) == _lib.LORA_EINVAL
+    bad = list(args); bad[7] = None  # weight_indices with G > 0
+    assert L.lora_check_metadata(*bad) == _lib.LORA_EINVAL
+    bad = list(args); bad[13] = 16  # workspace too small for T = 8
+    assert L.lora_check_metadata(*bad) == _lib.LORA_EWORKSPACE
+    bad = list(args); bad[12] = None
+    assert L.lora_check_metadata(*bad) == _lib.LORA_EWORKSPACE
+    assert _lib.lora_check_metadata_workspace_size(8) == 256 + 32
