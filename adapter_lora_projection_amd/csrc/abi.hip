@@ -35,8 +35,8 @@ int esize(int dtype) { return dtype == LORA_F32 ? 4 : 2; }
 // Columns per expand workgroup, in multiples of the 64-column chunks the waves walk: the widest
 // blocks (up to 4096 columns) that still give about 400 workgroups. Longer column runs per wave
 // measured faster than more workgroups once the chip is covered (rocprofv3 sweeps on MI355X).
-int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves) {
-  const int unit = 64 * waves;
+int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves, int chunk) {
+  const int unit = chunk * waves;
   if (g_expand_bn_override > 0) return int(cdiv(g_expand_bn_override, unit) * unit);
   const int64_t tiles = cdiv(T, bm) + G;
   const int64_t blocks = std::max<int64_t>(1, cdiv(400, tiles));
@@ -67,12 +67,14 @@ struct ShrinkWs {
   size_t sched, part, total;
 };
 
-// 4 waves with a 2-deep ring of y and B chunks: fewer bytes in flight per compute unit measured
-// faster than deeper rings at every token count of the decode sweep.
+// 4 waves with a 2-deep ring of y and B chunks up to 1024 tokens; from 2048 tokens 128-column
+// chunks with 16-byte y pieces and a 1-deep ring (rocprofv3 sweeps on MI355X: fewer bytes in
+// flight per compute unit measured faster than deeper rings; the wide chunks saved 3-12% at
+// 2048..6144 tokens and tied at 8192). Blocks whose y rows or start are not 16-byte aligned
+// take the 8-byte form inside the same launch.
 int expand_variant(int64_t T) {
-  (void)T;
   if (g_expand_override >= 0) return g_expand_override;
-  return 3;
+  return T >= 2048 ? 6 : 3;
 }
 
 size_t schedule_bytes(int64_t T, int32_t G, int bm) {
@@ -483,7 +485,8 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
   if (R > lmx::expand_max_rank(int(dtype))) return LORA_EUNSUPPORTED;
   const int variant = expand_variant(T);
   const int bm = lmx::expand_plan_bm(int(dtype), variant);
-  const int bn = expand_bn(T, G, N, bm, lmx::expand_plan_waves(int(dtype), variant));
+  const int bn = expand_bn(T, G, N, bm, lmx::expand_plan_waves(int(dtype), variant),
+                           lmx::expand_plan_chunk(int(dtype), variant));
   if (cdiv(N, bn) + S > 65535) return LORA_EUNSUPPORTED;
   const size_t need = schedule_bytes(T, G, bm);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_EWORKSPACE;

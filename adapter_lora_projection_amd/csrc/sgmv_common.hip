@@ -21,8 +21,9 @@ hipError_t launch_expand_f32(const ExpandArgs& a, const ExpandPlan& plan, hipStr
 static const int kShrinkBM[] = {16, 32, 16, 32, 32};
 static const int kShrinkWaves[] = {8, 4, 8, 4, 4};
 static const int kShrinkCB[] = {1, 4, 1, 3, 3};
-static const int kExpandBM[] = {16, 16, 16, 16, 16};
-static const int kExpandWaves[] = {4, 8, 4, 4, 8};
+static const int kExpandBM[] = {16, 16, 16, 16, 16, 16, 16, 16};
+static const int kExpandWaves[] = {4, 8, 4, 4, 8, 4, 4, 8};
+static const int kExpandChunk[] = {64, 64, 64, 64, 64, 128, 128, 128};
 
 int num_shrink_variants() { return int(sizeof(kShrinkBM) / sizeof(int)); }
 int num_expand_variants() { return int(sizeof(kExpandBM) / sizeof(int)); }
@@ -35,6 +36,7 @@ int num_shrink_lds_variants() { return int(sizeof(kShrinkLdsNCB) / sizeof(int));
 int shrink_lds_ncb(int variant) { return kShrinkLdsNCB[variant]; }
 int expand_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kExpandBM[variant]; }
 int expand_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 4 : kExpandWaves[variant]; }
+int expand_plan_chunk(int dtype, int variant) { return dtype == DT_F32 ? 64 : kExpandChunk[variant]; }
 int expand_max_rank(int dtype) { return 2 * (dtype == DT_F32 ? Traits<DT_F32>::kStep : Traits<DT_BF16>::kStep); }
 
 hipError_t launch_shrink(int dtype, const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st) {

@@ -484,7 +484,141 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
   }(std::make_integer_sequence<int, D>{});
 }
 
-template <int DT, int NW, int JS, int D, bool ALB, bool ALY>
+// Wide form of the expand body for 16-bit types with 16-byte aligned y rows: a chunk is 128
+// columns and lane (c, g) owns the 8 adjacent columns 8c .. 8c+7 of tokens 4g .. 4g+3 (MFMA
+// column block q is output column 8c + q), so each token's y piece is one 16-byte load and one
+// 16-byte store, half the memory instructions of the 8-byte form for the same bytes. Tail
+// chunks load the aligned 16-byte granule holding their first valid column and store element by
+// element.
+template <int DT, int NW, int JS, int D, bool ALB>
+__device__ __forceinline__ void expand_body_wide(const ExpandArgs& p, const Tile& tile, int s,
+                                                 int nb0, int nblen) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  static_assert(sizeof(S) == 2, "16-bit types");
+  constexpr int KSTEP = Tr::kStep;
+  constexpr int EPF = Tr::kPerFrag;
+  constexpr int CW = 128;  // columns per chunk
+
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int c = lane & 15, g = lane >> 4;
+  const int a = tile.a, r = tile.r;
+  const float sigma = tile.sigma;
+  const int nend = nb0 + nblen;
+  const int nchunks = (nblen + CW - 1) / CW;
+  const int nci = w < nchunks ? (nchunks - w + NW - 1) / NW : 0;  // this wave's chunks
+
+  const S* __restrict__ hbuf = reinterpret_cast<const S*>(p.h);
+  const S* __restrict__ wb = reinterpret_cast<const S*>(p.w_b);
+  S* __restrict__ y = reinterpret_cast<S*>(p.y);
+
+  uint4 hv[JS];
+  {
+    const bool ok = c < tile.mlen;
+    const S* hrow = hbuf + int64_t(tile.m0 + (ok ? c : 0)) * p.ldh + s * p.R;
+    Frag<S, ALB> hf[JS];
+#pragma unroll
+    for (int js = 0; js < JS; ++js) {
+      const int j = js * KSTEP + g * EPF;
+      hf[js].fetch(hrow + j, r - j, hrow);
+    }
+#pragma unroll
+    for (int js = 0; js < JS; ++js) hv[js] = hf[js].masked(r - (js * KSTEP + g * EPF));
+  }
+  S* yrow[4];
+  bool tok_ok[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * g + v;
+    tok_ok[v] = m < tile.mlen;
+    const int pos = tile.m0 + (tok_ok[v] ? m : 0);
+    yrow[v] = y + int64_t(p.permutation != nullptr ? p.permutation[pos] : pos) * p.ldy;
+  }
+  const S* bblk = wb + int64_t(a) * p.N * p.ldb;
+
+  Frag<S, true> yr[D][4];
+  Frag<S, ALB> br[D][JS][8];
+  auto fetch = [&](auto slot, int i) {
+    constexpr int d = decltype(slot)::value;
+    const int cbase = nb0 + (w + i * NW) * CW;
+    const bool in = i < nci;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int col = cbase + 8 * c + q;
+      const S* brow = bblk + int64_t((in && col < nend) ? col : nb0) * p.ldb;
+#pragma unroll
+      for (int js = 0; js < JS; ++js) {
+        const int j = js * KSTEP + g * EPF;
+        br[d][js][q].fetch(brow + j, in ? r - j : 0, brow);
+      }
+    }
+    const int c0 = cbase + 8 * c;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int valid = (in && tok_ok[v]) ? nend - c0 : 0;
+      yr[d][v].fetch(yrow[v] + c0, valid, yrow[v] + nb0);
+    }
+  };
+  auto do_chunk = [&](auto slot, int i, auto refill) {
+    constexpr int d = decltype(slot)::value;
+    f32x4_t acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int js = 0; js < JS; ++js) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        acc[q] = mma_step<DT>(hv[js], br[d][js][q].masked(r - (js * KSTEP + g * EPF)), acc[q]);
+    }
+    const int c0 = nb0 + (w + i * NW) * CW + 8 * c;
+    const int ncols = min(8, nend - c0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      union {
+        uint4 u;
+        S e[8];
+      } o;
+      o.u = yr[d][v].raw();
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        o.e[q] = Tr::from_f32(__builtin_fmaf(sigma, acc[q][v], Tr::to_f32(o.e[q])));
+      if (tok_ok[v] && ncols > 0) {
+        S* dst = yrow[v] + c0;
+        if (ncols == 8) {
+          *reinterpret_cast<uint4*>(dst) = o.u;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (q < ncols) dst[q] = o.e[q];
+        }
+      }
+    }
+    if constexpr (decltype(refill)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(slot, i + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  [&]<int... dd>(std::integer_sequence<int, dd...>) {
+    ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
+  }(std::make_integer_sequence<int, D>{});
+  const int nfull = nci / D;
+  for (int gi = 0; gi < nfull; ++gi) {
+    [&]<int... dd>(std::integer_sequence<int, dd...>) {
+      (do_chunk(std::integral_constant<int, dd>{}, gi * D + dd, std::true_type{}), ...);
+    }(std::make_integer_sequence<int, D>{});
+  }
+  const int rem = nci - nfull * D;
+  [&]<int... dd>(std::integer_sequence<int, dd...>) {
+    auto one = [&](auto ddc) {
+      constexpr int d = decltype(ddc)::value;
+      if (d < rem) do_chunk(ddc, nfull * D + d, std::false_type{});
+    };
+    (one(std::integral_constant<int, dd>{}), ...);
+  }(std::make_integer_sequence<int, D>{});
+}
+
+template <int DT, int NW, int JS, int D, bool ALB, bool ALY, bool WIDE>
 __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
   constexpr int NT = NW * 64;
   constexpr int BM = 16;
@@ -498,6 +632,13 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
   if (tile.g < 0 || tile.r <= 0) return;  // a rank-0 adapter leaves y untouched
   int s, nb0, nblen;
   if (!find_nblock(p.slice_offsets, p.S, p.BN, int(blockIdx.y), &s, &nb0, &nblen)) return;
+  if constexpr (WIDE && ALY && DT != DT_F32) {
+    // 16-byte pieces when the block starts on a 16-byte boundary (rows are 16-byte aligned)
+    if ((nb0 * int(sizeof(typename Traits<DT>::store_t))) % 16 == 0) {
+      expand_body_wide<DT, NW, JS, D, ALB>(p, tile, s, nb0, nblen);
+      return;
+    }
+  }
   if constexpr (ALY) {
     // whole 8-byte pieces only when the block starts on an 8-byte boundary
     if ((nb0 * int(sizeof(typename Traits<DT>::store_t))) % 8 != 0) {
@@ -512,7 +653,7 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
 
 // Kernel shapes. Shrink: (token groups of 16 per tile, 16-column blocks per workgroup, waves,
 // ring depth of the streamed A and x fragments). Expand: (waves, ring depth of the
-// streamed y chunks); expand tiles are 16 tokens. fp32 (small correctness workloads) has one
+// streamed y chunks, 128-column chunks with 16-byte y pieces); expand tiles are 16 tokens. fp32 (small correctness workloads) has one
 // shape of each.
 #define LMX_SHRINK_VARIANTS(X) \
   X(0, 1, 1, 8, 4)             \
@@ -521,11 +662,14 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
   X(3, 2, 3, 4, 4)             \
   X(4, 2, 3, 4, 2)
 #define LMX_EXPAND_VARIANTS(X) \
-  X(0, 4, 3)                   \
-  X(1, 8, 2)                   \
-  X(2, 4, 4)                   \
-  X(3, 4, 2)                   \
-  X(4, 8, 1)
+  X(0, 4, 3, false)            \
+  X(1, 8, 2, false)            \
+  X(2, 4, 4, false)            \
+  X(3, 4, 2, false)            \
+  X(4, 8, 1, false)            \
+  X(5, 4, 2, true)             \
+  X(6, 4, 1, true)             \
+  X(7, 8, 1, true)
 
 template <int DT, int MT, int CB, int NW, int D>
 static hipError_t launch_shrink_t(const ShrinkArgs& a, bool aligned, int grid_x, hipStream_t st) {
@@ -565,27 +709,27 @@ hipError_t launch_shrink_sk_reduce_dt(const ShrinkArgs& a, int bm, hipStream_t s
   return hipGetLastError();
 }
 
-template <int DT, int NW, int JS, int D>
+template <int DT, int NW, int JS, int D, bool WIDE>
 static void launch_expand_al(const ExpandArgs& a, const ExpandPlan& plan, dim3 grid, hipStream_t st) {
   dim3 block(NW * 64);
   if (plan.aligned_b && plan.aligned_y)
-    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, true, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, true, true, WIDE>), grid, block, 0, st, a);
   else if (plan.aligned_b)
-    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, true, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, true, false, WIDE>), grid, block, 0, st, a);
   else if (plan.aligned_y)
-    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, false, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, false, true, WIDE>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, false, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((expand_kernel<DT, NW, JS, D, false, false, WIDE>), grid, block, 0, st, a);
 }
 
-template <int DT, int NW, int D>
+template <int DT, int NW, int D, bool WIDE>
 static hipError_t launch_expand_t(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st) {
   const int64_t gy = (a.N + a.BN - 1) / a.BN + a.S;
   dim3 grid(plan.grid_x, unsigned(gy));
   constexpr int KS = Traits<DT>::kStep;
   const int js = (a.R + KS - 1) / KS;
-  if (js <= 1) launch_expand_al<DT, NW, 1, D>(a, plan, grid, st);
-  else if (js == 2) launch_expand_al<DT, NW, 2, D>(a, plan, grid, st);
+  if (js <= 1) launch_expand_al<DT, NW, 1, D, WIDE>(a, plan, grid, st);
+  else if (js == 2) launch_expand_al<DT, NW, 2, D, WIDE>(a, plan, grid, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -593,11 +737,11 @@ static hipError_t launch_expand_t(const ExpandArgs& a, const ExpandPlan& plan, h
 template <int DT>
 hipError_t launch_expand_dt(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st) {
   if constexpr (DT == DT_F32) {
-    return launch_expand_t<DT, 4, 2>(a, plan, st);
+    return launch_expand_t<DT, 4, 2, false>(a, plan, st);
   } else {
     switch (plan.variant) {
-#define X(V, NW, D) \
-      case V: return launch_expand_t<DT, NW, D>(a, plan, st);
+#define X(V, NW, D, WIDE) \
+      case V: return launch_expand_t<DT, NW, D, WIDE>(a, plan, st);
       LMX_EXPAND_VARIANTS(X)
 #undef X
     }

@@ -69,6 +69,7 @@ int num_expand_variants();
 int shrink_plan_bm(int dtype, int variant);
 int expand_plan_bm(int dtype, int variant);
 int expand_plan_waves(int dtype, int variant);
+int expand_plan_chunk(int dtype, int variant);  // columns per wave chunk (64 or 128)
 int expand_max_rank(int dtype);  // largest padded rank the expand kernels take
 
 hipError_t launch_shrink(int dtype, const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st);

@@ -103,7 +103,7 @@ def test_sweep(T):
 
 @pytest.mark.parametrize("direct", [False, True])
 @pytest.mark.parametrize("sv", range(5))
-@pytest.mark.parametrize("ev", range(5))
+@pytest.mark.parametrize("ev", range(8))  # every expand kernel shape
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_variants_small(sv, ev, dtype, direct):
     """Several tiles per segment plus ragged tails, odd ranks, K tail, unaligned slices; every
@@ -112,6 +112,21 @@ def test_variants_small(sv, ev, dtype, direct):
                      slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
     print("case", c.name, sv, ev, direct, flush=True)
     h, y = _run_pair(c, variant=(sv, ev), ksplit=0 if direct else None)
+    _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("ev", [5, 6, 7])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("offs", [[0, 128, 256, 520], [0, 132, 264, 520], [0, 1024, 1032, 2064]])
+def test_wide_expand_shapes(ev, dtype, offs):
+    """The 128-column chunks with 16-byte y pieces (16-byte aligned y rows): slices starting on a
+    16-byte boundary take them, others (132, 264 elements) the 8-byte form in the same launch;
+    tail chunks of 8 and fewer than 8 columns; ranks 0, 1, 7, 17 and 32."""
+    N = offs[-1]
+    c = li.make_sgmv(f"wide_{dtype}", seed=44, T=157, K=256, S=3, R=32, L=5, slice_offsets=offs,
+                     dtype=dtype, ranks=[32, 7, 1, 0, 17])
+    print("case", c.name, ev, offs, flush=True)
+    h, y = _run_pair(c, variant=(0, ev))
     _check_pair(c, h, y)
 
 
