@@ -618,6 +618,148 @@ __device__ __forceinline__ void expand_body_wide(const ExpandArgs& p, const Tile
   }(std::make_integer_sequence<int, D>{});
 }
 
+// 16-bit types, padded rank <= 16: the 16x16x16 MFMA covers the rank exactly, so h and B
+// fragments are 8 bytes (4 ranks) per lane and every lane's B load is useful (the 16x16x32 form
+// spends half of each B fragment on rank padding).
+__device__ __forceinline__ uint2 mask4(uint2 v, int valid) {
+  if (valid >= 4) return v;
+  if (valid <= 0) return make_uint2(0u, 0u);
+  if (valid == 1) return make_uint2(v.x & 0xffffu, 0u);
+  if (valid == 2) return make_uint2(v.x, 0u);
+  return make_uint2(v.x, v.y & 0xffffu);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mma_k16(uint2 a, uint2 b, f32x4_t acc);
+
+template <>
+__device__ __forceinline__ f32x4_t mma_k16<DT_BF16>(uint2 a, uint2 b, f32x4_t acc) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b),
+                                                   acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4_t mma_k16<DT_F16>(uint2 a, uint2 b, f32x4_t acc) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b),
+                                               acc, 0, 0, 0);
+}
+
+// The wide body (128-column chunks, 16-byte y pieces) with the 16x16x16 MFMA for ranks <= 16.
+template <int DT, int NW, int D, bool ALB>
+__device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Tile& tile, int s,
+                                                   int nb0, int nblen) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  static_assert(sizeof(S) == 2, "16-bit types");
+  constexpr int CW = 128;
+
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int c = lane & 15, g = lane >> 4;
+  const int a = tile.a, r = tile.r;
+  const float sigma = tile.sigma;
+  const int nend = nb0 + nblen;
+  const int nchunks = (nblen + CW - 1) / CW;
+  const int nci = w < nchunks ? (nchunks - w + NW - 1) / NW : 0;
+  const int jv = r - 4 * g;  // valid ranks of this lane's 4
+
+  const S* __restrict__ hbuf = reinterpret_cast<const S*>(p.h);
+  const S* __restrict__ wb = reinterpret_cast<const S*>(p.w_b);
+  S* __restrict__ y = reinterpret_cast<S*>(p.y);
+
+  uint2 hv;
+  {
+    const bool ok = c < tile.mlen;
+    const S* hrow = hbuf + int64_t(tile.m0 + (ok ? c : 0)) * p.ldh + s * p.R;
+    Frag8<S, ALB> hf;
+    hf.fetch(hrow + 4 * g, jv, hrow);
+    hv = mask4(hf.raw(), jv);
+  }
+  S* yrow[4];
+  bool tok_ok[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * g + v;
+    tok_ok[v] = m < tile.mlen;
+    const int pos = tile.m0 + (tok_ok[v] ? m : 0);
+    yrow[v] = y + int64_t(p.permutation != nullptr ? p.permutation[pos] : pos) * p.ldy;
+  }
+  const S* bblk = wb + int64_t(a) * p.N * p.ldb;
+
+  Frag<S, true> yr[D][4];
+  Frag8<S, ALB> br[D][8];
+  auto fetch = [&](auto slot, int i) {
+    constexpr int d = decltype(slot)::value;
+    const int cbase = nb0 + (w + i * NW) * CW;
+    const bool in = i < nci;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int col = cbase + 8 * c + q;
+      const S* brow = bblk + int64_t((in && col < nend) ? col : nb0) * p.ldb;
+      br[d][q].fetch(brow + 4 * g, in ? jv : 0, brow);
+    }
+    const int c0 = cbase + 8 * c;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int valid = (in && tok_ok[v]) ? nend - c0 : 0;
+      yr[d][v].fetch(yrow[v] + c0, valid, yrow[v] + nb0);
+    }
+  };
+  auto do_chunk = [&](auto slot, int i, auto refill) {
+    constexpr int d = decltype(slot)::value;
+    f32x4_t acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      acc[q] = mma_k16<DT>(hv, mask4(br[d][q].raw(), jv), f32x4_t{0.f, 0.f, 0.f, 0.f});
+    const int c0 = nb0 + (w + i * NW) * CW + 8 * c;
+    const int ncols = min(8, nend - c0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      union {
+        uint4 u;
+        S e[8];
+      } o;
+      o.u = yr[d][v].raw();
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        o.e[q] = Tr::from_f32(__builtin_fmaf(sigma, acc[q][v], Tr::to_f32(o.e[q])));
+      if (tok_ok[v] && ncols > 0) {
+        S* dst = yrow[v] + c0;
+        if (ncols == 8) {
+          *reinterpret_cast<uint4*>(dst) = o.u;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (q < ncols) dst[q] = o.e[q];
+        }
+      }
+    }
+    if constexpr (decltype(refill)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(slot, i + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  [&]<int... dd>(std::integer_sequence<int, dd...>) {
+    ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
+  }(std::make_integer_sequence<int, D>{});
+  const int nfull = nci / D;
+  for (int gi = 0; gi < nfull; ++gi) {
+    [&]<int... dd>(std::integer_sequence<int, dd...>) {
+      (do_chunk(std::integral_constant<int, dd>{}, gi * D + dd, std::true_type{}), ...);
+    }(std::make_integer_sequence<int, D>{});
+  }
+  const int rem = nci - nfull * D;
+  [&]<int... dd>(std::integer_sequence<int, dd...>) {
+    auto one = [&](auto ddc) {
+      constexpr int d = decltype(ddc)::value;
+      if (d < rem) do_chunk(ddc, nfull * D + d, std::false_type{});
+    };
+    (one(std::integral_constant<int, dd>{}), ...);
+  }(std::make_integer_sequence<int, D>{});
+}
+
 template <int DT, int NW, int JS, int D, bool ALB, bool ALY, bool WIDE>
 __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
   constexpr int NT = NW * 64;
@@ -635,6 +777,12 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
   if constexpr (WIDE && ALY && DT != DT_F32) {
     // 16-byte pieces when the block starts on a 16-byte boundary (rows are 16-byte aligned)
     if ((nb0 * int(sizeof(typename Traits<DT>::store_t))) % 16 == 0) {
+      if constexpr (JS == 1) {
+        if (p.R <= 16) {
+          expand_body_wide16<DT, NW, D, ALB>(p, tile, s, nb0, nblen);
+          return;
+        }
+      }
       expand_body_wide<DT, NW, JS, D, ALB>(p, tile, s, nb0, nblen);
       return;
     }

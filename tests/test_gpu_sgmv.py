@@ -115,16 +115,21 @@ def test_variants_small(sv, ev, dtype, direct):
     _check_pair(c, h, y)
 
 
+@pytest.mark.parametrize("R", [32, 16])
 @pytest.mark.parametrize("ev", [5, 6, 7])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("offs", [[0, 128, 256, 520], [0, 132, 264, 520], [0, 1024, 1032, 2064]])
-def test_wide_expand_shapes(ev, dtype, offs):
+def test_wide_expand_shapes(ev, dtype, offs, R):
     """The 128-column chunks with 16-byte y pieces (16-byte aligned y rows): slices starting on a
     16-byte boundary take them, others (132, 264 elements) the 8-byte form in the same launch;
-    tail chunks of 8 and fewer than 8 columns; ranks 0, 1, 7, 17 and 32."""
-    N = offs[-1]
-    c = li.make_sgmv(f"wide_{dtype}", seed=44, T=157, K=256, S=3, R=32, L=5, slice_offsets=offs,
-                     dtype=dtype, ranks=[32, 7, 1, 0, 17])
+    tail chunks of 8 and fewer than 8 columns; padded rank 32 (16x16x32 MFMA) and 16 (16x16x16
+    MFMA, 4 ranks per lane); adapter ranks 0, 1, 7 and 12..32, NaN in the padding."""
+    c = li.make_sgmv(f"wide_{dtype}_R{R}", seed=44, T=157, K=256, S=3, R=R, L=5,
+                     slice_offsets=offs, dtype=dtype, ranks=[R, 7, 1, 0, min(17, R) - (R == 16) * 5])
+    for a in range(c.L):  # rank padding of A and B holds NaN: it must never be read
+        r = int(c.lora_ranks[a])
+        c.A.view(c.L, c.S, c.R, c.K)[a, :, r:, :] = float("nan")
+        c.B[a, :, r:] = float("nan")
     print("case", c.name, ev, offs, flush=True)
     h, y = _run_pair(c, variant=(0, ev))
     _check_pair(c, h, y)
