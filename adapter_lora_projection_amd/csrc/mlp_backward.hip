@@ -76,9 +76,10 @@ hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int
 // Workgroup (x = column block of 1024 columns of one job, y = chunk of rows, z = block of 16 of
 // the nq columns of Q): each thread owns 4 adjacent columns of P and the 16 Q columns, so it
 // keeps 64 fp32 sums and reads P with 8-byte loads (a wave covers 512 contiguous bytes of a row).
-// The Q values of 256 rows at a time are staged once in LDS as fp32 and read back as broadcasts;
-// P rows are loaded 8 at a time, two groups in flight, so the loads of one group overlap the FMAs
-// of the previous one. The partial sums of the chunk go to part[job][(chunk * JB + z) * C + c][16];
+// The Q values of 256 rows at a time are staged once in LDS as bf16 pairs of consecutive rows and
+// read back as broadcasts; each thread pairs its P values of the same two rows, so one packed dot
+// product (fp32 sum) adds both rows' terms. P rows are loaded 8 at a time, two groups in flight,
+// so the loads of one group overlap the arithmetic of the previous one. The partial sums of the chunk go to part[job][(chunk * JB + z) * C + c][16];
 // a second kernel adds the chunks in order.
 namespace {
 constexpr int kColThreads = 256;
@@ -107,7 +108,8 @@ ColGeom col_geom(const ColJobs& j) {
 size_t colred_partial_floats(const ColJobs& jobs) { return size_t(col_geom(jobs).part0[jobs.n]); }
 
 __global__ __launch_bounds__(kColThreads) void colred_kernel(ColJobs jobs, ColGeom geo, float* part) {
-  __shared__ __align__(16) float qs[kColRows][16];
+  // Q of 256 rows at a time as bf16 pairs of consecutive rows: qs[p][j] = (Q[2p][j], Q[2p+1][j])
+  __shared__ __align__(16) uint32_t qs[kColRows / 2][16];
   // this workgroup's job (uniform; constant-index selection keeps the job table in registers)
   int q = 0;
 #pragma unroll
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(kColThreads) void colred_kernel(ColJobs jobs, ColGe
   const int nvalid = min(16, jb.nq - 16 * zb);  // Q columns of this block (uniform)
   const uint16_t* __restrict__ P = jb.P + cc;
   const uint16_t* __restrict__ Q = jb.Q + 16 * zb;
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
   float acc[kColPerThread][16];
 #pragma unroll
@@ -141,42 +144,56 @@ __global__ __launch_bounds__(kColThreads) void colred_kernel(ColJobs jobs, ColGe
   auto load_group = [&](uint2* dst, int mg, int mend) {
 #pragma unroll
     for (int i = 0; i < kColGroup; ++i) {
-      const int m = min(mg + i, mend - 1);  // past the end: a valid row, never added
+      const int m = min(mg + i, mend - 1);  // past the end: a valid row, weighted by zero
       dst[i] = *reinterpret_cast<const uint2*>(P + int64_t(m) * jb.ldp);
     }
   };
+  // rows mg + i, mg + i + 1 (i even): the second may lie past mend, where its Q pair half is 0
   auto add_group = [&](const uint2* src, int mg, int mend, int sb) {
 #pragma unroll
-    for (int i = 0; i < kColGroup; ++i) {
+    for (int i = 0; i < kColGroup; i += 2) {
       if (mg + i < mend) {  // uniform
-        float pf[4];
-        pf[0] = __uint_as_float(src[i].x << 16);
-        pf[1] = __uint_as_float(src[i].x & 0xffff0000u);
-        pf[2] = __uint_as_float(src[i].y << 16);
-        pf[3] = __uint_as_float(src[i].y & 0xffff0000u);
-        const float4* qr = reinterpret_cast<const float4*>(qs[mg + i - sb]);
-        float qv[16];
+        const bool two = mg + i + 1 < mend;
+        const uint2 r0 = src[i];
+        const uint2 r1 = two ? src[i + 1] : make_uint2(0u, 0u);
+        // (P[m][c + a], P[m + 1][c + a]) for the lane's 4 columns
+        uint32_t pp[4];
+        pp[0] = __builtin_amdgcn_perm(r1.x, r0.x, 0x05040100u);
+        pp[1] = __builtin_amdgcn_perm(r1.x, r0.x, 0x07060302u);
+        pp[2] = __builtin_amdgcn_perm(r1.y, r0.y, 0x05040100u);
+        pp[3] = __builtin_amdgcn_perm(r1.y, r0.y, 0x07060302u);
+        const uint4* qr = reinterpret_cast<const uint4*>(qs[(mg + i - sb) >> 1]);
+        uint32_t qp[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float4 t = qr[k];
-          qv[4 * k] = t.x; qv[4 * k + 1] = t.y; qv[4 * k + 2] = t.z; qv[4 * k + 3] = t.w;
+          const uint4 t = qr[k];
+          qp[4 * k] = t.x; qp[4 * k + 1] = t.y; qp[4 * k + 2] = t.z; qp[4 * k + 3] = t.w;
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j)
 #pragma unroll
-          for (int a = 0; a < kColPerThread; ++a) acc[a][j] = fmaf(pf[a], qv[j], acc[a][j]);
+          for (int a = 0; a < kColPerThread; ++a)
+            acc[a][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2_t, pp[a]),
+                                                        __builtin_bit_cast(bf2_t, qp[j]),
+                                                        acc[a][j], false);
       }
     }
   };
 
   for (int sb = m0; sb < m1; sb += kColRows) {
     const int se = min(m1, sb + kColRows);
-    // stage the Q rows [sb, se) as fp32 (zeros past the block's valid columns)
+    // stage the Q row pairs of [sb, se) (zeros past the block's valid columns and past se)
     __syncthreads();  // the previous rows' reads of qs are done
-    if (sb + tid < se) {
-      const uint16_t* qrow = Q + int64_t(sb + tid) * jb.ldq;
+    if (tid < kColRows / 2 && sb + 2 * tid < se) {
+      const uint16_t* q0 = Q + int64_t(sb + 2 * tid) * jb.ldq;
+      const bool has1 = sb + 2 * tid + 1 < se;
+      const uint16_t* q1 = has1 ? q0 + jb.ldq : q0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) qs[tid][j] = j < nvalid ? Traits<DT_BF16>::to_f32(qrow[j]) : 0.f;
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t lo = j < nvalid ? q0[j] : 0u;
+        const uint32_t hi = (j < nvalid && has1) ? q1[j] : 0u;
+        qs[tid][j] = lo | (hi << 16);
+      }
     }
     __syncthreads();
     uint2 ga[kColGroup], gb[kColGroup];
