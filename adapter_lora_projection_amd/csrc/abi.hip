@@ -35,11 +35,16 @@ int esize(int dtype) { return dtype == LORA_F32 ? 4 : 2; }
 // Columns per expand workgroup, in multiples of the 64-column chunks the waves walk: the widest
 // blocks (up to 4096 columns) that still give about 400 workgroups. Longer column runs per wave
 // measured faster than more workgroups once the chip is covered (rocprofv3 sweeps on MI355X).
-int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves, int chunk) {
+// The shared-B kernel (three 256-thread workgroups resident per compute unit, 768 on the chip)
+// also takes at least 600 / tiles blocks: more blocks than that leave a second round of
+// workgroups (8192 tokens: 660 workgroups 55.7 us, 792 workgroups 63.6 us), fewer leave the
+// chip half idle (6144 tokens: 500 workgroups 44.0 us, 600 workgroups 40.6 us).
+int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves, int chunk, bool shared) {
   const int unit = chunk * waves;
   if (g_expand_bn_override > 0) return int(cdiv(g_expand_bn_override, unit) * unit);
   const int64_t tiles = cdiv(T, bm) + G;
-  const int64_t blocks = std::max<int64_t>(1, cdiv(400, tiles));
+  int64_t blocks = std::max<int64_t>(1, cdiv(400, tiles));
+  if (shared) blocks = std::max<int64_t>(blocks, 600 / tiles);
   int64_t bn = cdiv(cdiv(N, blocks), unit) * unit;
   bn = std::min<int64_t>(std::max<int64_t>(bn, unit), 4096);
   return int(bn);
@@ -67,13 +72,20 @@ struct ShrinkWs {
   size_t sched, part, total;
 };
 
-// 4 waves with a 2-deep ring of y and B chunks up to 1024 tokens; from 2048 tokens 128-column
-// chunks with 16-byte y pieces and a 1-deep ring (rocprofv3 sweeps on MI355X: fewer bytes in
-// flight per compute unit measured faster than deeper rings; the wide chunks saved 3-12% at
-// 2048..6144 tokens and tied at 8192). Blocks whose y rows or start are not 16-byte aligned
-// take the 8-byte form inside the same launch.
-int expand_variant(int64_t T) {
-  if (g_expand_override >= 0) return g_expand_override;
+// Expand kernel shape (rocprofv3 sweeps and event timings on MI355X). From 1024 tokens, slices of
+// rank exactly 16 with 16-bit types and 16-byte aligned h, B and y rows take the shared-B kernel
+// (8192 tokens: 62 -> 56 us; 1024: 17.6 -> 16.7 us). Otherwise 4 waves with a 2-deep ring of y
+// and B chunks up to 1024 tokens, and from 2048 tokens 128-column chunks with 16-byte y pieces
+// and a 1-deep ring (fewer bytes in flight per compute unit measured faster than deeper rings;
+// the wide chunks saved 3-12% at 2048..6144 tokens). Blocks whose y rows or start are not
+// 16-byte aligned take the 8-byte form inside the same launch.
+int expand_variant(int64_t T, bool shared_ok) {
+  if (g_expand_override >= 0) {
+    const bool shared = g_expand_override == lmx::kExpandSharedD1 ||
+                        g_expand_override == lmx::kExpandSharedD2;
+    return (shared && !shared_ok) ? 6 : g_expand_override;
+  }
+  if (shared_ok && T >= 1024) return lmx::kExpandSharedD1;
   return T >= 2048 ? 6 : 3;
 }
 
@@ -417,7 +429,7 @@ size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_
                                   int64_t N) {
   (void)dtype; (void)S; (void)R; (void)N;
   if (T <= 0 || G <= 0) return 0;
-  return schedule_bytes(T, G, lmx::expand_plan_bm(int(dtype), expand_variant(T)));
+  return schedule_bytes(T, G, 16);  // the smallest tile of any expand shape: the longest list
 }
 
 lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t L,
@@ -483,10 +495,16 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
     return LORA_EINVAL;
   if (ldh < int64_t(S) * R || ldb < R || ldy < N) return LORA_EINVAL;
   if (R > lmx::expand_max_rank(int(dtype))) return LORA_EUNSUPPORTED;
-  const int variant = expand_variant(T);
+  const int e = esize(dtype);
+  const bool aligned_b = al16(h) && al16(w_b) && (ldh * e) % 16 == 0 && (ldb * e) % 16 == 0 &&
+                         (int64_t(R) * e) % 16 == 0;
+  const bool aligned_y = al16(y) && (ldy * e) % 16 == 0;
+  const int variant = expand_variant(T, dtype != LORA_F32 && R == 16 && aligned_b && aligned_y);
   const int bm = lmx::expand_plan_bm(int(dtype), variant);
+  const bool shared = dtype != LORA_F32 && (variant == lmx::kExpandSharedD1 ||
+                                            variant == lmx::kExpandSharedD2);
   const int bn = expand_bn(T, G, N, bm, lmx::expand_plan_waves(int(dtype), variant),
-                           lmx::expand_plan_chunk(int(dtype), variant));
+                           lmx::expand_plan_chunk(int(dtype), variant), shared);
   if (cdiv(N, bn) + S > 65535) return LORA_EUNSUPPORTED;
   const size_t need = schedule_bytes(T, G, bm);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_EWORKSPACE;
@@ -506,10 +524,6 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
     if (e != hipSuccess) return LORA_EHIP;
     a.tiles = tiles; a.tile_count = count;
   }
-  const int e = esize(dtype);
-  const bool aligned_b = al16(h) && al16(w_b) && (ldh * e) % 16 == 0 && (ldb * e) % 16 == 0 &&
-                         (int64_t(R) * e) % 16 == 0;
-  const bool aligned_y = al16(y) && (ldy * e) % 16 == 0;
   lmx::ExpandPlan plan{variant, int(bound), aligned_b, aligned_y};
   return hip_status(lmx::launch_expand(int(dtype), a, plan, st));
 }

@@ -138,6 +138,23 @@ struct Frag<S, false> {
   __device__ __forceinline__ uint4 masked(int valid) const { return mask_elems<S>(raw(), valid); }
 };
 
+// Non-temporal 16-byte load and store for data touched exactly once (the expand's y rows): the
+// lines are not kept in the caches, so they neither evict reused operands nor leave dirty lines
+// behind for the next kernel to wait on.
+__device__ __forceinline__ uint4 gload16_nt(const void* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(1))) u32x4_t gu4;
+  const u32x4_t v = __builtin_nontemporal_load((gu4*)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void gstore16_nt(void* p, uint4 a) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) u32x4_t gu4;
+  const u32x4_t v = {a.x, a.y, a.z, a.w};
+  __builtin_nontemporal_store(v, (gu4*)(p));
+}
+
 // 8-byte variant of Frag for the streamed output rows (4 elements of a 16-bit type, 2 of fp32).
 __device__ __forceinline__ uint2 gload8(const void* p) {
   typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));

@@ -21,9 +21,9 @@ hipError_t launch_expand_f32(const ExpandArgs& a, const ExpandPlan& plan, hipStr
 static const int kShrinkBM[] = {16, 32, 16, 32, 32};
 static const int kShrinkWaves[] = {8, 4, 8, 4, 4};
 static const int kShrinkCB[] = {1, 4, 1, 3, 3};
-static const int kExpandBM[] = {16, 16, 16, 16, 16, 16, 16, 16};
-static const int kExpandWaves[] = {4, 8, 4, 4, 8, 4, 4, 8};
-static const int kExpandChunk[] = {64, 64, 64, 64, 64, 128, 128, 128};
+static const int kExpandBM[] = {16, 16, 16, 16, 16, 16, 16, 16, 64, 64};
+static const int kExpandWaves[] = {4, 8, 4, 4, 8, 4, 4, 8, 1, 1};  // column-splitting waves
+static const int kExpandChunk[] = {64, 64, 64, 64, 64, 128, 128, 128, 128, 128};
 
 int num_shrink_variants() { return int(sizeof(kShrinkBM) / sizeof(int)); }
 int num_expand_variants() { return int(sizeof(kExpandBM) / sizeof(int)); }

@@ -344,14 +344,14 @@ __global__ __launch_bounds__(256) void shrink_sk_reduce_kernel(ShrinkArgs p, int
 // into a D-deep ring, so data are consumed in the order they were requested.
 template <int DT, int NW, int JS, int D, bool ALB, bool ALY>
 __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& tile, int s, int nb0,
-                                            int nblen) {
+                                            int nblen, int w) {
   using Tr = Traits<DT>;
   using S = typename Tr::store_t;
   constexpr int KSTEP = Tr::kStep;
   constexpr int EPF = Tr::kPerFrag;
   constexpr int NY = 4 * int(sizeof(S)) / 8;  // 8-byte pieces per lane and token (4 elements)
 
-  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int a = tile.a, r = tile.r;
   const float sigma = tile.sigma;
@@ -647,6 +647,7 @@ __device__ __forceinline__ f32x4_t mma_k16<DT_F16>(uint2 a, uint2 b, f32x4_t acc
 }
 
 // The wide body (128-column chunks, 16-byte y pieces) with the 16x16x16 MFMA for ranks <= 16.
+// y moves with non-temporal loads and stores: each element is read and written exactly once.
 template <int DT, int NW, int D, bool ALB>
 __device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Tile& tile, int s,
                                                    int nb0, int nblen) {
@@ -687,7 +688,7 @@ __device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Ti
   }
   const S* bblk = wb + int64_t(a) * p.N * p.ldb;
 
-  Frag<S, true> yr[D][4];
+  uint4 yr[D][4];
   Frag8<S, ALB> br[D][8];
   auto fetch = [&](auto slot, int i) {
     constexpr int d = decltype(slot)::value;
@@ -703,7 +704,7 @@ __device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Ti
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int valid = (in && tok_ok[v]) ? nend - c0 : 0;
-      yr[d][v].fetch(yrow[v] + c0, valid, yrow[v] + nb0);
+      yr[d][v] = gload16_nt(valid > 0 ? yrow[v] + c0 : yrow[v] + nb0);
     }
   };
   auto do_chunk = [&](auto slot, int i, auto refill) {
@@ -720,14 +721,14 @@ __device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Ti
         uint4 u;
         S e[8];
       } o;
-      o.u = yr[d][v].raw();
+      o.u = yr[d][v];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         o.e[q] = Tr::from_f32(__builtin_fmaf(sigma, acc[q][v], Tr::to_f32(o.e[q])));
       if (tok_ok[v] && ncols > 0) {
         S* dst = yrow[v] + c0;
         if (ncols == 8) {
-          *reinterpret_cast<uint4*>(dst) = o.u;
+          gstore16_nt(dst, o.u);
         } else {
 #pragma unroll
           for (int q = 0; q < 8; ++q)
@@ -790,11 +791,166 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
   if constexpr (ALY) {
     // whole 8-byte pieces only when the block starts on an 8-byte boundary
     if ((nb0 * int(sizeof(typename Traits<DT>::store_t))) % 8 != 0) {
-      expand_body<DT, NW, JS, D, ALB, false>(p, tile, s, nb0, nblen);
+      expand_body<DT, NW, JS, D, ALB, false>(p, tile, s, nb0, nblen, wave_id());
       return;
     }
   }
-  expand_body<DT, NW, JS, D, ALB, ALY>(p, tile, s, nb0, nblen);
+  expand_body<DT, NW, JS, D, ALB, ALY>(p, tile, s, nb0, nblen, wave_id());
+}
+
+// Expand for slices of rank exactly 16 at large token counts. A workgroup owns up to 64 tokens of
+// one segment (16 per wave) and its four waves walk the same 128-column chunks. Each chunk's B
+// rows (128 x 16 values, 4 KB) are loaded once for the workgroup, one 16-byte piece per thread,
+// and written to LDS in MFMA fragment order (q-th 16x16x16 product, lane), so each wave reads its
+// eight B fragments with linear 8-byte LDS reads: one global B load per thread and chunk instead
+// of eight per lane. Ranks at or past the adapter's rank are zeroed as the pieces go to LDS. Two
+// LDS buffers and one barrier per chunk (chunk i+1 is written while chunk i is read). Lane
+// (c, g) of a wave owns columns 8c .. 8c+7 of tokens 4g .. 4g+3 of the wave's 16; y moves as
+// non-temporal 16-byte pieces through a D-deep ring per wave. Column blocks whose start is not
+// 16-byte aligned run the 8-byte form per wave on that wave's 16 tokens.
+template <int DT, int D, bool ALB>
+__global__ __launch_bounds__(256) void expand_shared_kernel(ExpandArgs p) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  static_assert(sizeof(S) == 2, "16-bit types");
+  constexpr int NW = 4, NT = 256, BM = 64, CW = 128;
+  constexpr int PQ = 68;  // 8-byte LDS slots per product: 64 lanes + 4 of padding (bank spread)
+
+  __shared__ Tile s_tile;
+  __shared__ int s_scan[NW];
+  __shared__ __align__(16) uint2 bsh[2][8 * PQ];
+
+  get_tile<NT>(p.seg_indptr, p.weight_indices, p.lora_ranks, p.scalings, p.G, BM, p.tiles,
+               p.tile_count, int(blockIdx.x), &s_tile, s_scan);
+  const Tile tile = s_tile;
+  if (tile.g < 0 || tile.r <= 0) return;  // a rank-0 adapter leaves y untouched
+  int s, nb0, nblen;
+  if (!find_nblock(p.slice_offsets, p.S, p.BN, int(blockIdx.y), &s, &nb0, &nblen)) return;
+  const int w = wave_id();
+  const int mw = tile.mlen - 16 * w;  // tokens of this wave (uniform over the wave; may be <= 0)
+  if ((nb0 * int(sizeof(S))) % 16 != 0) {
+    Tile sub = tile;
+    sub.m0 = tile.m0 + 16 * w;
+    sub.mlen = min(16, mw);
+    if (sub.mlen > 0) expand_body<DT, 1, 1, 1, ALB, false>(p, sub, s, nb0, nblen, 0);
+    return;
+  }
+
+  const int t = int(threadIdx.x), lane = t & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int r = tile.r;
+  const float sigma = tile.sigma;
+  const int nend = nb0 + nblen;
+  const int nchunks = (nblen + CW - 1) / CW;
+  const int jv = r - 4 * g;
+
+  const S* __restrict__ hbuf = reinterpret_cast<const S*>(p.h);
+  const S* __restrict__ wb = reinterpret_cast<const S*>(p.w_b);
+  S* __restrict__ y = reinterpret_cast<S*>(p.y);
+
+  // A operand: h row of this wave's token c (ranks 4g .. 4g+3)
+  uint2 hv;
+  {
+    const bool ok = c < mw;
+    const S* hrow = hbuf + int64_t(ok ? tile.m0 + 16 * w + c : tile.m0) * p.ldh + s * p.R;
+    Frag8<S, ALB> hf;
+    hf.fetch(hrow + 4 * g, jv, hrow);
+    hv = mask4(hf.raw(), jv);
+  }
+  S* yrow[4];
+  bool tok_ok[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * g + v;
+    tok_ok[v] = m < mw;
+    const int pos = tok_ok[v] ? tile.m0 + 16 * w + m : tile.m0;
+    yrow[v] = y + int64_t(p.permutation != nullptr ? p.permutation[pos] : pos) * p.ldy;
+  }
+
+  // B loader: thread t moves ranks 8h .. 8h+7 (h = t & 1) of chunk row t >> 1, which feed
+  // fragment groups 2h and 2h+1 of product q = row & 7 for lane c = row >> 3.
+  const int lrow = t >> 1, lhalf = t & 1;
+  const int slot = (lrow & 7) * PQ + 32 * lhalf + (lrow >> 3);
+  const int lvalid = r - 8 * lhalf;
+  const S* bblk = wb + int64_t(tile.a) * p.N * p.ldb + 8 * lhalf;
+  auto bload = [&](int i) -> uint4 {
+    const int col = nb0 + i * CW + lrow;
+    return gload16(bblk + int64_t((i < nchunks && col < nend) ? col : nb0) * p.ldb);
+  };
+  auto bput = [&](int buf, uint4 v) {
+    v = mask_elems<S>(v, lvalid);
+    bsh[buf][slot] = make_uint2(v.x, v.y);
+    bsh[buf][slot + 16] = make_uint2(v.z, v.w);
+  };
+
+  uint4 yr[D][4];
+  auto yfetch = [&](auto slotc, int i) {
+    constexpr int d = decltype(slotc)::value;
+    const int c0 = nb0 + i * CW + 8 * c;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int valid = (i < nchunks && tok_ok[v]) ? nend - c0 : 0;
+      yr[d][v] = gload16_nt(valid > 0 ? yrow[v] + c0 : yrow[v] + nb0);
+    }
+  };
+  const bool active = mw > 0;
+  uint4 bnext = bload(0);
+  if (active) {
+    [&]<int... dd>(std::integer_sequence<int, dd...>) {
+      (yfetch(std::integral_constant<int, dd>{}, dd), ...);
+    }(std::make_integer_sequence<int, D>{});
+  }
+  bput(0, bnext);
+  bnext = bload(1);
+  __syncthreads();
+
+  auto step = [&](auto slotc, int i) {
+    constexpr int d = decltype(slotc)::value;
+    const int buf = i & 1;
+    if (active) {
+      f32x4_t acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        acc[q] = mma_k16<DT>(hv, bsh[buf][q * PQ + lane], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      const int c0 = nb0 + i * CW + 8 * c;
+      const int ncols = min(8, nend - c0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        union {
+          uint4 u;
+          S e[8];
+        } o;
+        o.u = yr[d][v];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          o.e[q] = Tr::from_f32(__builtin_fmaf(sigma, acc[q][v], Tr::to_f32(o.e[q])));
+        if (tok_ok[v] && ncols > 0) {
+          S* dst = yrow[v] + c0;
+          if (ncols == 8) {
+            gstore16_nt(dst, o.u);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (q < ncols) dst[q] = o.e[q];
+          }
+        }
+      }
+      yfetch(slotc, i + D);
+    }
+    bput(buf ^ 1, bnext);  // chunk i+1 (never read when i+1 == nchunks)
+    bnext = bload(i + 2);
+    __syncthreads();
+  };
+  const int ngroups = (nchunks + D - 1) / D;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    [&]<int... dd>(std::integer_sequence<int, dd...>) {
+      auto one = [&](auto ddc) {
+        constexpr int d = decltype(ddc)::value;
+        if (gi * D + d < nchunks) step(ddc, gi * D + d);  // uniform over the workgroup
+      };
+      (one(std::integral_constant<int, dd>{}), ...);
+    }(std::make_integer_sequence<int, D>{});
+  }
 }
 
 // ------------------------------------------------------------------------------------ launchers
@@ -882,11 +1038,22 @@ static hipError_t launch_expand_t(const ExpandArgs& a, const ExpandPlan& plan, h
   return hipGetLastError();
 }
 
+template <int DT, int D>
+static hipError_t launch_expand_shared_t(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st) {
+  const int64_t gy = (a.N + a.BN - 1) / a.BN + a.S;
+  dim3 grid(plan.grid_x, unsigned(gy));
+  if (!plan.aligned_b || !plan.aligned_y || a.R != 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((expand_shared_kernel<DT, D, true>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_expand_dt(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st) {
   if constexpr (DT == DT_F32) {
     return launch_expand_t<DT, 4, 2, false>(a, plan, st);
   } else {
+    if (plan.variant == kExpandSharedD1) return launch_expand_shared_t<DT, 1>(a, plan, st);
+    if (plan.variant == kExpandSharedD2) return launch_expand_shared_t<DT, 2>(a, plan, st);
     switch (plan.variant) {
 #define X(V, NW, D, WIDE) \
       case V: return launch_expand_t<DT, NW, D, WIDE>(a, plan, st);

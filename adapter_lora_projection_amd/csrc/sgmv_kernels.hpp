@@ -66,6 +66,10 @@ struct ExpandPlan {
 
 int num_shrink_variants();
 int num_expand_variants();
+// Expand shapes of the shared-B kernel (64-token tiles, B chunks through LDS): slice rank exactly
+// 16, 16-bit types, 16-byte aligned h, B and y rows. Their column unit is one 128-column chunk.
+constexpr int kExpandSharedD1 = 8;
+constexpr int kExpandSharedD2 = 9;
 int shrink_plan_bm(int dtype, int variant);
 int expand_plan_bm(int dtype, int variant);
 int expand_plan_waves(int dtype, int variant);

@@ -26,7 +26,7 @@ def _alp():
     return alp
 
 
-def _run_pair(c, d=None, variant=(None, None), ksplit=None, lds=None):
+def _run_pair(c, d=None, variant=(None, None), ksplit=None, lds=None, bn=None):
     alp = _alp()
     from adapter_lora_projection_amd import _lib
 
@@ -40,6 +40,8 @@ def _run_pair(c, d=None, variant=(None, None), ksplit=None, lds=None):
             _lib.lora_tuning_override(3, ksplit)
         if lds is not None:
             _lib.lora_tuning_override(4, lds)
+        if bn is not None:
+            _lib.lora_tuning_override(2, bn)
         h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
                        d["lora_ranks"], c.S, c.R)
         y = d["y_in"].clone()
@@ -51,6 +53,7 @@ def _run_pair(c, d=None, variant=(None, None), ksplit=None, lds=None):
         _lib.lora_tuning_override(1, -1)
         _lib.lora_tuning_override(3, -1)
         _lib.lora_tuning_override(4, -1)
+        _lib.lora_tuning_override(2, -1)
     return h.cpu(), y.cpu()
 
 
@@ -103,7 +106,7 @@ def test_sweep(T):
 
 @pytest.mark.parametrize("direct", [False, True])
 @pytest.mark.parametrize("sv", range(5))
-@pytest.mark.parametrize("ev", range(8))  # every expand kernel shape
+@pytest.mark.parametrize("ev", range(10))  # every expand kernel shape
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_variants_small(sv, ev, dtype, direct):
     """Several tiles per segment plus ragged tails, odd ranks, K tail, unaligned slices; every
@@ -132,6 +135,36 @@ def test_wide_expand_shapes(ev, dtype, offs, R):
         c.B[a, :, r:] = float("nan")
     print("case", c.name, ev, offs, flush=True)
     h, y = _run_pair(c, variant=(0, ev))
+    _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("null_perm", [False, True])
+@pytest.mark.parametrize("bn", [None, 128, 256])
+@pytest.mark.parametrize("ev", [8, 9])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("offs", [[0, 128, 256, 520], [0, 132, 264, 520], [0, 1024, 1032, 2064]])
+def test_shared_b_expand(ev, dtype, offs, bn, null_perm):
+    """The rank-16 expand with B chunks shared through LDS (64-token tiles, 16 per wave), one or
+    two y chunks in flight: segments of 0, 5, 17, 37, 49, 64, 130 and 200 tokens, so tiles of
+    64 positions end inside a wave's 16 or leave whole waves idle; adapter ranks 16, 12, 7, 1
+    and 0 with NaN in the rank padding; slices on and off the 16-byte grid (the latter run the
+    8-byte form per wave); column blocks of one and two chunks and whole slices; tail chunks
+    of 8 columns; random permutation or NULL (identity)."""
+    lens = [37, 0, 5, 130, 64, 17, 200, 49]
+    indptr = np.concatenate(([0], np.cumsum(lens)))
+    c = li.make_sgmv(f"sharedb_{dtype}", seed=46, T=int(indptr[-1]), K=256, S=3, R=16, L=5,
+                     slice_offsets=offs, dtype=dtype, ranks=[16, 7, 1, 0, 12],
+                     fixed_indptr=indptr, fixed_weight_indices=[0, 1, 2, 3, 4, 0, 4, 1],
+                     identity_perm=null_perm)
+    for a in range(c.L):
+        r = int(c.lora_ranks[a])
+        c.A.view(c.L, c.S, c.R, c.K)[a, :, r:, :] = float("nan")
+        c.B[a, :, r:] = float("nan")
+    d = to_dev(c)
+    if null_perm:
+        d["permutation"] = None
+    print("case", c.name, ev, offs, bn, null_perm, flush=True)
+    h, y = _run_pair(c, d=d, variant=(0, ev), bn=bn)
     _check_pair(c, h, y)
 
 
