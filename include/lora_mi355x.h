@@ -128,7 +128,9 @@ size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_
  *   N              columns covered by the slices; slice_offsets[S] == N.
  *   h              device [T][ldh], ldh >= S*R, sorted order (the output of lora_shrink).
  *   w_b            device [L*N][ldb], ldb >= R: row a*N + n holds B[a][n][:]. Entries with
- *                  j >= lora_ranks[a] are never read.
+ *                  j >= lora_ranks[a] never reach the result: the kernels may load them with
+ *                  their row (within the first R entries) and zero them before use, so NaN or
+ *                  garbage there is harmless.
  *   slice_offsets  device int32 [S+1]: 0 <= slice_offsets[0] <= ... <= slice_offsets[S] = N.
  *   scalings       device float32 [L] (alpha / rank of each adapter).
  *   y              device [T][ldy] read and written in place, ldy >= N; row t is token t.
