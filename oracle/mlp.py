@@ -120,49 +120,38 @@ def lora_mlp_saved(x, w_gate, w_up, a_gate, b_gate, a_up, b_up, scale: float, ou
 
 
 def lora_mlp_backward(x, e, v, dout, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down,
-                      b_down, scale: float, out_dtype: str, return_intermediates: bool = False,
-                      given: dict | None = None):
+                      b_down, scale: float, out_dtype: str, return_intermediates: bool = False):
     """Gradients of the LoRA MLP (see the module docstring for the formulas and rounding points).
 
-    Returns a dict with dx [M][H], da_gate [r][H], db_gate [I][r], da_up [r][H], db_up [I][r],
-    da_down [r][I], db_down [H][r] (fp64 arrays holding values of ``out_dtype``).
+    ``e`` and ``v`` are the saved gate and up pre-activations; for the plain definition from the
+    input alone they come from ``lora_mlp_saved`` (``lora_mlp_grads`` does both steps).
 
-    ``given`` (optional) supplies stored intermediates by name (hmid, xa_g, xa_u, xa_d, dxa_d, de,
-    dv, dxa_g, dxa_u): every later step then uses the given value in place of its own, while the
-    returned intermediates are still computed here from their (given or own) inputs. This checks
-    each step of another implementation on that implementation's own inputs, so a one-unit
-    rounding difference of a stored intermediate is not carried into the later steps. With no
-    ``given`` it is the plain definition."""
+    Returns a dict with dx [M][H], da_gate [r][H], db_gate [I][r], da_up [r][H], db_up [I][r],
+    da_down [r][I], db_down [H][r] (fp64 arrays holding values of ``out_dtype``); with
+    ``return_intermediates`` also a dict of the stored intermediates (hmid, xa_*, dxa_*, de, dv)
+    and the unrounded dhmid."""
     x, e, v, d = _f64(x), _f64(e), _f64(v), _f64(dout)
     Wg, Wu, Wd = _f64(w_gate), _f64(w_up), _f64(w_down)
     Ag, Bg, Au, Bu = _f64(a_gate), _f64(b_gate), _f64(a_up), _f64(b_up)
     Ad, Bd = _f64(a_down), _f64(b_down)
     s = float(scale)
     rnd = lambda t: rho(t, out_dtype)
-    own = {}
-
-    def use(name, value):
-        """Record this step's own value; pass on the given one when there is one."""
-        own[name] = value
-        if given is not None and name in given:
-            return _f64(given[name])
-        return value
 
     # recomputed forward quantities
     f = silu(e)
-    hmid = use("hmid", rnd(f * v))
-    xa_g = use("xa_g", rnd(x @ Ag.T))
-    xa_u = use("xa_u", rnd(x @ Au.T))
-    xa_d = use("xa_d", rnd(hmid @ Ad.T))
+    hmid = rnd(f * v)
+    xa_g = rnd(x @ Ag.T)
+    xa_u = rnd(x @ Au.T)
+    xa_d = rnd(hmid @ Ad.T)
     # down projection: out = hmid W_d^T + s (hmid A_d^T) B_d^T
-    dxa_d = use("dxa_d", rnd(s * (d @ Bd)))
+    dxa_d = rnd(s * (d @ Bd))
     dhmid = d @ Wd + dxa_d @ Ad
     # SwiGLU: hmid = silu(e) * v
-    de = use("de", rnd(dhmid * v * silu_grad(e)))
-    dv = use("dv", rnd(dhmid * f))
+    de = rnd(dhmid * v * silu_grad(e))
+    dv = rnd(dhmid * f)
     # gate and up projections
-    dxa_g = use("dxa_g", rnd(s * (de @ Bg)))
-    dxa_u = use("dxa_u", rnd(s * (dv @ Bu)))
+    dxa_g = rnd(s * (de @ Bg))
+    dxa_u = rnd(s * (dv @ Bu))
     dx = rnd(de @ Wg + dv @ Wu + dxa_g @ Ag + dxa_u @ Au)
     grads = {
         "dx": dx,
@@ -171,5 +160,16 @@ def lora_mlp_backward(x, e, v, dout, w_gate, w_up, w_down, a_gate, b_gate, a_up,
         "da_down": rnd(dxa_d.T @ hmid), "db_down": rnd(s * (d.T @ xa_d)),
     }
     if return_intermediates:
-        return grads, dict(own, dhmid=dhmid)
+        inter = {"hmid": hmid, "xa_g": xa_g, "xa_u": xa_u, "xa_d": xa_d, "dxa_d": dxa_d,
+                 "de": de, "dv": dv, "dxa_g": dxa_g, "dxa_u": dxa_u, "dhmid": dhmid}
+        return grads, inter
     return grads
+
+
+def lora_mlp_grads(x, dout, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_down,
+                   scale: float, out_dtype: str, return_intermediates: bool = False):
+    """The gradients from the layer input, the upstream gradient and the weights alone: the saved
+    pre-activations of ``lora_mlp_saved`` fed to ``lora_mlp_backward``."""
+    e, v = lora_mlp_saved(x, w_gate, w_up, a_gate, b_gate, a_up, b_up, scale, out_dtype)
+    return lora_mlp_backward(x, e, v, dout, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up,
+                             a_down, b_down, scale, out_dtype, return_intermediates)

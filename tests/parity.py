@@ -6,6 +6,18 @@ Tolerances (stated by the workload definition and restated here):
 * fp32 outputs: |gpu - oracle| <= 1e-5 * M per element, where M is the magnitude the sum is
   conditioned on (sum of |terms|, plus |y_in| for expand), computed by the oracle on absolute
   values; this equals 1e-5 * |oracle| when nothing cancels.
+* bf16 gradients of the MLP backward (sums whose terms carry bf16-stored factors, such as
+  dA = dxa^T x over 4096 tokens): |gpu - ref| <= 1e-2 + 1e-2 |ref| + u * RSS, with u = 2^-8 the
+  unit roundoff of bf16 and RSS the root-sum-square of the sum's terms, from the oracle's own
+  values. Derivation: a stored bf16 factor (de, dv, hmid, the LoRA-A products) whose exact value
+  lies within the accumulation error of a rounding boundary is rounded one way by an fp32
+  evaluation and the other way by the fp64 oracle; each such decision moves its term by up to
+  2u of itself, with a sign independent of the others, so the sum moves by about
+  2u sqrt(p) RSS when a fraction p of the terms disagree. u * RSS is one standard deviation at
+  p = 1/4; an fp32 evaluation disagrees on fewer than 0.1% of the stored values. Near |ref| = 0
+  (cancellation over the tokens) the plain 1e-2 + 1e-2 |ref| bar is far below that noise: a
+  correct fp32 evaluation fails it on 0.07-1.6% of the weight-gradient entries at the Qwen3-8B
+  layer (tests/test_backward_tolerance.py shows both facts on the CPU).
 """
 
 from __future__ import annotations
@@ -40,6 +52,55 @@ def assert_close_lowp(got, ref, what=""):
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; first "
                              f"{[(tuple(i), g[tuple(i)], r[tuple(i)]) for i in idx]}")
+
+
+BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8-bit significand)
+
+
+def assert_close_sum_lowp(got, ref, rss, what=""):
+    """bf16 sum whose terms carry bf16-stored factors: |got - ref| <= 1e-2 + 1e-2 |ref| + u RSS."""
+    g = f64(got)
+    r = f64(ref)
+    q = f64(rss)
+    bad = ~(np.abs(g - r) <= 1e-2 + 1e-2 * np.abs(r) + BF16_U * q)
+    bad |= np.isnan(g) != np.isnan(r)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside 1e-2+1e-2|ref|+u*RSS; first "
+                             f"{[(tuple(i), g[tuple(i)], r[tuple(i)], q[tuple(i)]) for i in idx]}")
+
+
+def strict_fail_fraction(got, ref) -> float:
+    """Fraction of entries outside the plain bar 1e-2 + 1e-2 |ref| (reported, not asserted)."""
+    g = f64(got)
+    r = f64(ref)
+    return float(np.mean(~(np.abs(g - r) <= 1e-2 + 1e-2 * np.abs(r))))
+
+
+def backward_rss(x, dout, w, inter, scale, rows=None):
+    """Root-sum-square of the terms of each MLP-backward gradient's sum, from the oracle's own
+    fp64 values (``inter`` from oracle.lora_mlp_backward(..., return_intermediates=True); ``w``
+    maps the weight names to tensors). ``rows``: dx on those token rows only.
+
+    dx[m]      = de[m] W_g + dv[m] W_u + dxa_g[m] A_g + dxa_u[m] A_u
+    dA_g[j][k] = sum_m dxa_g[m][j] x[m][k]       dB_g[i][j] = s sum_m de[m][i] xa_g[m][j]
+    dA_d[j][i] = sum_m dxa_d[m][j] hmid[m][i]    dB_d[n][j] = s sum_m dout[m][n] xa_d[m][j]
+    (up like gate)."""
+    sq = lambda t: np.square(f64(t))
+    s2 = float(scale) ** 2
+    X, D = sq(x), sq(dout)
+    sel = (lambda t: t) if rows is None else (lambda t: t[rows])
+    de, dv = sq(inter["de"]), sq(inter["dv"])
+    dx = (sel(de) @ sq(w["w_gate"]) + sel(dv) @ sq(w["w_up"]) + sel(sq(inter["dxa_g"])) @ sq(w["a_gate"])
+          + sel(sq(inter["dxa_u"])) @ sq(w["a_up"]))
+    out = {
+        "dx": np.sqrt(dx),
+        "da_gate": np.sqrt(sq(inter["dxa_g"]).T @ X), "db_gate": np.sqrt(s2 * (de.T @ sq(inter["xa_g"]))),
+        "da_up": np.sqrt(sq(inter["dxa_u"]).T @ X), "db_up": np.sqrt(s2 * (dv.T @ sq(inter["xa_u"]))),
+        "da_down": np.sqrt(sq(inter["dxa_d"]).T @ sq(inter["hmid"])),
+        "db_down": np.sqrt(s2 * (D.T @ sq(inter["xa_d"]))),
+    }
+    return out
 
 
 def assert_close_f32(got, ref, mag, what=""):

@@ -1,17 +1,15 @@
 """GPU parity of the LoRA MLP training forward and backward (through the C ABI) against the CPU
-oracle, bf16 tolerance |err| <= 1e-2 + 1e-2 |ref|.
+oracle computed from x, dout and the weights alone (oracle.lora_mlp_grads: its own saved
+pre-activations, its own intermediates).
 
-Each step is checked on its own inputs: the saved pre-activations e, v against the oracle's
-from x; every stored intermediate of the backward (hmid, de, dv, the LoRA-A products and their
-gradients) against the oracle's step applied to the GPU's own inputs of that step, and every
-gradient against the oracle applied to the GPU's intermediates. A stored bf16 intermediate may
-differ from the oracle's by one unit where its fp32 and fp64 values straddle a rounding
-boundary; carried into a later sum with cancellation (dA = dxa^T x over the tokens) such a
-difference alone can exceed the tolerance, so only the small layers are also compared end to
-end (oracle from x, e, v and dout alone). Small layers compare every output; the Qwen3-8B-shaped
-layer (H = 4096, I = 12288, r = 16, scale 4) compares every output on its first 160 tokens
-(M = 160: one partial row tile) and, at M = 4096, sampled rows of e, v, out and dx and sampled
-columns of de, dv, hmid, db_gate, db_up and da_down.
+Tolerances (tests/parity.py): the saved pre-activations e, v and the output are stored values of
+row-local sums, compared with the plain bf16 bar |err| <= 1e-2 + 1e-2 |ref|; the seven gradients
+are sums whose terms carry bf16-stored factors and are compared with 1e-2 + 1e-2 |ref| + u RSS
+(u = 2^-8, RSS the root-sum-square of the sum's terms from the oracle's values), the bar derived
+in tests/parity.py; the fraction outside the plain bar is printed. Small layers compare every
+output; the Qwen3-8B-shaped layer (H = 4096, I = 12288, r = 16, scale 4) compares every output on
+its first 160 tokens and, at M = 4096, all seven gradients in full against the oracle over all
+4096 tokens (e, v and out on sampled rows).
 """
 
 import functools
@@ -22,9 +20,8 @@ import torch
 
 import lora_inputs as li
 import oracle
-from oracle.mlp import silu, silu_grad
-from oracle.rounding import rho
-from tests.parity import assert_close_lowp
+from tests.parity import (assert_close_lowp, assert_close_sum_lowp, backward_rss,
+                          strict_fail_fraction)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,38 +41,36 @@ def _gpu(c, dout):
                                     c.scale)
     w_gu_t, w_down_t = alp.mlp_prepare_backward(d["w_gate"], d["w_up"], d["w_down"])
     x_before = d["x"].clone()
-    g, inter = alp.mlp_backward(d["x"], e, v, dout.to("cuda").contiguous(), w_gu_t, w_down_t,
-                                *[d[k] for k in LORA], c.scale, return_intermediates=True)
+    g = alp.mlp_backward(d["x"], e, v, dout.to("cuda").contiguous(), w_gu_t, w_down_t,
+                         *[d[k] for k in LORA], c.scale)
     torch.cuda.synchronize()
     assert torch.equal(d["x"], x_before)  # the saved input is only read
     # the prepared layouts are the transposes of the frozen weights, bit for bit
     assert torch.equal(w_gu_t[:, :c.I].cpu(), c.w_gate.T.contiguous())
     assert torch.equal(w_gu_t[:, c.I:].cpu(), c.w_up.T.contiguous())
     assert torch.equal(w_down_t.cpu(), c.w_down.T.contiguous())
-    return (out.cpu(), e.cpu(), v.cpu(), {k: t.cpu() for k, t in g.items()},
-            {k: t.cpu() for k, t in inter.items()})
+    return out.cpu(), e.cpu(), v.cpu(), {k: t.cpu() for k, t in g.items()}
 
 
-def _check_all(c, dout, out, e, v, g, inter, end_to_end):
-    re, rv = oracle.lora_mlp_saved(c.x, c.w_gate, c.w_up, c.a_gate, c.b_gate, c.a_up, c.b_up,
+def _check_all(c, dout, out, e, v, g, rows=None):
+    """e, v, out (on ``rows``, all when None) and the seven gradients in full, end to end."""
+    sel = (lambda t: t) if rows is None else (lambda t: t[rows])
+    xs = sel(c.x)
+    re, rv = oracle.lora_mlp_saved(xs, c.w_gate, c.w_up, c.a_gate, c.b_gate, c.a_up, c.b_up,
                                    c.scale, "bf16")
-    assert_close_lowp(e, re, f"e {c.name}")
-    assert_close_lowp(v, rv, f"v {c.name}")
-    ro = oracle.lora_mlp(c.x, c.w_gate, c.w_up, c.w_down, *[getattr(c, k) for k in LORA], c.scale,
+    assert_close_lowp(sel(e), re, f"e {c.name}")
+    assert_close_lowp(sel(v), rv, f"v {c.name}")
+    ro = oracle.lora_mlp(xs, c.w_gate, c.w_up, c.w_down, *[getattr(c, k) for k in LORA], c.scale,
                          "bf16")
-    assert_close_lowp(out, ro, f"out {c.name}")
-    W = (c.w_gate, c.w_up, c.w_down, *[getattr(c, k) for k in LORA])
-    # step by step: each intermediate and gradient from the GPU's own inputs of that step
-    ref, own = oracle.lora_mlp_backward(c.x, e, v, dout, *W, c.scale, "bf16",
-                                        return_intermediates=True, given=inter)
-    for k, t in inter.items():
-        assert_close_lowp(t, own[k], f"{k} {c.name}")
+    assert_close_lowp(sel(out), ro, f"out {c.name}")
+    W = {k: getattr(c, k) for k in ("w_gate", "w_up", "w_down") + LORA}
+    ref, inter = oracle.lora_mlp_grads(c.x, dout, *W.values(), c.scale, "bf16",
+                                       return_intermediates=True)
+    rss = backward_rss(c.x, dout, W, inter, c.scale)
+    fails = {k: strict_fail_fraction(g[k], ref[k]) for k in NAMES}
+    print(f"{c.name}: fraction outside the plain bar {fails}", flush=True)
     for k in NAMES:
-        assert_close_lowp(g[k], ref[k], f"{k} {c.name}")
-    if end_to_end:
-        ref = oracle.lora_mlp_backward(c.x, e, v, dout, *W, c.scale, "bf16")
-        for k in NAMES:
-            assert_close_lowp(g[k], ref[k], f"{k} {c.name} end to end")
+        assert_close_sum_lowp(g[k], ref[k], rss[k], f"{k} {c.name}")
 
 
 @pytest.mark.parametrize("M,H,I,r,scale", [
@@ -89,8 +84,8 @@ def test_backward_small(M, H, I, r, scale):
     c = li.config_mlp(seed=70 + M, M=M, H=H, I=I, r=r, scale=scale)
     dout = li.mlp_dout(seed=70 + M, M=M, H=H)
     print("case", c.name, flush=True)
-    out, e, v, g, inter = _gpu(c, dout)
-    _check_all(c, dout, out, e, v, g, inter, end_to_end=True)
+    out, e, v, g = _gpu(c, dout)
+    _check_all(c, dout, out, e, v, g)
 
 
 def test_b_zero_gives_zero_lora_a_gradients():
@@ -99,10 +94,10 @@ def test_b_zero_gives_zero_lora_a_gradients():
         setattr(c, k, torch.zeros_like(getattr(c, k)))
     dout = li.mlp_dout(seed=81, M=128, H=128)
     print("case", c.name, "B=0", flush=True)
-    out, e, v, g, inter = _gpu(c, dout)
+    out, e, v, g = _gpu(c, dout)
     for k in ("da_gate", "da_up", "da_down"):
         assert torch.all(g[k] == 0), k
-    _check_all(c, dout, out, e, v, g, inter, end_to_end=True)
+    _check_all(c, dout, out, e, v, g)
 
 
 def test_autograd_function_matches_the_direct_calls():
@@ -141,51 +136,15 @@ def test_qwen3_8b_layer_first_160_tokens():
     c.x = full.x[:M].contiguous()
     dout = full_dout[:M].contiguous()
     print("case", c.name, flush=True)
-    out, e, v, g, inter = _gpu(c, dout)
-    _check_all(c, dout, out, e, v, g, inter, end_to_end=False)
+    out, e, v, g = _gpu(c, dout)
+    _check_all(c, dout, out, e, v, g)
 
 
-def test_qwen3_8b_layer_sampled():
+def test_qwen3_8b_layer_full():
     c, dout = _qwen3_8b()
-    print("case", c.name, "sampled", flush=True)
-    out, e, v, g, inter = _gpu(c, dout)
+    print("case", c.name, "M = 4096", flush=True)
+    out, e, v, g = _gpu(c, dout)
     rng = np.random.default_rng(9)
-    rows = np.sort(rng.choice(c.M, size=24, replace=False))
+    rows = np.sort(rng.choice(c.M, size=32, replace=False))
     rows[0], rows[-1] = 0, c.M - 1
-    W = [getattr(c, k) for k in LORA]
-    # e, v, out on sampled rows (each row depends on its own input row only)
-    re, rv = oracle.lora_mlp_saved(c.x[rows], c.w_gate, c.w_up, c.a_gate, c.b_gate, c.a_up, c.b_up,
-                                   c.scale, "bf16")
-    assert_close_lowp(e[rows], re, "e rows")
-    assert_close_lowp(v[rows], rv, "v rows")
-    ro = oracle.lora_mlp_rows(rows, c.x, c.w_gate, c.w_up, c.w_down, *W, c.scale, "bf16")
-    assert_close_lowp(out[rows], ro, "out rows")
-    # every row-local step on the sampled rows, from the GPU's own inputs of each step (the
-    # oracle's weight gradients are then partial sums over those rows and are not used)
-    given = {k: t[rows] for k, t in inter.items()}
-    rb, own = oracle.lora_mlp_backward(c.x[rows], e[rows], v[rows], dout[rows], c.w_gate, c.w_up,
-                                       c.w_down, *W, c.scale, "bf16", return_intermediates=True,
-                                       given=given)
-    for k, t in given.items():
-        assert_close_lowp(t, own[k], f"{k} rows")
-    assert_close_lowp(g["dx"][rows], rb["dx"], "dx rows")
-    # sampled columns i: de, dv, hmid (over all tokens) from the GPU's inputs of their step, and
-    # the sums over the tokens db_gate[i], db_up[i], da_down[:, i] from the GPU's intermediates
-    f64 = lambda t: t.to(torch.float64).numpy()
-    d, E, V = f64(dout), f64(e), f64(v)
-    s = c.scale
-    dxa_d = f64(inter["dxa_d"])
-    Wd, Ad = f64(c.w_down), f64(c.a_down)
-    xa_g, xa_u = f64(inter["xa_g"]), f64(inter["xa_u"])
-    cols = np.sort(rng.choice(c.I, size=24, replace=False))
-    cols[0], cols[-1] = 0, c.I - 1
-    for i in cols:
-        dh = d @ Wd[:, i] + dxa_d @ Ad[:, i]
-        f = silu(E[:, i])
-        assert_close_lowp(inter["de"][:, i], rho(dh * V[:, i] * silu_grad(E[:, i]), "bf16"), f"de col {i}")
-        assert_close_lowp(inter["dv"][:, i], rho(dh * f, "bf16"), f"dv col {i}")
-        assert_close_lowp(inter["hmid"][:, i], rho(f * V[:, i], "bf16"), f"hmid col {i}")
-        de, dv, hm = f64(inter["de"][:, i]), f64(inter["dv"][:, i]), f64(inter["hmid"][:, i])
-        assert_close_lowp(g["db_gate"][i], rho(s * (de @ xa_g), "bf16"), f"db_gate col {i}")
-        assert_close_lowp(g["db_up"][i], rho(s * (dv @ xa_u), "bf16"), f"db_up col {i}")
-        assert_close_lowp(g["da_down"][:, i], rho(dxa_d.T @ hm, "bf16"), f"da_down col {i}")
+    _check_all(c, dout, out, e, v, g, rows=rows)
