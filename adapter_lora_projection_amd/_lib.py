@@ -15,6 +15,20 @@ LIB_PATH = os.path.join(HERE, "liblora_mi355x.so")
 
 LORA_OK, LORA_EINVAL, LORA_EUNSUPPORTED, LORA_EWORKSPACE, LORA_EHIP, LORA_EVALUE = range(6)
 LORA_F32, LORA_BF16, LORA_F16 = 0, 1, 2
+LORA_SHRINK_RING_SHAPES, LORA_SHRINK_LDS_SHAPES, LORA_EXPAND_SHAPES = 5, 5, 10
+
+
+class Plan(ctypes.Structure):
+    """``lora_plan``: explicit kernel-shape choices of one call (-1 = the library's choice)."""
+
+    _fields_ = [("shrink_kernel", ctypes.c_int32), ("shrink_shape", ctypes.c_int32),
+                ("shrink_split", ctypes.c_int32), ("shrink_finish", ctypes.c_int32),
+                ("expand_shape", ctypes.c_int32), ("expand_block_n", ctypes.c_int32)]
+
+    def __init__(self, shrink_kernel=-1, shrink_shape=-1, shrink_split=-1, shrink_finish=-1,
+                 expand_shape=-1, expand_block_n=-1):
+        super().__init__(shrink_kernel, shrink_shape, shrink_split, shrink_finish, expand_shape,
+                         expand_block_n)
 
 # Every symbol the public header declares, with (restype, argtypes).
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
@@ -29,7 +43,11 @@ SIGNATURES = {
     "lora_expand_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, _i64]),
     "lora_schedule_tiles": (_i32, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                    _sz, _vp]),
-    "lora_tuning_override": (None, [_i32, _i32]),
+    "lora_shrink_ex": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
+                              _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "lora_shrink_workspace_size_ex": (_sz, [_i32, _i64, _i64, _i32, _i32, _i32, _vp]),
+    "lora_expand_ex": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _i64,
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_mlp_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
     "lora_mlp_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
@@ -114,6 +132,32 @@ def lora_shrink_workspace_size(dtype, T, K, S, R, G) -> int:
     return int(lib().lora_shrink_workspace_size(dtype, T, K, S, R, G))
 
 
+def _plan(plan):
+    return None if plan is None else ctypes.addressof(plan)
+
+
+def lora_shrink_ex(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr, weight_indices,
+                   permutation, lora_ranks, h, ldh, plan, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_shrink_ex(dtype, T, K, S, R, L, G, _p(x), ldx, _p(w_a), lda, _p(seg_indptr),
+                              _p(weight_indices), _p(permutation), _p(lora_ranks), _p(h), ldh,
+                              _plan(plan), _p(workspace), workspace_bytes, stream)
+    _check("lora_shrink_ex", st)
+
+
+def lora_shrink_workspace_size_ex(dtype, T, K, S, R, G, plan) -> int:
+    return int(lib().lora_shrink_workspace_size_ex(dtype, T, K, S, R, G, _plan(plan)))
+
+
+def lora_expand_ex(dtype, T, S, R, L, G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
+                   weight_indices, permutation, lora_ranks, scalings, y, ldy, plan, workspace,
+                   workspace_bytes, stream) -> None:
+    st = lib().lora_expand_ex(dtype, T, S, R, L, G, N, _p(h), ldh, _p(w_b), ldb, _p(slice_offsets),
+                              _p(seg_indptr), _p(weight_indices), _p(permutation), _p(lora_ranks),
+                              _p(scalings), _p(y), ldy, _plan(plan), _p(workspace),
+                              workspace_bytes, stream)
+    _check("lora_expand_ex", st)
+
+
 def lora_expand(dtype, T, S, R, L, G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
                 weight_indices, permutation, lora_ranks, scalings, y, ldy, workspace,
                 workspace_bytes, stream) -> None:
@@ -176,10 +220,6 @@ def lora_mlp_backward(dtype, M, H, I, r, scale, x, ldx, e, v, lde, dout, lddo, w
 
 def lora_mlp_backward_workspace_size(dtype, M, H, I, r) -> int:
     return int(lib().lora_mlp_backward_workspace_size(dtype, M, H, I, r))
-
-
-def lora_tuning_override(op: int, variant: int) -> None:
-    lib().lora_tuning_override(op, variant)
 
 
 def lora_linear_fused(dtype, M, K, N, r, scale, x, ldx, w, a, b, out, ldo, workspace,

@@ -18,11 +18,38 @@ constexpr int kInlineMaxSegments = 1024;  // above this the standalone scheduler
 constexpr int kMaxSlices = 64;
 constexpr int kMaxRank = 1024;
 
-int g_shrink_override = -1;
-int g_lds_override = -1;  // shrink kernel family: 0 = register ring, 1 = LDS-staged where eligible
-int g_sk_override = -1;  // shrink workgroups along x in stream-K mode; 0 = direct mode
-int g_expand_override = -1;
-int g_expand_bn_override = -1;
+// Arrival counters of the in-launch stream-K completion: the first kCounterBytes of every
+// nonzero shrink workspace, zero before the call and zero after it.
+constexpr size_t kCounterBytes = 32768;
+constexpr int64_t kMaxCounters = int64_t(kCounterBytes / 4);
+
+// The caller's kernel-shape choices (lora_plan; -1 = the library's own choice). A plain value
+// passed down the planning functions: the library keeps no state between calls.
+struct Knobs {
+  int family = -1, shape = -1, split = -1, finish = -1, eshape = -1, ebn = -1;
+};
+
+Knobs knobs_of(const lora_plan* p) {
+  Knobs k;
+  if (p == nullptr) return k;
+  k.family = p->shrink_kernel;
+  k.shape = p->shrink_shape;
+  k.split = p->shrink_split;
+  k.finish = p->shrink_finish;
+  k.eshape = p->expand_shape;
+  k.ebn = p->expand_block_n;
+  return k;
+}
+
+// Plan fields outside their documented ranges are argument errors.
+bool knobs_valid(const Knobs& k) {
+  return k.family >= -1 && k.family <= 1 && k.shape >= -1 &&
+         k.shape < std::max(lmx::num_shrink_variants(), lmx::num_shrink_lds_variants()) &&
+         !(k.family == 1 && k.shape >= lmx::num_shrink_lds_variants()) &&
+         !(k.family == 0 && k.shape >= lmx::num_shrink_variants()) && k.split >= -1 &&
+         k.split <= 65535 && k.finish >= -1 && k.finish <= 1 && k.eshape >= -1 &&
+         k.eshape < lmx::num_expand_variants() && (k.ebn == -1 || (k.ebn >= 1 && k.ebn <= 65536));
+}
 
 bool valid_dtype(int d) { return d == LORA_F32 || d == LORA_BF16 || d == LORA_F16; }
 
@@ -39,9 +66,10 @@ int esize(int dtype) { return dtype == LORA_F32 ? 4 : 2; }
 // also takes at least 600 / tiles blocks: more blocks than that leave a second round of
 // workgroups (8192 tokens: 660 workgroups 55.7 us, 792 workgroups 63.6 us), fewer leave the
 // chip half idle (6144 tokens: 500 workgroups 44.0 us, 600 workgroups 40.6 us).
-int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves, int chunk, bool shared) {
+int expand_bn(const Knobs& kn, int64_t T, int32_t G, int64_t N, int bm, int waves, int chunk,
+              bool shared) {
   const int unit = chunk * waves;
-  if (g_expand_bn_override > 0) return int(cdiv(g_expand_bn_override, unit) * unit);
+  if (kn.ebn > 0) return int(cdiv(kn.ebn, unit) * unit);
   const int64_t tiles = cdiv(T, bm) + G;
   int64_t blocks = std::max<int64_t>(1, cdiv(400, tiles));
   if (shared) blocks = std::max<int64_t>(blocks, 600 / tiles);
@@ -50,15 +78,23 @@ int expand_bn(int64_t T, int32_t G, int64_t N, int bm, int waves, int chunk, boo
   return int(bn);
 }
 
-// Kernel shape for a shrink call, from host-known sizes only (rocprofv3 sweeps on MI355X over
-// the decode sweep, prefill and irregular workloads). Small token counts: one token group and
-// one 16-column block per workgroup, 8 waves splitting K. Otherwise two token groups per
-// workgroup sharing each A fragment, over 3 column blocks, or 4 when the slices have 4 or fewer
-// blocks that 3 does not divide. The 2-deep operand ring measured faster than 4-deep.
-int shrink_variant(int64_t T, int32_t S, int32_t R) {
-  if (g_shrink_override >= 0) return g_shrink_override;
+// Kernel shape for a shrink call, from host-known sizes only (event timings and rocprofv3 sweeps
+// on MI355X over the decode sweep, prefill and irregular workloads). One compute unit streams
+// about 25 GB/s through the register ring, so the time of a call is set by the bytes each
+// workgroup streams (x rows of its tile and A rows of its column blocks over all of K) as long as
+// the grid fits on the chip. One token group of 16 and one 16-column block per workgroup, 8
+// waves splitting K, while that grid stays within two workgroups per compute unit; beyond that
+// two token groups sharing each A fragment over 3 column blocks (x read once per tile), or 4
+// when the slices have 4 or fewer blocks that 3 does not divide. The 2-deep operand ring
+// measured faster than 4-deep. `pub`: the shrink entry point (the internal dense products keep
+// the rule they were tuned with: two token groups from 2048 rows).
+int shrink_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t G, bool pub) {
+  if (kn.shape >= 0 && kn.shape < lmx::num_shrink_variants()) return kn.shape;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  if (nblk % 3 == 0) return T <= 2048 ? 2 : 4;
+  if (nblk % 3 == 0) {
+    if (!pub) return T <= 2048 ? 2 : 4;
+    return (cdiv(T, 16) + G) * nblk <= 512 ? 2 : 4;
+  }
   return nblk <= 4 ? 1 : 4;
 }
 
@@ -67,9 +103,10 @@ int shrink_variant(int64_t T, int32_t S, int32_t R) {
 // share of the (tile, reduction step) work, about one workgroup per compute unit.
 struct ShrinkWs {
   bool lds;          // LDS-staged kernel (else the register-ring kernel)
-  int variant, bm, grid_x, mp, unit;
+  bool in_launch;    // stream-K pieces added by each tile's last workgroup (arrival counters)
+  int variant, bm, grid_x, gy, mp, unit;
   int64_t bound, q;  // tile bound; stream-K units per workgroup (0 = direct mode)
-  size_t sched, part, total;
+  size_t sched, part, total;  // byte offsets: schedule list at kCounterBytes, partial planes
 };
 
 // Expand kernel shape (rocprofv3 sweeps and event timings on MI355X). From 1024 tokens, slices of
@@ -79,11 +116,10 @@ struct ShrinkWs {
 // and a 1-deep ring (fewer bytes in flight per compute unit measured faster than deeper rings;
 // the wide chunks saved 3-12% at 2048..6144 tokens). Blocks whose y rows or start are not
 // 16-byte aligned take the 8-byte form inside the same launch.
-int expand_variant(int64_t T, bool shared_ok) {
-  if (g_expand_override >= 0) {
-    const bool shared = g_expand_override == lmx::kExpandSharedD1 ||
-                        g_expand_override == lmx::kExpandSharedD2;
-    return (shared && !shared_ok) ? 6 : g_expand_override;
+int expand_variant(const Knobs& kn, int64_t T, bool shared_ok) {
+  if (kn.eshape >= 0) {
+    const bool shared = kn.eshape == lmx::kExpandSharedD1 || kn.eshape == lmx::kExpandSharedD2;
+    return (shared && !shared_ok) ? 6 : kn.eshape;
   }
   if (shared_ok && T >= 1024) return lmx::kExpandSharedD1;
   return T >= 2048 ? 6 : 3;
@@ -99,59 +135,90 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // The LDS-staged shrink covers the 16-bit types whose x and A rows are 16-byte aligned and
 // whose K is a multiple of 8; its shape is the smallest column-block count that holds every
 // block of the slices (or 12 blocks per workgroup beyond that).
-int shrink_lds_variant(int32_t S, int32_t R) {
-  if (g_shrink_override >= 0 && g_shrink_override < lmx::num_shrink_lds_variants())
-    return g_shrink_override;
+int shrink_lds_variant(const Knobs& kn, int32_t S, int32_t R) {
+  if (kn.shape >= 0 && kn.shape < lmx::num_shrink_lds_variants()) return kn.shape;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
   for (int v = 0; v < lmx::num_shrink_lds_variants(); ++v)
     if (lmx::shrink_lds_ncb(v) >= nblk) return v;
   return lmx::num_shrink_lds_variants() - 1;
 }
 
-// Which shrink kernel to run when the LDS-staged one is eligible (rocprofv3 sweeps on MI355X):
-// it pays for its shared-work second launch when every compute unit streams a lot of x
-// (T * K at least 16 Mi elements: decode tok >= 4096, prefill down-proj, the MLP's LoRA-A)
-// and the slices have few column blocks; the register-ring kernel is faster below that.
-bool prefer_lds(int64_t T, int64_t K, int32_t S, int32_t R) {
-  if (g_lds_override >= 0) return g_lds_override == 1;
+// Which shrink kernel to run when the LDS-staged one is eligible (event timings and rocprofv3
+// sweeps on MI355X). The LDS-staged kernel streams about twice as fast per workgroup (its
+// direct-to-LDS loads keep more bytes in flight) and shares each A chunk over 128 positions,
+// but a tile of 128 positions leaves most compute units idle unless T is large. Internal dense
+// products (fused MLP, projections, backward): from T * K = 16 Mi elements with few column
+// blocks, as tuned with their shared-work second launch. Shrink entry point: when even the
+// register ring's wider shape would need a second round of workgroups (decode 8192 tokens:
+// 260 workgroups of 32 positions), and T * K is large.
+bool prefer_lds(const Knobs& kn, int64_t T, int64_t K, int32_t S, int32_t R) {
+  if (kn.family >= 0) return kn.family == 1;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
   return T * K >= (int64_t(16) << 20) && nblk <= 4;
 }
 
-ShrinkWs shrink_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t G, bool lds) {
+bool prefer_lds_pub(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                    int32_t G) {
+  if (kn.family >= 0) return kn.family == 1;
+  const int64_t nblk = int64_t(S) * ((R + 15) / 16);
+  if (T * K < (int64_t(16) << 20) || nblk > 4) return false;
+  const int v = shrink_variant(kn, T, S, R, G, true);
+  const int64_t ring_wgs = (cdiv(T, lmx::shrink_plan_bm(dtype, v)) + G) *
+                           cdiv(nblk, lmx::shrink_plan_cb(dtype, v));
+  return ring_wgs > 256;
+}
+
+ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                   int32_t G, bool lds, bool in_launch_ok) {
   ShrinkWs w{};
   w.lds = lds;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
   int64_t gy, frags;
   if (lds) {
-    w.variant = shrink_lds_variant(S, R);
+    w.variant = shrink_lds_variant(kn, S, R);
     w.bm = lmx::kShrinkLdsBM;
     w.unit = lmx::kShrinkLdsUnit;
     gy = cdiv(nblk, lmx::shrink_lds_ncb(w.variant));
     frags = (w.bm + 16 * lmx::shrink_lds_ncb(w.variant)) / 8;  // 1 KiB loads per stage
   } else {
-    w.variant = shrink_variant(T, S, R);
+    w.variant = shrink_variant(kn, T, S, R, G, in_launch_ok);
     w.bm = lmx::shrink_plan_bm(dtype, w.variant);
     w.unit = dtype == LORA_F32 ? 16 : 32;
     gy = cdiv(nblk, lmx::shrink_plan_cb(dtype, w.variant));
     frags = w.bm / 16 + lmx::shrink_plan_cb(dtype, w.variant);  // 1 KiB loads per step
   }
+  w.gy = int(gy);
   w.bound = cdiv(T, w.bm) + G;
   const int64_t nsteps = cdiv(K, w.unit);
-  // Shared (tile, step) work pays for its second launch only when one workgroup per tile leaves
-  // half the compute units idle and each workgroup would stream a lot.
-  // (The LDS-staged kernel is chosen only for such problems: it always shares when its tiles
-  // leave compute units idle.)
+  // Shared (tile, step) work pays when one workgroup per tile leaves most compute units idle and
+  // each workgroup would stream a lot. With the in-launch completion (arrival counters; the
+  // shrink entry point) it costs three dependent memory round trips instead of a second launch:
+  // measured on the decode sweep it pays only below about 48 direct workgroups (50 tokens: 24
+  // workgroups 14.9 us, 192 sharing 12.0 us, cold calls), with 64 workgroups per grid row; the
+  // LDS-staged kernel runs direct there (8192 tokens: 52 us against 55 us shared). The internal
+  // dense products keep their second launch and the rule they were tuned with.
   const int64_t direct_wgs = w.bound * gy;
-  const bool shared = lds ? direct_wgs < 256
-                          : direct_wgs < 128 && nsteps * frags * 1024 >= (int64_t(512) << 10);
-  const int64_t P = g_sk_override >= 0 ? g_sk_override : (shared ? std::max<int64_t>(1, 256 / gy) : 0);
+  const bool counters_fit = in_launch_ok && w.bound * gy <= kMaxCounters;
+  w.in_launch = kn.finish >= 0 ? (kn.finish == 1 && counters_fit) : counters_fit;
+  bool shared;
+  int64_t pdef;
+  if (w.in_launch) {
+    shared = !lds && direct_wgs < 48;
+    pdef = std::max<int64_t>(1, 192 / gy);
+  } else {
+    shared = lds ? direct_wgs < 256
+                 : direct_wgs < 128 && nsteps * frags * 1024 >= (int64_t(512) << 10);
+    pdef = std::max<int64_t>(1, 256 / gy);
+  }
+  const int64_t P = kn.split >= 0 ? kn.split : (shared ? pdef : 0);
   w.sched = schedule_bytes(T, G, w.bm);
-  w.part = align256(w.sched);
+  const size_t base = kCounterBytes;  // the counter region leads every nonzero workspace
+  w.part = align256(base + w.sched);
   if (P == 0) {
     w.q = 0;
+    w.in_launch = false;
     w.grid_x = int(w.bound);
-    w.total = w.sched;
+    w.total = w.sched > 0 ? base + w.sched : 0;
   } else {
     const int64_t units = w.bound * nsteps;
     w.q = cdiv(units, P);
@@ -164,6 +231,10 @@ ShrinkWs shrink_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_
 
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_EHIP; }
 
+// Bytes of a plan's partial planes (zero in direct mode), for the internal layouts that place
+// them in a section of their own.
+size_t part_bytes(const ShrinkWs& w) { return w.q > 0 ? w.total - w.part : 0; }
+
 // Workspace of the fused MLP: byte offsets of its six sections (256-byte aligned).
 struct MlpLayout {
   int64_t rp;           // rank rounded up to 32
@@ -173,15 +244,16 @@ struct MlpLayout {
 };
 
 MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
+  const Knobs kn;
   MlpLayout L{};
   L.rp = cdiv(r, 32) * 32;
   // dense mode has no segments: the tile bound is ceil(M / BM)
   // plans for both shrink families (the LDS-staged one needs aligned A pointers, known only
   // at call time); the partials section fits either
-  L.s_gu = shrink_ws(LORA_BF16, M, H, 2, int(L.rp), 0, prefer_lds(M, H, 2, int(L.rp)));
-  L.s_d = shrink_ws(LORA_BF16, M, I, 1, int(L.rp), 0, prefer_lds(M, I, 1, int(L.rp)));
-  L.r_gu = shrink_ws(LORA_BF16, M, H, 2, int(L.rp), 0, false);
-  L.r_d = shrink_ws(LORA_BF16, M, I, 1, int(L.rp), 0, false);
+  L.s_gu = shrink_ws(kn, LORA_BF16, M, H, 2, int(L.rp), 0, prefer_lds(kn, M, H, 2, int(L.rp)), false);
+  L.s_d = shrink_ws(kn, LORA_BF16, M, I, 1, int(L.rp), 0, prefer_lds(kn, M, I, 1, int(L.rp)), false);
+  L.r_gu = shrink_ws(kn, LORA_BF16, M, H, 2, int(L.rp), 0, false, false);
+  L.r_d = shrink_ws(kn, LORA_BF16, M, I, 1, int(L.rp), 0, false, false);
   size_t off = 0;
   L.xa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
   L.lb_gu = off; off += align256(size_t(2 * I) * 2 * L.rp * 2);
@@ -189,8 +261,8 @@ MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   L.xa_d = off; off += align256(size_t(M) * L.rp * 2);
   L.lb_d = off; off += align256(size_t(H) * L.rp * 2);
   L.part = off;
-  off += align256(std::max(std::max(L.s_gu.total - L.s_gu.part, L.s_d.total - L.s_d.part),
-                           std::max(L.r_gu.total - L.r_gu.part, L.r_d.total - L.r_d.part)));
+  off += align256(std::max(std::max(part_bytes(L.s_gu), part_bytes(L.s_d)),
+                           std::max(part_bytes(L.r_gu), part_bytes(L.r_d))));
   L.total = off;
   return L;
 }
@@ -205,16 +277,17 @@ struct LinearLayout {
 };
 
 LinearLayout linear_layout(int64_t M, int64_t K, const int64_t* N, int P, int32_t r) {
+  const Knobs kn;
   LinearLayout L{};
   L.rp = cdiv(r, 32) * 32;
   L.P = P;
-  L.s = shrink_ws(LORA_BF16, M, K, P, int(L.rp), 0, prefer_lds(M, K, P, int(L.rp)));
-  L.r = shrink_ws(LORA_BF16, M, K, P, int(L.rp), 0, false);
+  L.s = shrink_ws(kn, LORA_BF16, M, K, P, int(L.rp), 0, prefer_lds(kn, M, K, P, int(L.rp)), false);
+  L.r = shrink_ws(kn, LORA_BF16, M, K, P, int(L.rp), 0, false, false);
   size_t off = 0;
   L.xa = off; off += align256(size_t(M) * P * L.rp * 2);
   for (int p = 0; p < P; ++p) { L.lb[p] = off; off += align256(size_t(N[p]) * L.rp * 2); }
   L.part = off;
-  off += align256(std::max(L.s.total - L.s.part, L.r.total - L.r.part));
+  off += align256(std::max(part_bytes(L.s), part_bytes(L.r)));
   L.total = off;
   return L;
 }
@@ -255,14 +328,15 @@ lmx::ColJobs mlp_bwd_coljobs(int64_t M, int64_t H, int64_t I, int32_t r) {
 }
 
 MlpBwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
+  const Knobs kn;
   MlpBwdLayout L{};
   L.rp = cdiv(r, 32) * 32;
   const int rp = int(L.rp);
-  L.s_x = shrink_ws(LORA_BF16, M, H, 2, rp, 0, prefer_lds(M, H, 2, rp));
-  L.r_x = shrink_ws(LORA_BF16, M, H, 2, rp, 0, false);
-  L.s_w = shrink_ws(LORA_BF16, M, H, 1, rp, 0, prefer_lds(M, H, 1, rp));
-  L.s_i = shrink_ws(LORA_BF16, M, I, 1, rp, 0, prefer_lds(M, I, 1, rp));
-  L.r_i = shrink_ws(LORA_BF16, M, I, 1, rp, 0, false);
+  L.s_x = shrink_ws(kn, LORA_BF16, M, H, 2, rp, 0, prefer_lds(kn, M, H, 2, rp), false);
+  L.r_x = shrink_ws(kn, LORA_BF16, M, H, 2, rp, 0, false, false);
+  L.s_w = shrink_ws(kn, LORA_BF16, M, H, 1, rp, 0, prefer_lds(kn, M, H, 1, rp), false);
+  L.s_i = shrink_ws(kn, LORA_BF16, M, I, 1, rp, 0, prefer_lds(kn, M, I, 1, rp), false);
+  L.r_i = shrink_ws(kn, LORA_BF16, M, I, 1, rp, 0, false, false);
   L.cj = mlp_bwd_coljobs(M, H, I, r);
   size_t off = 0;
   L.sbdt = off; off += align256(size_t(r) * H * 2);
@@ -277,7 +351,7 @@ MlpBwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   L.hmid = off; off += align256(size_t(M) * I * 2);
   L.dedv = off; off += align256(size_t(M) * 2 * I * 2);
   size_t sp = 0;
-  for (const ShrinkWs* w : {&L.s_x, &L.r_x, &L.s_w, &L.s_i, &L.r_i}) sp = std::max(sp, w->total - w->part);
+  for (const ShrinkWs* w : {&L.s_x, &L.r_x, &L.s_w, &L.s_i, &L.r_i}) sp = std::max(sp, part_bytes(*w));
   L.part = off; off += align256(sp);
   L.colpart = off; off += align256(lmx::colred_partial_floats(L.cj) * 4);
   L.total = off;
@@ -390,6 +464,64 @@ lora_status linear_fused(lora_dtype dtype, int64_t M, int64_t K, const int64_t* 
   return LORA_OK;
 }
 
+// The shrink entry points' shared body. `in_scratch`: the workspace is the library's device
+// scratch array (lora_shrink_noalloc): a plan needing more is refused, and the arrival counters
+// a call uses are cleared first by a small fill kernel (the array keeps the last call's
+// contents).
+lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t L,
+                        int32_t G, const void* x, int64_t ldx, const void* w_a, int64_t lda,
+                        const int32_t* seg_indptr, const int32_t* weight_indices,
+                        const int32_t* permutation, const int32_t* lora_ranks, void* h,
+                        int64_t ldh, const Knobs& kn, void* workspace, size_t workspace_bytes,
+                        void* stream, bool in_scratch) {
+  if (!valid_dtype(dtype)) return LORA_EUNSUPPORTED;
+  if (T < 0 || G < 0 || S < 1 || R < 1) return LORA_EINVAL;
+  if (S > kMaxSlices || R > kMaxRank) return LORA_EUNSUPPORTED;
+  if (T == 0 || G == 0) return LORA_OK;
+  if (K < 1 || L < 1) return LORA_EINVAL;
+  if (T >= INT_MAX || K >= INT_MAX || G >= INT_MAX / 2) return LORA_EUNSUPPORTED;
+  if (!x || !w_a || !seg_indptr || !weight_indices || !lora_ranks || !h)
+    return LORA_EINVAL;
+  if (ldx < K || lda < K || ldh < int64_t(S) * R) return LORA_EINVAL;
+  if (int64_t(S) * R * T * 16 >= int64_t(1) << 62) return LORA_EUNSUPPORTED;
+  const int e = esize(dtype);
+  const bool aligned = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
+  const bool lds = dtype != LORA_F32 && aligned && K % 8 == 0 &&
+                   prefer_lds_pub(kn, int(dtype), T, K, S, R, G);
+  const ShrinkWs ws = shrink_ws(kn, int(dtype), T, K, S, R, G, lds, true);
+  const int variant = ws.variant;
+  const int bm = ws.bm;
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total)) return LORA_EWORKSPACE;
+  if (ws.total > 0 && !al16(workspace)) return LORA_EWORKSPACE;
+  const int64_t bound = ws.bound;
+  if (bound >= INT_MAX) return LORA_EUNSUPPORTED;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(workspace);
+  if (in_scratch && ws.q > 0 && ws.in_launch &&
+      lmx::launch_zero_ints(reinterpret_cast<int*>(wsb), int(bound) * ws.gy, st) != hipSuccess)
+    return LORA_EHIP;
+  lmx::ShrinkArgs a{};
+  a.x = x; a.w_a = w_a; a.seg_indptr = seg_indptr; a.weight_indices = weight_indices;
+  a.permutation = permutation; a.lora_ranks = lora_ranks; a.h = h;
+  a.K = K; a.ldx = ldx; a.lda = lda; a.ldh = ldh; a.S = S; a.R = R; a.G = G; a.T = int(T);
+  if (ws.sched > 0) {
+    int4* tiles = reinterpret_cast<int4*>(wsb + kCounterBytes + 256);
+    int* count = reinterpret_cast<int*>(wsb + kCounterBytes);
+    hipError_t err = lmx::launch_schedule(seg_indptr, weight_indices, G, bm, tiles, count, st);
+    if (err != hipSuccess) return LORA_EHIP;
+    a.tiles = tiles; a.tile_count = count;
+  }
+  a.sk_q = ws.q; a.sk_tiles = int(bound); a.sk_mp = ws.mp; a.sk_unit = ws.unit;
+  if (ws.q > 0) a.part = reinterpret_cast<float*>(wsb + ws.part);
+  if (ws.q > 0 && ws.in_launch) a.counters = reinterpret_cast<int*>(wsb);
+  lmx::ShrinkPlan splan{variant, ws.grid_x, aligned, ws.lds};
+  if (lmx::launch_shrink(int(dtype), a, splan, st) != hipSuccess) return LORA_EHIP;
+  if (ws.q > 0 && !ws.in_launch)
+    return hip_status(lmx::launch_shrink_sk_reduce(int(dtype), a, bm, st));
+  return LORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -408,21 +540,20 @@ const char* lora_status_str(lora_status s) {
 
 const char* lora_version(void) { return "lora_mi355x 0.1 gfx950"; }
 
-void lora_tuning_override(int32_t op, int32_t variant) {
-  if (op == 0) g_shrink_override = (variant >= 0 && variant < lmx::num_shrink_variants()) ? variant : -1;
-  if (op == 1) g_expand_override = (variant >= 0 && variant < lmx::num_expand_variants()) ? variant : -1;
-  if (op == 2) g_expand_bn_override = (variant > 0 && variant <= 65536) ? variant : -1;
-  if (op == 3) g_sk_override = (variant >= 0 && variant <= 65535) ? variant : -1;
-  if (op == 4) g_lds_override = (variant == 0 || variant == 1) ? variant : -1;
+size_t lora_shrink_workspace_size_ex(lora_dtype dtype, int64_t T, int64_t K, int32_t S,
+                                     int32_t R, int32_t G, const lora_plan* plan) {
+  if (T <= 0 || G <= 0 || K <= 0 || S <= 0 || R <= 0 || !valid_dtype(dtype)) return 0;
+  const Knobs kn = knobs_of(plan);
+  if (!knobs_valid(kn)) return 0;
+  // the kernel family depends on pointer alignment, which the query does not see: cover both
+  const size_t reg = shrink_ws(kn, int(dtype), T, K, S, R, G, false, true).total;
+  if (dtype == LORA_F32 || K % 8 != 0 || kn.family == 0) return reg;
+  return std::max(reg, shrink_ws(kn, int(dtype), T, K, S, R, G, true, true).total);
 }
 
 size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
                                   int32_t G) {
-  if (T <= 0 || G <= 0 || K <= 0 || S <= 0 || R <= 0 || !valid_dtype(dtype)) return 0;
-  // the kernel family depends on pointer alignment, which the query does not see: cover both
-  const size_t reg = shrink_ws(int(dtype), T, K, S, R, G, false).total;
-  if (dtype == LORA_F32 || K % 8 != 0 || g_lds_override == 0) return reg;
-  return std::max(reg, shrink_ws(int(dtype), T, K, S, R, G, true).total);
+  return lora_shrink_workspace_size_ex(dtype, T, K, S, R, G, nullptr);
 }
 
 size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t G,
@@ -432,59 +563,39 @@ size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_
   return schedule_bytes(T, G, 16);  // the smallest tile of any expand shape: the longest list
 }
 
+lora_status lora_shrink_ex(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                           int32_t L, int32_t G, const void* x, int64_t ldx, const void* w_a,
+                           int64_t lda, const int32_t* seg_indptr, const int32_t* weight_indices,
+                           const int32_t* permutation, const int32_t* lora_ranks, void* h,
+                           int64_t ldh, const lora_plan* plan, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const Knobs kn = knobs_of(plan);
+  if (!knobs_valid(kn)) return LORA_EINVAL;
+  return shrink_impl(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr, weight_indices,
+                     permutation, lora_ranks, h, ldh, kn, workspace, workspace_bytes, stream,
+                     false);
+}
+
 lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t L,
                         int32_t G, const void* x, int64_t ldx, const void* w_a, int64_t lda,
                         const int32_t* seg_indptr, const int32_t* weight_indices,
                         const int32_t* permutation, const int32_t* lora_ranks, void* h,
                         int64_t ldh, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(dtype)) return LORA_EUNSUPPORTED;
-  if (T < 0 || G < 0 || S < 1 || R < 1) return LORA_EINVAL;
-  if (S > kMaxSlices || R > kMaxRank) return LORA_EUNSUPPORTED;
-  if (T == 0 || G == 0) return LORA_OK;
-  if (K < 1 || L < 1) return LORA_EINVAL;
-  if (T >= INT_MAX || K >= INT_MAX || G >= INT_MAX / 2) return LORA_EUNSUPPORTED;
-  if (!x || !w_a || !seg_indptr || !weight_indices || !lora_ranks || !h)
-    return LORA_EINVAL;
-  if (ldx < K || lda < K || ldh < int64_t(S) * R) return LORA_EINVAL;
-  if (int64_t(S) * R * T * 16 >= int64_t(1) << 62) return LORA_EUNSUPPORTED;
-  const int e = esize(dtype);
-  const bool aligned = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
-  const bool lds = dtype != LORA_F32 && aligned && K % 8 == 0 && prefer_lds(T, K, S, R);
-  const ShrinkWs ws = shrink_ws(int(dtype), T, K, S, R, G, lds);
-  const int variant = ws.variant;
-  const int bm = ws.bm;
-  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total)) return LORA_EWORKSPACE;
-  if (ws.q > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return LORA_EWORKSPACE;
-  const int64_t bound = ws.bound;
-  if (bound >= INT_MAX) return LORA_EUNSUPPORTED;
-
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  lmx::ShrinkArgs a{};
-  a.x = x; a.w_a = w_a; a.seg_indptr = seg_indptr; a.weight_indices = weight_indices;
-  a.permutation = permutation; a.lora_ranks = lora_ranks; a.h = h;
-  a.K = K; a.ldx = ldx; a.lda = lda; a.ldh = ldh; a.S = S; a.R = R; a.G = G; a.T = int(T);
-  if (ws.sched > 0) {
-    int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + 256);
-    int* count = static_cast<int*>(workspace);
-    hipError_t e = lmx::launch_schedule(seg_indptr, weight_indices, G, bm, tiles, count, st);
-    if (e != hipSuccess) return LORA_EHIP;
-    a.tiles = tiles; a.tile_count = count;
-  }
-  a.sk_q = ws.q; a.sk_tiles = int(bound); a.sk_mp = ws.mp; a.sk_unit = ws.unit;
-  if (ws.q > 0) a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part);
-  lmx::ShrinkPlan plan{variant, ws.grid_x, aligned, ws.lds};
-  if (lmx::launch_shrink(int(dtype), a, plan, st) != hipSuccess) return LORA_EHIP;
-  if (ws.q > 0) return hip_status(lmx::launch_shrink_sk_reduce(int(dtype), a, bm, st));
-  return LORA_OK;
+  return lora_shrink_ex(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr, weight_indices,
+                        permutation, lora_ranks, h, ldh, nullptr, workspace, workspace_bytes,
+                        stream);
 }
 
-lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t L, int32_t G,
-                        int64_t N, const void* h, int64_t ldh, const void* w_b, int64_t ldb,
-                        const int32_t* slice_offsets, const int32_t* seg_indptr,
-                        const int32_t* weight_indices, const int32_t* permutation,
-                        const int32_t* lora_ranks, const float* scalings, void* y, int64_t ldy,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+lora_status lora_expand_ex(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t L,
+                           int32_t G, int64_t N, const void* h, int64_t ldh, const void* w_b,
+                           int64_t ldb, const int32_t* slice_offsets, const int32_t* seg_indptr,
+                           const int32_t* weight_indices, const int32_t* permutation,
+                           const int32_t* lora_ranks, const float* scalings, void* y,
+                           int64_t ldy, const lora_plan* plan, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (!valid_dtype(dtype)) return LORA_EUNSUPPORTED;
+  const Knobs kn = knobs_of(plan);
+  if (!knobs_valid(kn)) return LORA_EINVAL;
   if (T < 0 || G < 0 || S < 1 || R < 1 || N < 0) return LORA_EINVAL;
   if (S > kMaxSlices || R > kMaxRank) return LORA_EUNSUPPORTED;
   if (T == 0 || G == 0 || N == 0) return LORA_OK;
@@ -499,11 +610,11 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
   const bool aligned_b = al16(h) && al16(w_b) && (ldh * e) % 16 == 0 && (ldb * e) % 16 == 0 &&
                          (int64_t(R) * e) % 16 == 0;
   const bool aligned_y = al16(y) && (ldy * e) % 16 == 0;
-  const int variant = expand_variant(T, dtype != LORA_F32 && R == 16 && aligned_b && aligned_y);
+  const int variant = expand_variant(kn, T, dtype != LORA_F32 && R == 16 && aligned_b && aligned_y);
   const int bm = lmx::expand_plan_bm(int(dtype), variant);
   const bool shared = dtype != LORA_F32 && (variant == lmx::kExpandSharedD1 ||
                                             variant == lmx::kExpandSharedD2);
-  const int bn = expand_bn(T, G, N, bm, lmx::expand_plan_waves(int(dtype), variant),
+  const int bn = expand_bn(kn, T, G, N, bm, lmx::expand_plan_waves(int(dtype), variant),
                            lmx::expand_plan_chunk(int(dtype), variant), shared);
   if (cdiv(N, bn) + S > 65535) return LORA_EUNSUPPORTED;
   const size_t need = schedule_bytes(T, G, bm);
@@ -520,12 +631,23 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
   if (need > 0) {
     int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + 256);
     int* count = static_cast<int*>(workspace);
-    hipError_t e = lmx::launch_schedule(seg_indptr, weight_indices, G, bm, tiles, count, st);
-    if (e != hipSuccess) return LORA_EHIP;
+    hipError_t err = lmx::launch_schedule(seg_indptr, weight_indices, G, bm, tiles, count, st);
+    if (err != hipSuccess) return LORA_EHIP;
     a.tiles = tiles; a.tile_count = count;
   }
-  lmx::ExpandPlan plan{variant, int(bound), aligned_b, aligned_y};
-  return hip_status(lmx::launch_expand(int(dtype), a, plan, st));
+  lmx::ExpandPlan eplan{variant, int(bound), aligned_b, aligned_y};
+  return hip_status(lmx::launch_expand(int(dtype), a, eplan, st));
+}
+
+lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t L, int32_t G,
+                        int64_t N, const void* h, int64_t ldh, const void* w_b, int64_t ldb,
+                        const int32_t* slice_offsets, const int32_t* seg_indptr,
+                        const int32_t* weight_indices, const int32_t* permutation,
+                        const int32_t* lora_ranks, const float* scalings, void* y, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return lora_expand_ex(dtype, T, S, R, L, G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
+                        weight_indices, permutation, lora_ranks, scalings, y, ldy, nullptr,
+                        workspace, workspace_bytes, stream);
 }
 
 size_t lora_mlp_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r) {

@@ -109,6 +109,17 @@ hipError_t launch_zero_int(int* p, hipStream_t st) {
   return hipGetLastError();
 }
 
+__global__ void zero_ints_kernel(int* p, int n) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_ints(int* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_export_tiles(int method, const int* seg_indptr, const int* weight_indices,
                                const int* lora_ranks, int G, int BM, int bound, int* out,
                                int* count, int4* ws_tiles, int* ws_count, hipStream_t st) {

@@ -54,6 +54,87 @@ __device__ __forceinline__ Tile shrink_tile(const ShrinkArgs& p, int BM, int t, 
   return tile;
 }
 
+// Planes of tile t in a shared-work shrink: its (tile, step) units [t * nunits, (t+1) * nunits)
+// fall into the ranges of workgroups first .. last, with first = t * nunits / q; plane j holds
+// the piece of workgroup first + j.
+__device__ __forceinline__ int sk_pieces(int t, int64_t nunits, int64_t q) {
+  const int64_t first = (int64_t(t) * nunits) / q;
+  const int64_t last = ((int64_t(t) + 1) * nunits - 1) / q;
+  return int(last - first + 1);
+}
+
+// Partial sums of a shared-work shrink cross workgroups, and so compute units and XCDs. They are
+// written and read as device-scope relaxed atomics (stores that write through the L2 to the
+// device coherence point; loads that do not hit a stale cached copy), so no whole-cache
+// write-back or invalidation fence is needed: a store is visible device-wide once it has
+// completed (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void part_store(float* q, float v) {
+  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float part_load(const float* q) {
+  return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Completion of a shared-work shrink inside its own launch (p.counters non-null), called by
+// every thread of the workgroup right after its piece of tile t went to plane j (fp32 sums of
+// the rank columns of this grid row's CBY column blocks). Each workgroup waits until its
+// partial stores have completed, then counts its piece in on the arrival counter of
+// (tile, grid row); the workgroup that arrives last adds the np planes in plane order, whatever
+// the order of arrival (so the result does not depend on timing), rounds once, writes h with
+// exact zeros in the rank padding, and sets the counter back to zero, so every counter is zero
+// again when the launch ends. A rank-0 tile stores no pieces: its plane-0 workgroup writes its
+// zero rows.
+template <int DT, int NT>
+__device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, int np, int CBY,
+                          int* s_last) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  const int NB = (p.R + 15) >> 4;
+  const int nblk = p.S * NB;
+  const int SR = p.S * p.R;
+  if (tile.r > 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+    __syncthreads();                // ... and every other thread's
+    if (threadIdx.x == 0) {
+      int* ctr = p.counters + int64_t(t) * gridDim.y + blockIdx.y;
+      const int before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = before == np - 1;
+      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = last;
+    }
+    __syncthreads();
+    if (!*s_last) return;  // uniform over the workgroup
+  } else if (j != 0) {
+    return;
+  }
+  const int b0 = int(blockIdx.y) * CBY;
+  const int nb = min(CBY, nblk - b0);
+  const int W = nb * 16;
+  const int n = tile.mlen * W;
+  const int64_t plane = int64_t(p.T) * SR;
+  for (int e = int(threadIdx.x); e < n; e += NT) {
+    const int m = e / W, rem = e - (e / W) * W;
+    const int blk = b0 + (rem >> 4);
+    const int s = blk / NB, c = 16 * (blk - (blk / NB) * NB) + (rem & 15);
+    if (c >= p.R) continue;
+    S v = S(0);
+    if (c < tile.r) {
+      const float* src = p.part + int64_t(tile.m0 + m) * SR + s * p.R + c;
+      float acc = 0.f;
+      for (int q0 = 0; q0 < np; q0 += 8) {
+        float b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = (q0 + i < np) ? part_load(src + (q0 + i) * plane) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (q0 + i < np) acc = (q0 + i == 0) ? b[i] : acc + b[i];
+      }
+      v = Tr::from_f32(acc);
+    }
+    reinterpret_cast<S*>(p.h)[int64_t(tile.m0 + m) * p.ldh + s * p.R + c] = v;
+  }
+}
+
 // One piece of shrink work: reduction steps [k0, k1) of `tile` for the column blocks of this
 // workgroup (grid y). Returns, in `out`, the workgroup's fp32 sums in MFMA layout for the
 // (column block, token group) pairs idx = w, w + NW, ... that this wave finalises.
@@ -216,8 +297,9 @@ __device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& ti
 // Stream-K mode: the flattened work [0, tiles bound * steps) is cut into equal ranges of sk_q
 // steps, one per workgroup x, so every compute unit streams the same amount whatever the
 // segment lengths; each tile piece of a range is written as fp32 partial sums to plane
-// j = workgroup - first workgroup of the tile, rows = the tile's sorted positions, and
-// shrink_sk_reduce_kernel adds the planes in order.
+// j = workgroup - first workgroup of the tile, rows = the tile's sorted positions, and the
+// planes are added in order by the tile's last workgroup (sk_finish, with arrival counters) or
+// by shrink_sk_reduce_kernel in a second launch.
 template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL>
 __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
   using Tr = Traits<DT>;
@@ -228,6 +310,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
 
   __shared__ Tile s_tile;
   __shared__ int s_scan[NW];
+  __shared__ int s_last;
   __shared__ f32x4_t s_red[(NW > 1) ? NW : 1][CB * MT][64];
 
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -252,7 +335,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int c = 16 * b + 4 * lg + v;
-          if (c < tile.r) prow[c] = sums[n][v];
+          if (c < tile.r) part_store(prow + c, sums[n][v]);
         }
       } else {
         S* hrow = reinterpret_cast<S*>(p.h) + int64_t(tile.m0 + m) * p.ldh + s * p.R;
@@ -290,6 +373,8 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
       shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, k0, k1, s_red, sums);
       store(tile, sums, slot);
     }
+    if (p.counters != nullptr)
+      sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nsteps, p.sk_q), CB, &s_last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }

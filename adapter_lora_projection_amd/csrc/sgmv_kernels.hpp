@@ -31,6 +31,10 @@ struct ShrinkArgs {
   int sk_tiles, sk_mp;
   int sk_unit;  // reduction indices per unit of work (the kernel's step)
   float* part;
+  // Non-null in stream-K mode: arrival counters [tiles bound][grid rows], zero on entry and on
+  // exit; the last workgroup to store a piece of a tile adds the tile's planes into h in the
+  // same launch (no launch_shrink_sk_reduce).
+  int* counters;
 };
 
 struct ExpandArgs {
@@ -89,6 +93,8 @@ hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan,
 hipError_t launch_schedule(const int* seg_indptr, const int* weight_indices, int G, int BM,
                            int4* tiles, int* count, hipStream_t st);
 hipError_t launch_zero_int(int* p, hipStream_t st);
+// Clears n ints with a fill kernel (no memset node when captured in a graph).
+hipError_t launch_zero_ints(int* p, int n, hipStream_t st);
 hipError_t launch_export_tiles(int method, const int* seg_indptr, const int* weight_indices,
                                const int* lora_ranks, int G, int BM, int bound, int* out,
                                int* count, int4* ws_tiles, int* ws_count, hipStream_t st);

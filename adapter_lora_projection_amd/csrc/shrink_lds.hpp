@@ -16,8 +16,8 @@
 // Requires 16-byte aligned x and A rows and K a multiple of 8 (the host checks).
 //
 // Work split: direct (sk_q == 0, one workgroup per tile over all of K) or shared (the
-// (tile, stage) work cut into ranges of sk_q stages per workgroup, partial planes reduced by
-// shrink_sk_reduce_kernel), as for the register-ring shrink.
+// (tile, stage) work cut into ranges of sk_q stages per workgroup, partial planes added by the
+// tile's last workgroup or by shrink_sk_reduce_kernel), as for the register-ring shrink.
 //
 // The stage's 1 KiB load instructions are dealt round-robin to the waves with no padding, so
 // waves may differ by one instruction; each waits with the immediate for its own count.
@@ -47,6 +47,7 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
   __shared__ __align__(16) S lds[NS][ROWS * KB];
   __shared__ Tile s_tile;
   __shared__ int s_scan[NW];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63, w = wave_id();
   const int li = lane & 15, lg = lane >> 4;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int c = 16 * b + 4 * lg + v;
-            if (c < tile.r) prow[c] = acc[g][cb][v];
+            if (c < tile.r) part_store(prow + c, acc[g][cb][v]);
           }
         } else {
           S* hrow = reinterpret_cast<S*>(p.h) + int64_t(tile.m0 + m) * p.ldh + s * p.R;
@@ -200,6 +201,8 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
     const int j = int(blockIdx.x) - int((int64_t(t) * nunits) / p.sk_q);
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
     if (tile.r > 0) piece(tile, k0, k1, slot);
+    if (p.counters != nullptr)
+      sk_finish<DT, 256>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, &s_last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }

@@ -51,16 +51,39 @@ def _stream() -> int:
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A fresh SGMV workspace: zero-filled, as the shrink's arrival counters require."""
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def _given_workspace(ws: torch.Tensor, nbytes: int, device) -> torch.Tensor:
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous() or ws.device != device:
+        raise ValueError("workspace must be a contiguous uint8 vector on the device of the operands")
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace must hold at least {nbytes} bytes")
+    return ws
+
+
+def _out(t: torch.Tensor, shape, dtype, device, name: str) -> None:
+    """Checks a caller-provided output: shape, dtype and device (rows may be strided)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {device}")
+
+
+def _bf16_in(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bf16 (this operation is bf16 only)")
 
 
 def shrink(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, S: int, R: int,
-           h: torch.Tensor | None = None) -> torch.Tensor:
+           h: torch.Tensor | None = None, plan: _lib.Plan | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
     """h = x[perm] A_a^T per segment (``lora_shrink``). x: [T][K] (row stride >= K),
-    w_a: [L][S*R][K]; returns h [T][S*R] in sorted order. permutation=None: identity."""
-    _dev(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, h)
+    w_a: [L][S*R][K]; returns h [T][S*R] in sorted order. permutation=None: identity.
+    plan: explicit kernel shape (``lora_shrink_ex``). workspace: a reusable uint8 buffer of at
+    least the queried size whose first 32 KiB are zero (a fresh zeroed one otherwise)."""
+    _dev(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, h, workspace)
     T, K = x.shape
     ldx = _rows(x, "x")
     rows, lda = _stacked(w_a, "w_a")
@@ -72,23 +95,27 @@ def shrink(x, w_a, seg_indptr, weight_indices, permutation, lora_ranks, S: int, 
     if permutation is not None:  # None: identity (tokens already grouped by segment)
         _meta(permutation, T, "permutation")
     _meta(lora_ranks, w_a.shape[0], "lora_ranks")
+    dt = dtype_code(x)
+    if w_a.dtype != x.dtype:
+        raise TypeError("x and w_a must share a dtype")
     if h is None:
         h = torch.empty((T, S * R), dtype=x.dtype, device=x.device)
+    else:
+        _out(h, (T, S * R), x.dtype, x.device, "h")
     ldh = _rows(h, "h")
-    dt = dtype_code(x)
-    if w_a.dtype != x.dtype or h.dtype != x.dtype:
-        raise TypeError("x, w_a and h must share a dtype")
-    nbytes = _lib.lora_shrink_workspace_size(dt, T, K, S, R, G)
-    ws = _workspace(nbytes, x.device)
-    _lib.lora_shrink(dt, T, K, S, R, w_a.shape[0], G, x, ldx, w_a, lda, seg_indptr, weight_indices,
-                     permutation, lora_ranks, h, ldh, ws, nbytes, _stream())
+    nbytes = _lib.lora_shrink_workspace_size_ex(dt, T, K, S, R, G, plan)
+    ws = _workspace(nbytes, x.device) if workspace is None else _given_workspace(workspace, nbytes, x.device)
+    _lib.lora_shrink_ex(dt, T, K, S, R, w_a.shape[0], G, x, ldx, w_a, lda, seg_indptr,
+                        weight_indices, permutation, lora_ranks, h, ldh, plan, ws,
+                        0 if ws is None else ws.numel(), _stream())
     return h
 
 
 def expand(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks, scalings,
-           y, S: int, R: int) -> torch.Tensor:
+           y, S: int, R: int, plan: _lib.Plan | None = None) -> torch.Tensor:
     """y[perm[i], slice] += scale_a * h B_a^T in place (``lora_expand``). h: [T][S*R] sorted
-    order, w_b: [L][N][R], y: [T][>=N] token order. Returns y. permutation=None: identity."""
+    order, w_b: [L][N][R], y: [T][>=N] token order. Returns y. permutation=None: identity.
+    plan: explicit kernel shape (``lora_expand_ex``)."""
     _dev(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks, scalings, y)
     T = h.shape[0]
     ldh = _rows(h, "h")
@@ -110,10 +137,13 @@ def expand(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_
     dt = dtype_code(y)
     if h.dtype != y.dtype or w_b.dtype != y.dtype:
         raise TypeError("h, w_b and y must share a dtype")
+    if h.shape[1] != S * R:
+        raise ValueError("h must be [T][S*R]")
     nbytes = _lib.lora_expand_workspace_size(dt, T, S, R, G, N)
     ws = _workspace(nbytes, y.device)
-    _lib.lora_expand(dt, T, S, R, w_b.shape[0], G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
-                     weight_indices, permutation, lora_ranks, scalings, y, ldy, ws, nbytes, _stream())
+    _lib.lora_expand_ex(dt, T, S, R, w_b.shape[0], G, N, h, ldh, w_b, ldb, slice_offsets,
+                        seg_indptr, weight_indices, permutation, lora_ranks, scalings, y, ldy, plan,
+                        ws, nbytes, _stream())
     return y
 
 
@@ -146,9 +176,12 @@ def mlp_fused(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down, b_dow
                            (b_gate, (I, r), "b_gate"), (b_up, (I, r), "b_up"), (b_down, (H, r), "b_down")):
         if tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != torch.bfloat16:
             raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")
+    _bf16_in(x, "x")
     ldx = _rows(x, "x")
     if out is None:
         out = torch.empty((M, H), dtype=x.dtype, device=x.device)
+    else:
+        _out(out, (M, H), torch.bfloat16, x.device, "out")
     ldo = _rows(out, "out")
     nbytes = _lib.lora_mlp_workspace_size(_lib.LORA_BF16, M, H, I, r)
     if workspace is None or workspace.numel() < nbytes:
@@ -174,6 +207,7 @@ def mlp_fused_train(x, w_gate, w_up, w_down, a_gate, b_gate, a_up, b_up, a_down,
                            (a_gate, (r, H), "a_gate"), (a_up, (r, H), "a_up"), (a_down, (r, I), "a_down"),
                            (b_gate, (I, r), "b_gate"), (b_up, (I, r), "b_up"), (b_down, (H, r), "b_down")):
         _bf16_mat(t, shape, name)
+    _bf16_in(x, "x")
     out = torch.empty((M, H), dtype=x.dtype, device=x.device)
     e = torch.empty((M, I), dtype=x.dtype, device=x.device)
     v = torch.empty((M, I), dtype=x.dtype, device=x.device)
@@ -216,6 +250,7 @@ def mlp_backward(x, e, v, dout, w_gu_t, w_down_t, a_gate, b_gate, a_up, b_up, a_
                            (b_gate, (I, r), "b_gate"), (b_up, (I, r), "b_up"), (b_down, (H, r), "b_down"),
                            (e, (M, I), "e"), (v, (M, I), "v"), (dout, (M, H), "dout")):
         _bf16_mat(t, shape, name)
+    _bf16_in(x, "x")
     dev, bf = x.device, torch.bfloat16
     g = {"dx": torch.empty((M, H), dtype=bf, device=dev),
          "da_gate": torch.empty((r, H), dtype=bf, device=dev),
@@ -282,9 +317,12 @@ def linear_fused(x, w, a, b, scale: float, out: torch.Tensor | None = None,
     N, r = w.shape[0], a.shape[0]
     for t, shape, name in ((w, (N, K), "w"), (a, (r, K), "a"), (b, (N, r), "b")):
         _bf16_mat(t, shape, name)
+    _bf16_in(x, "x")
     ldx = _rows(x, "x")
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _out(out, (M, N), torch.bfloat16, x.device, "out")
     nbytes = _lib.lora_linear_workspace_size(_lib.LORA_BF16, M, K, N, r)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
@@ -303,6 +341,7 @@ def qkv_fused(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, scale: float,
                            (a_q, (r, K), "a_q"), (a_k, (r, K), "a_k"), (a_v, (r, K), "a_v"),
                            (b_q, (Nq, r), "b_q"), (b_k, (Nkv, r), "b_k"), (b_v, (Nkv, r), "b_v")):
         _bf16_mat(t, shape, name)
+    _bf16_in(x, "x")
     ldx = _rows(x, "x")
     q = torch.empty((M, Nq), dtype=x.dtype, device=x.device)
     k = torch.empty((M, Nkv), dtype=x.dtype, device=x.device)
@@ -334,11 +373,11 @@ def embedding_a(input_ids, w_a, seg_indptr, weight_indices, permutation, lora_ra
     if permutation is not None:
         _meta(permutation, T, "permutation")
     _meta(lora_ranks, L, "lora_ranks")
+    dt = dtype_code(w_a)
     if h is None:
         h = torch.empty((T, R), dtype=w_a.dtype, device=w_a.device)
-    dt = dtype_code(w_a)
-    if h.dtype != w_a.dtype:
-        raise TypeError("w_a and h must share a dtype")
+    else:
+        _out(h, (T, R), w_a.dtype, w_a.device, "h")
     sl, sr, sv = w_a.stride()
     _lib.lora_embedding_a(dt, T, V, R, L, G, input_ids, w_a, sl, sr, sv, seg_indptr,
                           weight_indices, permutation, lora_ranks, h, _rows(h, "h"), _stream())
@@ -364,3 +403,37 @@ def check_metadata(seg_indptr, weight_indices, lora_ranks, R: int, T: int, permu
     ws = torch.empty(nbytes, dtype=torch.uint8, device=seg_indptr.device)
     return _lib.lora_check_metadata(T, G, lora_ranks.numel(), R, S, N, seg_indptr, weight_indices,
                                     permutation, lora_ranks, slice_offsets, ws, nbytes, _stream())
+
+
+def fast_path_ineligibility(dropout: float, active_adapters: int, base_bias=None,
+                            merged: bool = False) -> str | None:
+    """Why the single-adapter fused LoRA path (mlp_fused, mlp_fused_train / mlp_backward,
+    linear_fused, qkv_fused) does not apply to a layer, or None when it does. A pure check of the
+    conditions of "Add optional fast lora path for qwen2/qwen3 on npu" (Compatibility checks):
+    LoRA dropout 0, exactly one active adapter, no base-layer bias, and adapter weights not merged
+    into the base weights. Reading: the fused kernels add no bias term at all, so a bias of any
+    kind (trainable or frozen) makes the layer ineligible, which covers the page's "no trainable
+    bias". Does no arithmetic; a caller that is told no runs its own composition."""
+    if not float(dropout) == 0.0:
+        return f"LoRA dropout is {dropout}, the fused path needs 0"
+    if int(active_adapters) != 1:
+        return f"{active_adapters} active adapters, the fused path takes exactly one"
+    if base_bias is not None:
+        return "the base layer has a bias, the fused path adds none"
+    if merged:
+        return "the adapter is merged into the base weights"
+    return None
+
+
+def fast_path_eligible(dropout: float, active_adapters: int, base_bias=None,
+                       merged: bool = False) -> bool:
+    """True when every fast-path condition holds (see fast_path_ineligibility)."""
+    return fast_path_ineligibility(dropout, active_adapters, base_bias, merged) is None
+
+
+def require_fast_path(dropout: float, active_adapters: int, base_bias=None,
+                      merged: bool = False) -> None:
+    """Raises ValueError naming the first fast-path condition that fails."""
+    why = fast_path_ineligibility(dropout, active_adapters, base_bias, merged)
+    if why is not None:
+        raise ValueError(f"fused LoRA path not applicable: {why}")

@@ -83,15 +83,17 @@ class SgmvCaseRun:
         self.y = d["y_in"].clone()
         ws_s = lib.lora_shrink_workspace_size(dt, c.T, c.K, c.S, c.R, c.G)
         ws_e = lib.lora_expand_workspace_size(dt, c.T, c.S, c.R, c.G, c.N)
-        self.ws = torch.empty(max(ws_s, ws_e, 1), dtype=torch.uint8, device=dev)
+        # the shrink workspace starts with arrival counters that must be zero before first use
+        self.ws_s = torch.zeros(max(ws_s, 1), dtype=torch.uint8, device=dev)
+        self.ws_e = torch.empty(max(ws_e, 1), dtype=torch.uint8, device=dev)
         p = lambda t: t.data_ptr()
         self.shrink_args = (dt, c.T, c.K, c.S, c.R, c.L, c.G, p(d["x"]), c.K, p(d["A"]), c.K,
                             p(d["seg_indptr"]), p(d["weight_indices"]), p(d["permutation"]),
-                            p(d["lora_ranks"]), p(self.h), c.S * c.R, p(self.ws), ws_s, stream)
+                            p(d["lora_ranks"]), p(self.h), c.S * c.R, p(self.ws_s), ws_s, stream)
         self.expand_args = (dt, c.T, c.S, c.R, c.L, c.G, c.N, p(self.h), c.S * c.R, p(d["B"]), c.R,
                             p(d["slice_offsets"]), p(d["seg_indptr"]), p(d["weight_indices"]),
                             p(d["permutation"]), p(d["lora_ranks"]), p(d["scalings"]), p(self.y),
-                            c.N, p(self.ws), ws_e, stream)
+                            c.N, p(self.ws_e), ws_e, stream)
         self.alg = algorithmic(c)
 
     def shrink(self, L):
@@ -476,6 +478,24 @@ def main() -> int:
             acc[i, 1] += ev[i][1].elapsed_time(ev[i][2])
     acc /= reps  # ms
     dom_i, dom_op = np.unravel_index(np.argmax(acc), acc.shape)
+
+    # cold single calls: a 512 MiB device write before each of `cold_reps` repetitions evicts
+    # the L2 and the Infinity Cache; the median of the event timings per call
+    cold_reps = 30
+    flush = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+    cold = np.zeros((len(runs), 2, cold_reps))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i, r in enumerate(runs):
+        for k in range(cold_reps):
+            for op in (0, 1):
+                flush.fill_(float(k))
+                e0.record()
+                r.shrink(L) if op == 0 else r.expand(L)
+                e1.record()
+                torch.cuda.synchronize()
+                cold[i, op, k] = e0.elapsed_time(e1)
+    del flush
+    cold_us = np.median(cold, axis=2) * 1e3
     print(f"[bench] breakdown done; dominant kernel: {'shrink' if dom_op == 0 else 'expand'} "
           f"tok={runs[dom_i].c.T}", file=sys.stderr, flush=True)
 
@@ -545,10 +565,14 @@ def main() -> int:
     for i, r in enumerate(runs):
         b = r.alg["shrink_bytes"] + r.alg["expand_bytes"]
         us = (acc[i, 0] + acc[i, 1]) * 1e3
+        cus = cold_us[i, 0] + cold_us[i, 1]
         per_case.append({"tok": r.c.T, "shrink_us": round(acc[i, 0] * 1e3, 2),
                          "expand_us": round(acc[i, 1] * 1e3, 2),
                          "pair_gbps": round(b / (us * 1e-6) / 1e9, 1),
-                         "pair_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+                         "pair_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "cold_shrink_us": round(float(cold_us[i, 0]), 2),
+                         "cold_expand_us": round(float(cold_us[i, 1]), 2),
+                         "cold_pair_gbps": round(b / (cus * 1e-6) / 1e9, 1)})
     mean_case = float(np.mean([p["pair_gbps"] for p in per_case]))
 
     traffic_table = load_traffic()
@@ -574,6 +598,9 @@ def main() -> int:
                    "timing": "graph replay" if graph is not None else "eager",
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
                    "mean_case_gbps": round(mean_case, 1),
+                   "per_case_timing": "shrink_us / expand_us: eager events, 5 back-to-back sweeps; "
+                                      "cold_*: median of 30 single calls each after a 512 MiB "
+                                      "device write",
                    "per_case": per_case},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),

@@ -97,11 +97,18 @@ const char* lora_version(void);
  *   h              device [T][ldh], ldh >= S*R; row i is sorted position i. Columns >= S*R are
  *                  not written.
  *   workspace      device scratch of at least lora_shrink_workspace_size(...) bytes, 16-byte
- *                  aligned; may be NULL when that size is 0. It holds the segment schedule for
- *                  many segments and the fp32 partial sums of the split reduction: the
- *                  (tile, K step) work is shared out evenly over about one workgroup per compute
- *                  unit, and a second launch adds each tile's pieces in a fixed order. Not read
- *                  before written; contents undefined afterwards.
+ *                  aligned; may be NULL when that size is 0. When the size is nonzero its first
+ *                  32 KiB are arrival counters that MUST hold zeros before the first call that
+ *                  uses the workspace (zero it once, e.g. with hipMemset, when allocating it);
+ *                  every call leaves them zero again, so a workspace can be reused across calls
+ *                  and in captured graphs with no clearing. The rest holds the segment schedule
+ *                  for many segments and the fp32 partial sums of the split reduction: when one
+ *                  workgroup per tile would leave compute units idle, the (tile, K step) work is
+ *                  shared out evenly over about one workgroup per compute unit, and the last
+ *                  workgroup to finish a piece of a tile adds the tile's pieces in a fixed order
+ *                  (results do not depend on timing). Calls that overlap in time (different
+ *                  streams) must not share a workspace. Its other contents are undefined after
+ *                  the call.
  */
 lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t L,
                         int32_t G, const void* x, int64_t ldx, const void* w_a, int64_t lda,
@@ -111,6 +118,50 @@ lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
 
 size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
                                   int32_t G);
+
+/*
+ * lora_plan -- an explicit choice of kernel shape for lora_shrink_ex / lora_expand_ex, for
+ * measurement sweeps and for tests that reach every shape. Every field -1 (or a NULL plan) is
+ * the library's own choice, which is what lora_shrink / lora_expand make. A plan is an input of
+ * the one call: the library keeps no state between calls. Results are identical for every plan
+ * up to the fp32 summation order. A field outside its range makes the call return LORA_EINVAL
+ * (and the workspace query 0).
+ *   shrink_kernel   0 operands loaded straight into registers; 1 staged through LDS (taken only
+ *                   for 16-bit types with 16-byte aligned x and A rows and K % 8 == 0, else 0).
+ *   shrink_shape    shape of the chosen kernel: 0 .. LORA_SHRINK_RING_SHAPES - 1 (kernel 0) or
+ *                   0 .. LORA_SHRINK_LDS_SHAPES - 1 (kernel 1).
+ *   shrink_split    0: one workgroup per tile over all of K; n in 1 .. 65535: n workgroups share
+ *                   the (tile, K step) work evenly.
+ *   shrink_finish   with a split: 1 the last workgroup of each tile adds the pieces in the same
+ *                   launch (arrival counters in the workspace); 0 a second launch adds them.
+ *   expand_shape    0 .. LORA_EXPAND_SHAPES - 1; shapes 8 and 9 need 16-bit types, padded rank
+ *                   16 and 16-byte aligned h, B and y rows (otherwise shape 6 runs).
+ *   expand_block_n  columns per expand workgroup, 1 .. 65536 (rounded up to the shape's unit).
+ */
+typedef struct lora_plan {
+  int32_t shrink_kernel;
+  int32_t shrink_shape;
+  int32_t shrink_split;
+  int32_t shrink_finish;
+  int32_t expand_shape;
+  int32_t expand_block_n;
+} lora_plan;
+
+#define LORA_SHRINK_RING_SHAPES 5
+#define LORA_SHRINK_LDS_SHAPES 5
+#define LORA_EXPAND_SHAPES 10
+
+/* lora_shrink with an explicit plan (NULL: as lora_shrink); the workspace query must be made
+ * with the same plan. */
+lora_status lora_shrink_ex(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                           int32_t L, int32_t G, const void* x, int64_t ldx, const void* w_a,
+                           int64_t lda, const int32_t* seg_indptr, const int32_t* weight_indices,
+                           const int32_t* permutation, const int32_t* lora_ranks, void* h,
+                           int64_t ldh, const lora_plan* plan, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+size_t lora_shrink_workspace_size_ex(lora_dtype dtype, int64_t T, int64_t K, int32_t S,
+                                     int32_t R, int32_t G, const lora_plan* plan);
 
 /*
  * lora_expand -- y[perm[i]][slice s] += scale_a * h_i,s * B_a^T (scaled scatter-add).
@@ -134,7 +185,9 @@ size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_
  *   slice_offsets  device int32 [S+1]: 0 <= slice_offsets[0] <= ... <= slice_offsets[S] = N.
  *   scalings       device float32 [L] (alpha / rank of each adapter).
  *   y              device [T][ldy] read and written in place, ldy >= N; row t is token t.
- *   workspace      as for lora_shrink, sized by lora_expand_workspace_size.
+ *   workspace      device scratch of lora_expand_workspace_size(...) bytes (the segment
+ *                  schedule for many segments; nonzero only then), 16-byte aligned; not read
+ *                  before written.
  */
 lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t L, int32_t G,
                         int64_t N, const void* h, int64_t ldh, const void* w_b, int64_t ldb,
@@ -145,6 +198,16 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
 
 size_t lora_expand_workspace_size(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t G,
                                   int64_t N);
+
+/* lora_expand with an explicit plan (NULL: as lora_expand); lora_expand_workspace_size covers
+ * every plan. */
+lora_status lora_expand_ex(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32_t L,
+                           int32_t G, int64_t N, const void* h, int64_t ldh, const void* w_b,
+                           int64_t ldb, const int32_t* slice_offsets, const int32_t* seg_indptr,
+                           const int32_t* weight_indices, const int32_t* permutation,
+                           const int32_t* lora_ranks, const float* scalings, void* y,
+                           int64_t ldy, const lora_plan* plan, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * lora_mlp_fused -- single-adapter LoRA MLP with fused SwiGLU (bf16).
@@ -381,21 +444,6 @@ lora_status lora_schedule_tiles(int64_t T, int32_t G, int32_t BM, int32_t method
                                 const int32_t* lora_ranks, int32_t* tiles, int64_t max_tiles,
                                 int32_t* count, void* workspace, size_t workspace_bytes,
                                 void* stream);
-
-/*
- * lora_tuning_override -- pins a choice the library makes for an operation, for measurement
- * sweeps:
- *   op 0  shrink kernel shape (0..4, of whichever shrink kernel runs);
- *   op 1  expand kernel shape (0..4);
- *   op 2  expand columns per workgroup (rounded up to the kernel's chunk multiple);
- *   op 3  shrink workgroups sharing the (tile, K step) work (1..65535), or 0 for one workgroup
- *         per tile over all of K with no second launch; the workspace query follows it;
- *   op 4  shrink kernel: 0 = operands loaded straight into registers, 1 = LDS-staged where the
- *         rows are 16-byte aligned and K % 8 == 0.
- * -1 or any other value restores the automatic choice. Process-wide, not thread-safe; results
- * are identical for every choice up to fp32 summation order.
- */
-void lora_tuning_override(int32_t op, int32_t variant);
 
 #ifdef __cplusplus
 }

@@ -7,17 +7,21 @@ Tolerances (stated by the workload definition and restated here):
   conditioned on (sum of |terms|, plus |y_in| for expand), computed by the oracle on absolute
   values; this equals 1e-5 * |oracle| when nothing cancels.
 * bf16 gradients of the MLP backward (sums whose terms carry bf16-stored factors, such as
-  dA = dxa^T x over 4096 tokens): |gpu - ref| <= 1e-2 + 1e-2 |ref| + u * RSS, with u = 2^-8 the
+  dA = dxa^T x over 4096 tokens): |gpu - ref| <= 1e-2 + 1e-2 |ref| + 2u * RSS, with u = 2^-8 the
   unit roundoff of bf16 and RSS the root-sum-square of the sum's terms, from the oracle's own
-  values. Derivation: a stored bf16 factor (de, dv, hmid, the LoRA-A products) whose exact value
-  lies within the accumulation error of a rounding boundary is rounded one way by an fp32
-  evaluation and the other way by the fp64 oracle; each such decision moves its term by up to
-  2u of itself, with a sign independent of the others, so the sum moves by about
-  2u sqrt(p) RSS when a fraction p of the terms disagree. u * RSS is one standard deviation at
-  p = 1/4; an fp32 evaluation disagrees on fewer than 0.1% of the stored values. Near |ref| = 0
-  (cancellation over the tokens) the plain 1e-2 + 1e-2 |ref| bar is far below that noise: a
-  correct fp32 evaluation fails it on 0.07-1.6% of the weight-gradient entries at the Qwen3-8B
-  layer (tests/test_backward_tolerance.py shows both facts on the CPU).
+  values; and normwise ||gpu - ref|| <= 2u ||ref|| (the output's own rounding contributes up to
+  u/sqrt(3), and a scale that is not a power of two, folded into a bf16 copy of B, about as much
+  again through each rounded factor). Derivation of the per-entry bar: a stored bf16 factor (de, dv,
+  hmid, the LoRA-A products) whose exact value lies within the accumulation error of a rounding
+  boundary is rounded one way by an fp32 evaluation and the other way by the fp64 oracle. Such a
+  one-unit disagreement moves its term by at most 2u of the term, so by at most 2u RSS: the
+  allowance covers any single disagreement in full (one term can dominate a sum over a few
+  tokens). Disagreements in a fraction p of the terms, with independent signs, move the sum by
+  about 2u sqrt(p) RSS, so the allowance is 1/sqrt(p) standard deviations; an fp32 evaluation
+  disagrees on fewer than 0.1% of the stored values. Near |ref| = 0 (cancellation over the
+  tokens) the plain 1e-2 + 1e-2 |ref| bar is far below that noise: a correct fp32 evaluation
+  fails it on 0.07-1.8% of the weight-gradient entries at the Qwen3-8B layer
+  (tests/test_backward_tolerance.py shows it on the CPU).
 """
 
 from __future__ import annotations
@@ -58,15 +62,19 @@ BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8-bit significand)
 
 
 def assert_close_sum_lowp(got, ref, rss, what=""):
-    """bf16 sum whose terms carry bf16-stored factors: |got - ref| <= 1e-2 + 1e-2 |ref| + u RSS."""
+    """bf16 sum whose terms carry bf16-stored factors: |got - ref| <= 1e-2 + 1e-2 |ref| + 2u RSS
+    per entry, and ||got - ref|| <= 2u ||ref|| over the whole tensor."""
     g = f64(got)
     r = f64(ref)
     q = f64(rss)
-    bad = ~(np.abs(g - r) <= 1e-2 + 1e-2 * np.abs(r) + BF16_U * q)
+    nw = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)
+    if not nw <= 2 * BF16_U:
+        raise AssertionError(f"{what}: normwise error {nw:.3e} above 2u = {2 * BF16_U:.3e}")
+    bad = ~(np.abs(g - r) <= 1e-2 + 1e-2 * np.abs(r) + 2 * BF16_U * q)
     bad |= np.isnan(g) != np.isnan(r)
     if bad.any():
         idx = np.argwhere(bad)[:5]
-        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside 1e-2+1e-2|ref|+u*RSS; first "
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside 1e-2+1e-2|ref|+2u*RSS; first "
                              f"{[(tuple(i), g[tuple(i)], r[tuple(i)], q[tuple(i)]) for i in idx]}")
 
 

@@ -95,22 +95,33 @@ def test_expand_host_validation(kw, code):
 
 def test_workspace_sizes():
     assert _lib.lora_expand_workspace_size(1, 50, 3, 16, 4, 6144) == 0
-    try:
-        # one workgroup per tile over all of K: nothing needed for few segments
-        _lib.lora_tuning_override(3, 0)
-        assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) == 0
-        # shared work over 256 workgroups: 50 tokens in 16-token tiles give a bound of
-        # 4 + 4 segments = 8 tiles of 128 steps, 4 steps per workgroup, at most
-        # 127 // 4 + 2 = 33 pieces per tile, each an fp32 plane of [T][S*R]
-        _lib.lora_tuning_override(3, 256)
-        assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) == 33 * 50 * 48 * 4
-        assert _lib.lora_shrink_workspace_size(2, 50, 4096, 3, 16, 4) == 33 * 50 * 48 * 4
-    finally:
-        _lib.lora_tuning_override(3, -1)
+    P = _lib.Plan
+    # one workgroup per tile over all of K: nothing needed for few segments
+    assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, P(shrink_split=0)) == 0
+    # shared work over 256 workgroups, register-ring shape 2 (16-token tiles, one 16-column block
+    # per workgroup: 3 grid rows): 50 tokens give a bound of 4 + 4 segments = 8 tiles of 128
+    # steps, 4 steps per workgroup, at most 127 // 4 + 2 = 33 pieces per tile, each an fp32 plane
+    # of [T][S*R], after the 32 KiB counter region
+    plan = P(shrink_kernel=0, shrink_shape=2, shrink_split=256)
+    for dt in (1, 2):
+        assert _lib.lora_shrink_workspace_size_ex(dt, 50, 4096, 3, 16, 4, plan) == 32768 + 33 * 50 * 48 * 4
+    # a plan outside its ranges is refused
+    assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, P(shrink_shape=5)) == 0
+    assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, P(shrink_finish=2)) == 0
+    assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, None) == \
+        _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4)
     assert _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4) % 4 == 0
     n = _lib.lora_shrink_workspace_size(1, 16384, 256, 3, 16, 16384)
-    assert n >= 16 * 16384
+    assert n >= 32768 + 16 * 16384
     assert _lib.lora_shrink_workspace_size(1, 0, 256, 3, 16, 4) == 0
+
+
+def test_queries_are_pure():
+    """The same query gives the same answer whatever plans other calls used (no hidden state)."""
+    a = _lib.lora_shrink_workspace_size(1, 300, 4096, 3, 16, 4)
+    _lib.lora_shrink_workspace_size_ex(1, 300, 4096, 3, 16, 4, _lib.Plan(shrink_split=7))
+    _lib.lora_shrink_workspace_size_ex(1, 300, 4096, 3, 16, 4, _lib.Plan(shrink_kernel=1))
+    assert _lib.lora_shrink_workspace_size(1, 300, 4096, 3, 16, 4) == a
 
 
 def test_schedule_host_validation():

@@ -1,4 +1,4 @@
-"""Why the MLP-backward weight gradients are compared with the bar 1e-2 + 1e-2 |ref| + u RSS
+"""Why the MLP-backward weight gradients are compared with the bar 1e-2 + 1e-2 |ref| + 2u RSS
 (tests/parity.py) and not the plain 1e-2 + 1e-2 |ref| (CPU only).
 
 A straightforward fp32-accumulating evaluation of the same formulas and rounding points (torch
@@ -8,7 +8,7 @@ I = 12288, r = 16, scale 4):
 * it fails the plain bar on a fraction of the entries of the weight gradients, because a sum over
   4096 tokens with cancellation carries the noise of the stored bf16 factors whose rounding went
   the other way, and entries near zero then have only the 1e-2 absolute allowance;
-* it passes the bar with the u RSS allowance on every entry of all seven gradients.
+* it passes the bar with the 2u RSS allowance on every entry of all seven gradients.
 """
 
 import numpy as np

@@ -4,9 +4,9 @@ pre-activations, its own intermediates).
 
 Tolerances (tests/parity.py): the saved pre-activations e, v and the output are stored values of
 row-local sums, compared with the plain bf16 bar |err| <= 1e-2 + 1e-2 |ref|; the seven gradients
-are sums whose terms carry bf16-stored factors and are compared with 1e-2 + 1e-2 |ref| + u RSS
-(u = 2^-8, RSS the root-sum-square of the sum's terms from the oracle's values), the bar derived
-in tests/parity.py; the fraction outside the plain bar is printed. Small layers compare every
+are sums whose terms carry bf16-stored factors and are compared with 1e-2 + 1e-2 |ref| + 2u RSS
+(u = 2^-8, RSS the root-sum-square of the sum's terms from the oracle's values) and normwise
+within 2u, the bar derived in tests/parity.py; the fraction outside the plain bar is printed. Small layers compare every
 output; the Qwen3-8B-shaped layer (H = 4096, I = 12288, r = 16, scale 4) compares every output on
 its first 160 tokens and, at M = 4096, all seven gradients in full against the oracle over all
 4096 tokens (e, v and out on sampled rows).

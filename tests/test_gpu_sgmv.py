@@ -26,34 +26,24 @@ def _alp():
     return alp
 
 
-def _run_pair(c, d=None, variant=(None, None), ksplit=None, lds=None, bn=None):
-    alp = _alp()
+def _plan(variant=(None, None), ksplit=None, lds=None, bn=None, finish=None):
     from adapter_lora_projection_amd import _lib
 
+    v = lambda q: -1 if q is None else q
+    return _lib.Plan(shrink_kernel=v(lds), shrink_shape=v(variant[0]), shrink_split=v(ksplit),
+                     shrink_finish=v(finish), expand_shape=v(variant[1]), expand_block_n=v(bn))
+
+
+def _run_pair(c, d=None, variant=(None, None), ksplit=None, lds=None, bn=None, finish=None):
+    alp = _alp()
     d = d or to_dev(c)
-    try:
-        if variant[0] is not None:
-            _lib.lora_tuning_override(0, variant[0])
-        if variant[1] is not None:
-            _lib.lora_tuning_override(1, variant[1])
-        if ksplit is not None:
-            _lib.lora_tuning_override(3, ksplit)
-        if lds is not None:
-            _lib.lora_tuning_override(4, lds)
-        if bn is not None:
-            _lib.lora_tuning_override(2, bn)
-        h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
-                       d["lora_ranks"], c.S, c.R)
-        y = d["y_in"].clone()
-        alp.expand(h, d["B"], d["slice_offsets"], d["seg_indptr"], d["weight_indices"],
-                   d["permutation"], d["lora_ranks"], d["scalings"], y, c.S, c.R)
-        torch.cuda.synchronize()
-    finally:
-        _lib.lora_tuning_override(0, -1)
-        _lib.lora_tuning_override(1, -1)
-        _lib.lora_tuning_override(3, -1)
-        _lib.lora_tuning_override(4, -1)
-        _lib.lora_tuning_override(2, -1)
+    plan = _plan(variant, ksplit, lds, bn, finish)
+    h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
+                   d["lora_ranks"], c.S, c.R, plan=plan)
+    y = d["y_in"].clone()
+    alp.expand(h, d["B"], d["slice_offsets"], d["seg_indptr"], d["weight_indices"],
+               d["permutation"], d["lora_ranks"], d["scalings"], y, c.S, c.R, plan=plan)
+    torch.cuda.synchronize()
     return h.cpu(), y.cpu()
 
 
@@ -168,32 +158,136 @@ def test_shared_b_expand(ev, dtype, offs, bn, null_perm):
     _check_pair(c, h, y)
 
 
+@pytest.mark.parametrize("finish", [0, 1])
 @pytest.mark.parametrize("wgs", [0, 1, 7, 64, 1000])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-def test_shared_work_split(wgs, dtype):
+def test_shared_work_split(wgs, dtype, finish):
     """The (tile, K step) work shared over `wgs` workgroups (0 = one per tile): a single
     workgroup walking every tile, ranges that start and end inside tiles, and one step per
-    workgroup (up to 18 pieces per tile, summed by the second launch)."""
+    workgroup (up to 18 pieces per tile), the pieces summed by a second launch (finish 0) or by
+    each tile's last workgroup in the same launch (finish 1, arrival counters)."""
     c = li.make_sgmv(f"sk_{dtype}", seed=43, T=203, K=517, S=3, R=32, L=5,
                      slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
-    print("case", c.name, wgs, flush=True)
-    h, y = _run_pair(c, ksplit=wgs)
+    print("case", c.name, wgs, finish, flush=True)
+    h, y = _run_pair(c, ksplit=wgs, finish=finish)
     _check_pair(c, h, y)
 
 
+@pytest.mark.parametrize("finish", [0, 1])
 @pytest.mark.parametrize("wgs", [0, 5, 300])
 @pytest.mark.parametrize("sv", range(5))
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_lds_shrink_shapes(sv, wgs, dtype):
+def test_lds_shrink_shapes(sv, wgs, dtype, finish):
     """The LDS-staged shrink in every column-block shape (2..12 blocks per workgroup, so the 6
     blocks here are split over 3, 2, 2, 1 and 1 workgroups), one workgroup per tile or the work
-    shared over 5 or 300 workgroups; K = 1032 ends in a stage with one valid 8-element chunk;
-    tiles of 128 positions with ragged ends; rank 0, 1, 7, 17 and 32 adapters."""
+    shared over 5 or 300 workgroups (pieces added by a second launch or in the same launch);
+    K = 1032 ends in a stage with one valid 8-element chunk; tiles of 128 positions with ragged
+    ends; rank 0, 1, 7, 17 and 32 adapters."""
     c = li.make_sgmv(f"lds_{dtype}", seed=44, T=301, K=1032, S=3, R=32, L=5,
                      slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
-    print("case", c.name, sv, wgs, flush=True)
-    h, y = _run_pair(c, variant=(sv, None), ksplit=wgs, lds=1)
+    print("case", c.name, sv, wgs, finish, flush=True)
+    h, y = _run_pair(c, variant=(sv, None), ksplit=wgs, lds=1, finish=finish)
     _check_pair(c, h, y)
+
+
+@pytest.mark.parametrize("wgs", [16, 96, 256, 512, 2048])
+@pytest.mark.parametrize("sv", range(5))
+@pytest.mark.parametrize("T", [50, 128, 1024])
+def test_in_launch_split_decode_shapes(T, sv, wgs):
+    """The decode-QKV workload (4 adapters r16, K = 4096, empty segments possible) with every
+    register-ring shape and the work shared over 16 .. 2048 workgroups, pieces added in the
+    same launch: up to 129 pieces per tile."""
+    c = li.sweep_case(T)
+    print("case", c.name, sv, wgs, flush=True)
+    h, y = _run_pair(c, variant=(sv, None), ksplit=wgs, lds=0, finish=1)
+    _check_pair(c, h, y)
+
+
+def test_workspace_counters_left_zero_and_reused():
+    """One workspace for many calls: its arrival counters are zero after every call, and
+    repeated calls (also of other shapes) give bit-identical results."""
+    alp = _alp()
+    from adapter_lora_projection_amd import _lib
+
+    cases = [li.sweep_case(50), li.sweep_case(1024), li.config_irregular()]
+    nbytes = max(_lib.lora_shrink_workspace_size(li_dt(c), c.T, c.K, c.S, c.R, c.G) for c in cases)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    first = {}
+    for rep in range(3):
+        for c in cases:
+            d = to_dev(c)
+            h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
+                           d["lora_ranks"], c.S, c.R, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(ws[:32768].count_nonzero()) == 0, (c.name, rep)
+            if rep == 0:
+                check_h(c, h.cpu())
+                first[c.name] = h.cpu()
+            else:
+                assert torch.equal(h.cpu(), first[c.name]), (c.name, rep)
+
+
+def li_dt(c):
+    return {"f32": 0, "bf16": 1, "f16": 2}[c.dtype]
+
+
+def test_graph_capture_replays():
+    """shrink + expand captured in a HIP graph over one workspace: every replay (with eager work
+    and synchronisations between them) equals the eager result bit for bit."""
+    alp = _alp()
+    from adapter_lora_projection_amd import _lib
+
+    c = li.sweep_case(128)
+    d = to_dev(c)
+    nbytes = _lib.lora_shrink_workspace_size(li_dt(c), c.T, c.K, c.S, c.R, c.G)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    h = torch.empty((c.T, c.S * c.R), dtype=torch.bfloat16, device="cuda")
+    y = d["y_in"].clone()
+
+    def run():
+        alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], d["permutation"],
+                   d["lora_ranks"], c.S, c.R, h=h, workspace=ws)
+        alp.expand(h, d["B"], d["slice_offsets"], d["seg_indptr"], d["weight_indices"],
+                   d["permutation"], d["lora_ranks"], d["scalings"], y, c.S, c.R)
+
+    run()
+    torch.cuda.synchronize()
+    h_ref, y_ref = h.clone(), y.clone()
+    check_h(c, h_ref.cpu())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    y.copy_(d["y_in"])
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for rep in range(4):
+        y.copy_(d["y_in"])
+        h.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, h_ref) and torch.equal(y, y_ref), rep
+        assert int(ws[:32768].count_nonzero()) == 0
+        del junk
+
+
+# ------------------------------------------------------------------ the whole chain from x
+
+@pytest.mark.parametrize("which", ["decode", "prefill0", "prefill1", "irregular"])
+def test_chain_from_x(which):
+    """y from the GPU's shrink and expand compared with oracle.expand(oracle.shrink(x)), the
+    oracle's own h: nothing computed on the GPU is fed to the oracle."""
+    c = {"decode": li.config_decode_qkv, "irregular": li.config_irregular,
+         "prefill0": lambda: li.config_prefill()[0], "prefill1": lambda: li.config_prefill()[1]}[which]()
+    print("case", c.name, "chain", flush=True)
+    _, y = _run_pair(c)
+    h_ref = oracle.shrink(c.x, c.A, c.seg_indptr, c.weight_indices, c.permutation, c.lora_ranks,
+                          c.S, c.R, c.dtype)
+    y_ref = oracle.expand(h_ref, c.B, c.slice_offsets, c.seg_indptr, c.weight_indices,
+                          c.permutation, c.lora_ranks, c.scalings, c.y_in, c.R, c.dtype)
+    assert_close_lowp(y, y_ref, f"chain {c.name}")
 
 
 @pytest.mark.parametrize("lds", [0, 1])
@@ -215,18 +309,13 @@ def test_identity_permutation_null(dtype, lds):
     assert torch.equal(c.permutation, torch.arange(c.T, dtype=torch.int32))
     d = to_dev(c)
     alp = _alp()
-    from adapter_lora_projection_amd import _lib
-
-    try:
-        _lib.lora_tuning_override(4, lds)
-        h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], None,
-                       d["lora_ranks"], c.S, c.R)
-        y = d["y_in"].clone()
-        alp.expand(h, d["B"], d["slice_offsets"], d["seg_indptr"], d["weight_indices"], None,
-                   d["lora_ranks"], d["scalings"], y, c.S, c.R)
-        torch.cuda.synchronize()
-    finally:
-        _lib.lora_tuning_override(4, -1)
+    plan = _plan(lds=lds)
+    h = alp.shrink(d["x"], d["A"], d["seg_indptr"], d["weight_indices"], None,
+                   d["lora_ranks"], c.S, c.R, plan=plan)
+    y = d["y_in"].clone()
+    alp.expand(h, d["B"], d["slice_offsets"], d["seg_indptr"], d["weight_indices"], None,
+               d["lora_ranks"], d["scalings"], y, c.S, c.R, plan=plan)
+    torch.cuda.synchronize()
     _check_pair(c, h.cpu(), y.cpu())
 
 
