@@ -46,6 +46,9 @@ SIGNATURES = {
     "lora_shrink_ex": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
                               _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_shrink_workspace_size_ex": (_sz, [_i32, _i64, _i64, _i32, _i32, _i32, _vp]),
+    "lora_shrink_noalloc": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
+                                   _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "lora_shrink_noalloc_max_workspace": (_sz, []),
     "lora_expand_ex": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _i64,
                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lora_mlp_fused": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp, _vp,
@@ -142,6 +145,18 @@ def lora_shrink_ex(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr, weight
                               _p(weight_indices), _p(permutation), _p(lora_ranks), _p(h), ldh,
                               _plan(plan), _p(workspace), workspace_bytes, stream)
     _check("lora_shrink_ex", st)
+
+
+def lora_shrink_noalloc(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr, weight_indices,
+                        permutation, lora_ranks, h, ldh, stream) -> None:
+    st = lib().lora_shrink_noalloc(dtype, T, K, S, R, L, G, _p(x), ldx, _p(w_a), lda,
+                                   _p(seg_indptr), _p(weight_indices), _p(permutation),
+                                   _p(lora_ranks), _p(h), ldh, stream)
+    _check("lora_shrink_noalloc", st)
+
+
+def lora_shrink_noalloc_max_workspace() -> int:
+    return int(lib().lora_shrink_noalloc_max_workspace())
 
 
 def lora_shrink_workspace_size_ex(dtype, T, K, S, R, G, plan) -> int:

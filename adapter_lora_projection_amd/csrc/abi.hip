@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/lora_mi355x.h"
 #include "embedding.hpp"
@@ -12,7 +13,35 @@
 #include "mlp_kernels.hpp"
 #include "sgmv_kernels.hpp"
 
+// Device scratch of lora_shrink_noalloc, for callers that cannot allocate: file-scope device
+// storage, one copy per GPU the library runs on, held until the process ends. In host code this
+// name is only a host-side stand-in: kernels and copies take the device address that
+// hipGetSymbolAddress returns for the current device (scratch_address below), never the name.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+// The scratch array's device address, taken once per device (with that device current) and kept
+// per device; thread-safe.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
 
 constexpr int kInlineMaxSegments = 1024;  // above this the standalone scheduler builds the list
 constexpr int kMaxSlices = 64;
@@ -575,6 +604,23 @@ lora_status lora_shrink_ex(lora_dtype dtype, int64_t T, int64_t K, int32_t S, in
                      permutation, lora_ranks, h, ldh, kn, workspace, workspace_bytes, stream,
                      false);
 }
+
+lora_status lora_shrink_noalloc(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                                int32_t L, int32_t G, const void* x, int64_t ldx,
+                                const void* w_a, int64_t lda, const int32_t* seg_indptr,
+                                const int32_t* weight_indices, const int32_t* permutation,
+                                const int32_t* lora_ranks, void* h, int64_t ldh, void* stream) {
+  const Knobs kn;
+  if (T > 0 && G > 0 && K > 0 && S > 0 && R > 0 && valid_dtype(dtype) &&
+      lora_shrink_workspace_size_ex(dtype, T, K, S, R, G, nullptr) > kScratchBytes)
+    return LORA_EWORKSPACE;  // needs more than the fixed scratch array
+  void* ptr = nullptr;
+  if (scratch_address(&ptr) != hipSuccess || ptr == nullptr) return LORA_EHIP;
+  return shrink_impl(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr, weight_indices,
+                     permutation, lora_ranks, h, ldh, kn, ptr, kScratchBytes, stream, true);
+}
+
+size_t lora_shrink_noalloc_max_workspace(void) { return kScratchBytes; }
 
 lora_status lora_shrink(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t L,
                         int32_t G, const void* x, int64_t ldx, const void* w_a, int64_t lda,

@@ -120,6 +120,29 @@ size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_
                                   int32_t G);
 
 /*
+ * lora_shrink_noalloc -- lora_shrink for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same operation,
+ * arguments, kernels and results as lora_shrink, with no workspace argument. Its scratch (segment
+ * schedule, partial sums, arrival counters) is a fixed array of
+ * lora_shrink_noalloc_max_workspace() bytes (16 MiB) in the library's own device memory, one per
+ * GPU, held until the process ends; its address is looked up once per device, on that device's
+ * first call. The call allocates and frees nothing. It returns LORA_EWORKSPACE when the problem
+ * needs more scratch than that (lora_shrink_workspace_size above 16 MiB), other errors as
+ * lora_shrink. Every call on one GPU shares that GPU's array and leaves its contents there; the
+ * counters a call uses are cleared at its start by a small fill kernel on `stream` (no memset), so
+ * the call can be captured in a graph. Calls that can overlap in time on one GPU (different
+ * streams, or graphs replayed concurrently) race on the array and give undefined results: order
+ * them on one stream. `stream` must belong to the current device.
+ */
+lora_status lora_shrink_noalloc(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                                int32_t L, int32_t G, const void* x, int64_t ldx,
+                                const void* w_a, int64_t lda, const int32_t* seg_indptr,
+                                const int32_t* weight_indices, const int32_t* permutation,
+                                const int32_t* lora_ranks, void* h, int64_t ldh, void* stream);
+
+size_t lora_shrink_noalloc_max_workspace(void);
+
+/*
  * lora_plan -- an explicit choice of kernel shape for lora_shrink_ex / lora_expand_ex, for
  * measurement sweeps and for tests that reach every shape. Every field -1 (or a NULL plan) is
  * the library's own choice, which is what lora_shrink / lora_expand make. A plan is an input of
