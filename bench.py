@@ -127,6 +127,24 @@ def mlp_flops(M: int, H: int, I: int, r: int) -> tuple[int, int]:
     return base, lora
 
 
+def timed_windows(call, steps: int, windows: int = 5) -> tuple[float, list]:
+    """Median over `windows` windows of `steps` calls back to back, each window between two HIP
+    events on the launch stream (ms per call), and the per-window figures."""
+    import torch
+
+    n = max(steps, 1)
+    per = []
+    for _ in range(windows):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / n)
+    return float(np.median(per)), [round(x, 4) for x in per]
+
+
 def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
     """The single-adapter fused LoRA+SwiGLU MLP (bf16, M=4096, H=4096, I=12288, r=16, scale 4):
     K calls back to back after a warm-up, timed with HIP events on the stream they are launched
@@ -151,20 +169,15 @@ def mlp_object(steps: int, warmup: int, traffic_table: dict) -> dict:
     for _ in range(max(warmup, 60)):
         call()
     torch.cuda.synchronize()
-    # K calls back to back between two events on the stream they run on
-    n = max(steps, 1)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(n):
-        call()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / n
+    # windows of K calls back to back between two events on the stream they run on; the median
+    # window is reported (robust to a transient clock dip in one window)
+    ms, windows = timed_windows(call, steps)
     base, lora = mlp_flops(c.M, c.H, c.I, c.r)
     tflops = (base + lora) / (ms * 1e-3) / 1e12
     return {"workload": f"fused LoRA+SwiGLU MLP bf16, M={c.M} H={c.H} I={c.I} r={c.r} "
                         f"scale={c.scale:g}", "ms_per_call": round(ms, 4),
             "flops_per_call": int(base + lora), "value": round(tflops, 1), "unit": "TFLOP/s",
+            "windows_ms": windows,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic_table.get("mlp_fused"),
@@ -227,14 +240,7 @@ def mlp_backward_object(steps: int, warmup: int) -> dict:
         for _ in range(max(warmup, 40)):
             call()
         torch.cuda.synchronize()
-        n = max(steps, 1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(n):
-            call()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
+        return timed_windows(call, max(steps // 2, 1), 3)[0]
 
     ms_f = timed(fwd)
     ms_b = timed(bwd)
@@ -288,14 +294,7 @@ def attention_object(steps: int, warmup: int) -> dict:
     for _ in range(max(warmup, 60)):
         call()
     torch.cuda.synchronize()
-    n = max(steps, 1)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(n):
-        call()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / n
+    ms, _ = timed_windows(call, steps)
     nqkv = c.Nq + 2 * c.Nkv
     flops = (2 * c.M * c.H * nqkv + 2 * c.M * c.r * (3 * c.H + nqkv)  # q, k, v
              + 2 * c.M * c.Nq * c.H + 2 * c.M * c.r * (c.Nq + c.H))   # o
