@@ -72,7 +72,7 @@ Knobs knobs_of(const lora_plan* p) {
 
 // Plan fields outside their documented ranges are argument errors.
 bool knobs_valid(const Knobs& k) {
-  return k.family >= -1 && k.family <= 1 && k.shape >= -1 &&
+  return k.family >= -1 && k.family <= 2 && k.shape >= -1 &&
          k.shape < std::max(lmx::num_shrink_variants(), lmx::num_shrink_lds_variants()) &&
          !(k.family == 1 && k.shape >= lmx::num_shrink_lds_variants()) &&
          !(k.family == 0 && k.shape >= lmx::num_shrink_variants()) && k.split >= -1 &&
@@ -132,6 +132,7 @@ int shrink_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t G, 
 // share of the (tile, reduction step) work, about one workgroup per compute unit.
 struct ShrinkWs {
   bool lds;          // LDS-staged kernel (else the register-ring kernel)
+  bool gemv;         // wave-reduction kernel (direct only)
   bool in_launch;    // stream-K pieces added by each tile's last workgroup (arrival counters)
   int variant, bm, grid_x, gy, mp, unit;
   int64_t bound, q;  // tile bound; stream-K units per workgroup (0 = direct mode)
@@ -198,11 +199,24 @@ bool prefer_lds_pub(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S,
 }
 
 ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, int32_t R,
-                   int32_t G, bool lds, bool in_launch_ok) {
+                   int32_t G, bool lds, bool in_launch_ok, bool gemv = false) {
   ShrinkWs w{};
   w.lds = lds;
+  w.gemv = gemv;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
   int64_t gy, frags;
+  if (gemv) {  // one workgroup per 16-token tile and 16-column block, over all of K
+    w.variant = 0;
+    w.bm = 16;
+    w.unit = 32;
+    w.gy = int(nblk);
+    w.bound = cdiv(T, 16) + G;
+    w.grid_x = int(w.bound);
+    w.sched = schedule_bytes(T, G, w.bm);
+    w.part = align256(kCounterBytes + w.sched);
+    w.total = w.sched > 0 ? kCounterBytes + w.sched : 0;
+    return w;
+  }
   if (lds) {
     w.variant = shrink_lds_variant(kn, S, R);
     w.bm = lmx::kShrinkLdsBM;
@@ -515,9 +529,10 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   if (int64_t(S) * R * T * 16 >= int64_t(1) << 62) return LORA_EUNSUPPORTED;
   const int e = esize(dtype);
   const bool aligned = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
-  const bool lds = dtype != LORA_F32 && aligned && K % 8 == 0 &&
+  const bool gemv = kn.family == 2 && dtype != LORA_F32 && aligned && K % 8 == 0;
+  const bool lds = !gemv && dtype != LORA_F32 && aligned && K % 8 == 0 &&
                    prefer_lds_pub(kn, int(dtype), T, K, S, R, G);
-  const ShrinkWs ws = shrink_ws(kn, int(dtype), T, K, S, R, G, lds, true);
+  const ShrinkWs ws = shrink_ws(kn, int(dtype), T, K, S, R, G, lds, true, gemv);
   const int variant = ws.variant;
   const int bm = ws.bm;
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total)) return LORA_EWORKSPACE;
@@ -544,7 +559,7 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   a.sk_q = ws.q; a.sk_tiles = int(bound); a.sk_mp = ws.mp; a.sk_unit = ws.unit;
   if (ws.q > 0) a.part = reinterpret_cast<float*>(wsb + ws.part);
   if (ws.q > 0 && ws.in_launch) a.counters = reinterpret_cast<int*>(wsb);
-  lmx::ShrinkPlan splan{variant, ws.grid_x, aligned, ws.lds};
+  lmx::ShrinkPlan splan{variant, ws.grid_x, aligned, ws.lds, ws.gemv};
   if (lmx::launch_shrink(int(dtype), a, splan, st) != hipSuccess) return LORA_EHIP;
   if (ws.q > 0 && !ws.in_launch)
     return hip_status(lmx::launch_shrink_sk_reduce(int(dtype), a, bm, st));
@@ -574,9 +589,11 @@ size_t lora_shrink_workspace_size_ex(lora_dtype dtype, int64_t T, int64_t K, int
   if (T <= 0 || G <= 0 || K <= 0 || S <= 0 || R <= 0 || !valid_dtype(dtype)) return 0;
   const Knobs kn = knobs_of(plan);
   if (!knobs_valid(kn)) return 0;
-  // the kernel family depends on pointer alignment, which the query does not see: cover both
+  // the kernel family depends on pointer alignment, which the query does not see: cover each
+  // family the call may take
   const size_t reg = shrink_ws(kn, int(dtype), T, K, S, R, G, false, true).total;
   if (dtype == LORA_F32 || K % 8 != 0 || kn.family == 0) return reg;
+  if (kn.family == 2) return std::max(reg, shrink_ws(kn, int(dtype), T, K, S, R, G, false, true, true).total);
   return std::max(reg, shrink_ws(kn, int(dtype), T, K, S, R, G, true, true).total);
 }
 

@@ -1,11 +1,13 @@
 // SGMV shrink/expand kernels instantiated for one storage type (bf16); split per type so the
 // build compiles the types in parallel.
 #include "sgmv_impl.hpp"
+#include "shrink_gemv.hpp"
 #include "shrink_lds.hpp"
 
 namespace lmx {
 
 hipError_t launch_shrink_bf16(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st) {
+  if (plan.gemv) return launch_shrink_gemv_dt<DT_BF16>(a, plan, st);
   if (plan.lds) return launch_shrink_lds_dt<DT_BF16>(a, plan, st);
   return launch_shrink_dt<DT_BF16>(a, plan, st);
 }

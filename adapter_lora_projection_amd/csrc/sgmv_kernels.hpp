@@ -59,6 +59,7 @@ struct ShrinkPlan {
   int grid_x;    // direct: tile bound ceil(T / BM) + G; stream-K: workgroups with work
   bool aligned;  // x, A bases and row strides are 16-byte aligned
   bool lds;      // the LDS-staged kernel (16-bit types, aligned rows, K % 8 == 0)
+  bool gemv;     // the wave-reduction kernel (16-bit types, aligned rows, K % 8 == 0; direct)
 };
 
 struct ExpandPlan {

@@ -149,8 +149,11 @@ size_t lora_shrink_noalloc_max_workspace(void);
  * the one call: the library keeps no state between calls. Results are identical for every plan
  * up to the fp32 summation order. A field outside its range makes the call return LORA_EINVAL
  * (and the workspace query 0).
- *   shrink_kernel   0 operands loaded straight into registers; 1 staged through LDS (taken only
- *                   for 16-bit types with 16-byte aligned x and A rows and K % 8 == 0, else 0).
+ *   shrink_kernel   0 operands loaded straight into MFMA registers; 1 staged through LDS; 2 the
+ *                   wave-reduction (GEMV) form: packed dot products and cross-lane sums instead
+ *                   of MFMA, one workgroup per 16-token tile and 16-column block (split ignored).
+ *                   1 and 2 are taken only for 16-bit types with 16-byte aligned x and A rows
+ *                   and K % 8 == 0, else 0 runs.
  *   shrink_shape    shape of the chosen kernel: 0 .. LORA_SHRINK_RING_SHAPES - 1 (kernel 0) or
  *                   0 .. LORA_SHRINK_LDS_SHAPES - 1 (kernel 1).
  *   shrink_split    0: one workgroup per tile over all of K; n in 1 .. 65535: n workgroups share

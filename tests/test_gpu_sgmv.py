@@ -190,6 +190,30 @@ def test_lds_shrink_shapes(sv, wgs, dtype, finish):
     _check_pair(c, h, y)
 
 
+@pytest.mark.parametrize("case", ["var", "decode50", "decode1024", "ones"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gemv_shrink(case, dtype):
+    """The wave-reduction (GEMV) shrink: tiles of up to 16 positions with ragged ends, odd ranks
+    and rank 0 with NaN in the rank padding, unaligned slices, 16,384-segment schedule, K with a
+    partial 512-element sweep (K = 520), and the decode workloads."""
+    if case == "var":
+        c = li.make_sgmv(f"gemv_{dtype}", seed=49, T=301, K=520, S=3, R=32, L=5,
+                         slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
+        for a in range(c.L):
+            c.A.view(c.L, c.S, c.R, c.K)[a, :, int(c.lora_ranks[a]):, :] = float("nan")
+    elif case == "ones":
+        c = li.make_sgmv(f"gemv_ones_{dtype}", seed=50, T=3000, K=256, S=1, R=16, L=8,
+                         slice_offsets=[0, 16], dtype=dtype, lengths="ones")
+    else:
+        c = li.sweep_case(50 if case == "decode50" else 1024)
+        if dtype == "f16":
+            c = li.make_sgmv(f"gemv_dec_{dtype}", seed=1, T=c.T, K=4096, S=3, R=16, L=4,
+                             slice_offsets=[0, 4096, 5120, 6144], dtype=dtype)
+    print("case", c.name, "gemv", flush=True)
+    h, y = _run_pair(c, lds=2)
+    _check_pair(c, h, y)
+
+
 @pytest.mark.parametrize("wgs", [16, 96, 256, 512, 2048])
 @pytest.mark.parametrize("sv", range(5))
 @pytest.mark.parametrize("T", [50, 128, 1024])
