@@ -559,6 +559,9 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   a.sk_q = ws.q; a.sk_tiles = int(bound); a.sk_mp = ws.mp; a.sk_unit = ws.unit;
   if (ws.q > 0) a.part = reinterpret_cast<float*>(wsb + ws.part);
   if (ws.q > 0 && ws.in_launch) a.counters = reinterpret_cast<int*>(wsb);
+#ifndef LMX_NO_XCD_ROWS
+  if (!ws.lds && !ws.gemv && ws.q == 0 && ws.gy > 1) a.xcd_rows = ws.gy;
+#endif
   lmx::ShrinkPlan splan{variant, ws.grid_x, aligned, ws.lds, ws.gemv};
   if (lmx::launch_shrink(int(dtype), a, splan, st) != hipSuccess) return LORA_EHIP;
   if (ws.q > 0 && !ws.in_launch)

@@ -86,7 +86,7 @@ __device__ __forceinline__ float part_load(const float* q) {
 // zero rows.
 template <int DT, int NT>
 __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, int np, int CBY,
-                          int* s_last) {
+                          int by, int ny, int* s_last) {
   using Tr = Traits<DT>;
   using S = typename Tr::store_t;
   const int NB = (p.R + 15) >> 4;
@@ -96,7 +96,7 @@ __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, i
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
     __syncthreads();                // ... and every other thread's
     if (threadIdx.x == 0) {
-      int* ctr = p.counters + int64_t(t) * gridDim.y + blockIdx.y;
+      int* ctr = p.counters + int64_t(t) * ny + by;
       const int before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = before == np - 1;
       if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -107,7 +107,7 @@ __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, i
   } else if (j != 0) {
     return;
   }
-  const int b0 = int(blockIdx.y) * CBY;
+  const int b0 = by * CBY;
   const int nb = min(CBY, nblk - b0);
   const int W = nb * 16;
   const int n = tile.mlen * W;
@@ -143,8 +143,8 @@ __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, i
 // fragment is partial or past the end and no operand needs masking (a lane outside the tile or
 // the rank only produces outputs that are never stored).
 template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL>
-__device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& tile, int k0, int k1,
-                                             f32x4_t (*s_red)[CB * MT][64],
+__device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& tile, int by, int k0,
+                                             int k1, f32x4_t (*s_red)[CB * MT][64],
                                              f32x4_t (&out)[(CB * MT + NW - 1) / NW]) {
   using Tr = Traits<DT>;
   using S = typename Tr::store_t;
@@ -178,7 +178,7 @@ __device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& ti
   bool any_col = false;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const int blk = int(blockIdx.y) * CB + cb;
+    const int blk = by * CB + cb;
     const int s = blk / NB, b = blk - (blk / NB) * NB;
     const int j = 16 * b + li;
     col_ok[cb] = (blk < nblk) && (j < r);
@@ -320,13 +320,13 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
   const int64_t nsteps = (p.K + Tr::kStep - 1) / Tr::kStep;
 
   // Stores the sums this wave finalises: to h (rounded) or to a partial slot (fp32).
-  auto store = [&](const Tile& tile, const f32x4_t (&sums)[NOUT], float* slot) {
+  auto store = [&](const Tile& tile, int by, const f32x4_t (&sums)[NOUT], float* slot) {
 #pragma unroll
     for (int n = 0; n < NOUT; ++n) {
       const int idx = (NW > 1) ? w + n * NW : n;
       if (idx >= CB * MT) continue;
       const int cb = idx / MT, mt = idx - (idx / MT) * MT;
-      const int blk = int(blockIdx.y) * CB + cb;
+      const int blk = by * CB + cb;
       const int m = mt * 16 + li;
       if (blk >= nblk || m >= tile.mlen) continue;
       const int s = blk / NB, b = blk - (blk / NB) * NB;
@@ -349,11 +349,23 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
   };
 
   if (p.sk_q == 0) {
-    const Tile tile = shrink_tile<NT>(p, BM, int(blockIdx.x), &s_tile, s_scan);
+    // Direct mode. With several grid rows (column-block groups) the grid is one-dimensional
+    // (p.xcd_rows > 0): workgroup L runs on XCD L % 8, which takes a contiguous eighth of the
+    // tiles, each tile's grid rows on consecutive workgroups of that XCD. The tile's x rows then
+    // come from the XCD's L2 after the first read, and the tiles of one segment (one adapter's
+    // A rows) stay on one or two XCDs.
+    int tx = int(blockIdx.x), by = int(blockIdx.y);
+    if (p.xcd_rows > 0) {
+      const int L = int(blockIdx.x);
+      const int tpx = (int(gridDim.x) / 8) / p.xcd_rows;  // tiles per XCD
+      tx = (L % 8) * tpx + (L / 8) / p.xcd_rows;
+      by = (L / 8) % p.xcd_rows;
+    }
+    const Tile tile = shrink_tile<NT>(p, BM, tx, &s_tile, s_scan);
     if (tile.g < 0) return;
     f32x4_t sums[NOUT];
-    shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, 0, int(nsteps), s_red, sums);
-    store(tile, sums, nullptr);
+    shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, by, 0, int(nsteps), s_red, sums);
+    store(tile, by, sums, nullptr);
     return;
   }
 
@@ -370,11 +382,12 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
     if (tile.r > 0) {
       f32x4_t sums[NOUT];
-      shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, k0, k1, s_red, sums);
-      store(tile, sums, slot);
+      shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, int(blockIdx.y), k0, k1, s_red, sums);
+      store(tile, int(blockIdx.y), sums, slot);
     }
     if (p.counters != nullptr)
-      sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nsteps, p.sk_q), CB, &s_last);
+      sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nsteps, p.sk_q), CB, int(blockIdx.y),
+                        int(gridDim.y), &s_last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }
@@ -1065,6 +1078,10 @@ static hipError_t launch_shrink_t(const ShrinkArgs& a, bool aligned, int grid_x,
   const int NB = (a.R + 15) / 16;
   const int nblk = a.S * NB;
   dim3 grid(grid_x, (nblk + CB - 1) / CB);
+  if (a.xcd_rows > 0) {  // direct mode, tiles of one tile's grid rows on one XCD (see the kernel)
+    if (a.sk_q != 0 || a.xcd_rows != int(grid.y)) return hipErrorInvalidValue;
+    grid = dim3(unsigned((grid_x + 7) / 8 * 8 * a.xcd_rows), 1);
+  }
   const bool kfull = a.K % Traits<DT>::kStep == 0;
   if (aligned && kfull)
     hipLaunchKernelGGL((shrink_kernel<DT, MT, CB, NW, D, true, true>), grid, dim3(NW * 64), 0, st, a);

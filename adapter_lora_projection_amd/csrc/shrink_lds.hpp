@@ -202,7 +202,8 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
     if (tile.r > 0) piece(tile, k0, k1, slot);
     if (p.counters != nullptr)
-      sk_finish<DT, 256>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, &s_last);
+      sk_finish<DT, 256>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, int(blockIdx.y),
+                         int(gridDim.y), &s_last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }
