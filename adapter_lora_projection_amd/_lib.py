@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "liblora_mi355x.so")
 
 LORA_OK, LORA_EINVAL, LORA_EUNSUPPORTED, LORA_EWORKSPACE, LORA_EHIP, LORA_EVALUE = range(6)
 LORA_F32, LORA_BF16, LORA_F16 = 0, 1, 2
-LORA_SHRINK_RING_SHAPES, LORA_SHRINK_LDS_SHAPES, LORA_EXPAND_SHAPES = 5, 5, 10
+LORA_SHRINK_RING_SHAPES, LORA_SHRINK_LDS_SHAPES, LORA_EXPAND_SHAPES = 5, 13, 10
 
 
 class Plan(ctypes.Structure):

@@ -165,22 +165,38 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // The LDS-staged shrink covers the 16-bit types whose x and A rows are 16-byte aligned and
 // whose K is a multiple of 8; its shape is the smallest column-block count that holds every
 // block of the slices (or 12 blocks per workgroup beyond that).
-int shrink_lds_variant(const Knobs& kn, int32_t S, int32_t R) {
+int shrink_lds_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t G, bool pub) {
   if (kn.shape >= 0 && kn.shape < lmx::num_shrink_lds_variants()) return kn.shape;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  for (int v = 0; v < lmx::num_shrink_lds_variants(); ++v)
+  if (pub && nblk == 3) {
+    // Three column blocks (rank 16 over three slices, the decode projections): the shortest
+    // tiles whose grid fits in one round of 256 workgroups. Kernel durations on the decode
+    // sweep (rocprofv3, each call after a 512 MiB read): 32-position tiles, 2 waves, 4 stages
+    // 21.3 / 21.5 / 21.8 us at 2048 / 4096 / 6144 tokens; at 8192 (260 such tiles) 48-position
+    // tiles, 3 waves, 6 stages 23.5 us, against 26.1 us for 64-position and 39 us for
+    // 128-position tiles. Shorter tiles re-read the A rows from the L2 more often but keep more
+    // compute units streaming x.
+    for (int v : {8, 12, 7})
+      if (cdiv(T, lmx::shrink_lds_bm(v)) + G <= 256) return v;
+    return 1;
+  }
+  int widest = 0;
+  for (int v = 0; v < lmx::num_shrink_lds_variants(); ++v) {
+    if (lmx::shrink_lds_bm(v) != 128) continue;
     if (lmx::shrink_lds_ncb(v) >= nblk) return v;
-  return lmx::num_shrink_lds_variants() - 1;
+    if (lmx::shrink_lds_ncb(v) > lmx::shrink_lds_ncb(widest)) widest = v;
+  }
+  return widest;
 }
 
 // Which shrink kernel to run when the LDS-staged one is eligible (event timings and rocprofv3
-// sweeps on MI355X). The LDS-staged kernel streams about twice as fast per workgroup (its
-// direct-to-LDS loads keep more bytes in flight) and shares each A chunk over 128 positions,
-// but a tile of 128 positions leaves most compute units idle unless T is large. Internal dense
+// sweeps on MI355X). The LDS-staged kernel's direct-to-LDS loads fetch whole 128-byte row
+// chunks (the register ring's MFMA-layout loads take 64 bytes from each of 16 rows, and its
+// address path stalls on the L1), and each A chunk is shared by the whole tile. Internal dense
 // products (fused MLP, projections, backward): from T * K = 16 Mi elements with few column
-// blocks, as tuned with their shared-work second launch. Shrink entry point: when even the
-// register ring's wider shape would need a second round of workgroups (decode 8192 tokens:
-// 260 workgroups of 32 positions), and T * K is large.
+// blocks, as tuned with their shared-work second launch. Shrink entry point: with three column
+// blocks from 8 Mi elements (the short-tile shapes, see shrink_lds_variant); otherwise when even
+// the register ring's wider shape would need a second round of workgroups and T * K is large.
 bool prefer_lds(const Knobs& kn, int64_t T, int64_t K, int32_t S, int32_t R) {
   if (kn.family >= 0) return kn.family == 1;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
@@ -191,6 +207,10 @@ bool prefer_lds_pub(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S,
                     int32_t G) {
   if (kn.family >= 0) return kn.family == 1;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
+  // three column blocks: the short-tile LDS shapes from 8 Mi elements of x (2048 tokens at
+  // K = 4096: 21.3 us against 22.9 us for the register ring; at 1024 tokens the ring's 13.6 us
+  // against 21.0 us)
+  if (nblk == 3) return T * K >= (int64_t(8) << 20);
   if (T * K < (int64_t(16) << 20) || nblk > 4) return false;
   const int v = shrink_variant(kn, T, S, R, G, true);
   const int64_t ring_wgs = (cdiv(T, lmx::shrink_plan_bm(dtype, v)) + G) *
@@ -218,8 +238,8 @@ ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, 
     return w;
   }
   if (lds) {
-    w.variant = shrink_lds_variant(kn, S, R);
-    w.bm = lmx::kShrinkLdsBM;
+    w.variant = shrink_lds_variant(kn, T, S, R, G, in_launch_ok);
+    w.bm = lmx::shrink_lds_bm(w.variant);
     w.unit = lmx::kShrinkLdsUnit;
     gy = cdiv(nblk, lmx::shrink_lds_ncb(w.variant));
     frags = (w.bm + 16 * lmx::shrink_lds_ncb(w.variant)) / 8;  // 1 KiB loads per stage

@@ -31,9 +31,11 @@ int shrink_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kShri
 int shrink_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 8 : kShrinkWaves[variant]; }
 int shrink_plan_cb(int dtype, int variant) { return dtype == DT_F32 ? 1 : kShrinkCB[variant]; }
 // mirrors LMX_SHRINK_LDS_VARIANTS of shrink_lds.hpp
-static const int kShrinkLdsNCB[] = {2, 3, 4, 8, 12};
+static const int kShrinkLdsNCB[] = {2, 3, 4, 8, 12, 3, 3, 3, 3, 3, 3, 3, 3};
+static const int kShrinkLdsBMs[] = {128, 128, 128, 128, 128, 64, 64, 64, 32, 32, 64, 48, 48};
 int num_shrink_lds_variants() { return int(sizeof(kShrinkLdsNCB) / sizeof(int)); }
 int shrink_lds_ncb(int variant) { return kShrinkLdsNCB[variant]; }
+int shrink_lds_bm(int variant) { return kShrinkLdsBMs[variant]; }
 int expand_plan_bm(int dtype, int variant) { return dtype == DT_F32 ? 16 : kExpandBM[variant]; }
 int expand_plan_waves(int dtype, int variant) { return dtype == DT_F32 ? 4 : kExpandWaves[variant]; }
 int expand_plan_chunk(int dtype, int variant) { return dtype == DT_F32 ? 64 : kExpandChunk[variant]; }

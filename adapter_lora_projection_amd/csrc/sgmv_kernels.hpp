@@ -91,7 +91,7 @@ int shrink_plan_waves(int dtype, int variant);
 int shrink_plan_cb(int dtype, int variant);
 int num_shrink_lds_variants();
 int shrink_lds_ncb(int variant);          // 16-column blocks per workgroup
-constexpr int kShrinkLdsBM = 128;         // positions per tile of the LDS-staged shrink
+int shrink_lds_bm(int variant);           // positions per tile
 constexpr int kShrinkLdsUnit = 64;        // reduction indices per stage
 hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
 hipError_t launch_schedule(const int* seg_indptr, const int* weight_indices, int G, int BM,

@@ -27,12 +27,12 @@ namespace lmx {
 
 static __device__ __align__(16) uint4 g_zero_block[1] = {{0u, 0u, 0u, 0u}};
 
-template <int DT, int BMG, int NCB, int NS>
-__global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
+template <int DT, int BMG, int NCB, int NS, int NW>
+__global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
   using Tr = Traits<DT>;
   using S = typename Tr::store_t;
   static_assert(sizeof(S) == 2, "16-bit storage types only");
-  constexpr int NW = 4;
+  constexpr int NT = NW * 64;
   constexpr int BM = 16 * BMG, NC = 16 * NCB;
   constexpr int KB = 64;                    // reduction indices per stage
   constexpr int XI = BM / 8, AI = NC / 8;   // 1 KiB load instructions per stage for x and A
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
   };
 
   if (p.sk_q == 0) {
-    const Tile tile = shrink_tile<256>(p, BM, int(blockIdx.x), &s_tile, s_scan);
+    const Tile tile = shrink_tile<NT>(p, BM, int(blockIdx.x), &s_tile, s_scan);
     if (tile.g < 0) return;
     piece(tile, 0, nunits, nullptr);
     return;
@@ -196,37 +196,45 @@ __global__ __launch_bounds__(256) void shrink_lds_kernel(ShrinkArgs p) {
     const int t = int(u / nunits);
     const int64_t k0 = u - int64_t(t) * nunits;
     const int64_t k1 = min(nunits, k0 + (uend - u));
-    const Tile tile = shrink_tile<256>(p, BM, t, &s_tile, s_scan);
+    const Tile tile = shrink_tile<NT>(p, BM, t, &s_tile, s_scan);
     if (tile.g < 0) break;  // past the last tile (uniform over the workgroup)
     const int j = int(blockIdx.x) - int((int64_t(t) * nunits) / p.sk_q);
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
     if (tile.r > 0) piece(tile, k0, k1, slot);
     if (p.counters != nullptr)
-      sk_finish<DT, 256>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, int(blockIdx.y),
+      sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, int(blockIdx.y),
                          int(gridDim.y), &s_last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }
 }
 
-// Kernel shapes of the LDS-staged shrink: (index, BMG, NCB, NS). 128 positions per tile;
-// NCB 16-column blocks per workgroup; NS stages.
+// Kernel shapes of the LDS-staged shrink: (index, BMG, NCB, NS, NW): 16 BMG positions per tile,
+// NCB 16-column blocks per workgroup, NS stages, NW waves.
 #define LMX_SHRINK_LDS_VARIANTS(X) \
-  X(0, 8, 2, 3)                    \
-  X(1, 8, 3, 3)                    \
-  X(2, 8, 4, 3)                    \
-  X(3, 8, 8, 3)                    \
-  X(4, 8, 12, 3)
+  X(0, 8, 2, 3, 4)                 \
+  X(1, 8, 3, 3, 4)                 \
+  X(2, 8, 4, 3, 4)                 \
+  X(3, 8, 8, 3, 4)                 \
+  X(4, 8, 12, 3, 4)                \
+  X(5, 4, 3, 3, 4)                 \
+  X(6, 4, 3, 4, 4)                 \
+  X(7, 4, 3, 6, 4)                 \
+  X(8, 2, 3, 4, 2)                 \
+  X(9, 2, 3, 6, 2)                 \
+  X(10, 4, 3, 6, 2)                \
+  X(11, 3, 3, 4, 3)                \
+  X(12, 3, 3, 6, 3)
 
 template <int DT>
 hipError_t launch_shrink_lds_dt(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st) {
   const int NB = (a.R + 15) / 16;
   const int nblk = a.S * NB;
   switch (plan.variant) {
-#define X(V, BMG, NCB, NS)                                                                   \
+#define X(V, BMG, NCB, NS, NW)                                                               \
     case V:                                                                                  \
-      hipLaunchKernelGGL((shrink_lds_kernel<DT, BMG, NCB, NS>),                             \
-                         dim3(plan.grid_x, (nblk + NCB - 1) / NCB), dim3(256), 0, st, a);     \
+      hipLaunchKernelGGL((shrink_lds_kernel<DT, BMG, NCB, NS, NW>),                         \
+                         dim3(plan.grid_x, (nblk + NCB - 1) / NCB), dim3(NW * 64), 0, st, a); \
       return hipGetLastError();
     LMX_SHRINK_LDS_VARIANTS(X)
 #undef X

@@ -174,7 +174,7 @@ typedef struct lora_plan {
 } lora_plan;
 
 #define LORA_SHRINK_RING_SHAPES 5
-#define LORA_SHRINK_LDS_SHAPES 5
+#define LORA_SHRINK_LDS_SHAPES 13
 #define LORA_EXPAND_SHAPES 10
 
 /* lora_shrink with an explicit plan (NULL: as lora_shrink); the workspace query must be made

@@ -106,7 +106,8 @@ def test_workspace_sizes():
     for dt in (1, 2):
         assert _lib.lora_shrink_workspace_size_ex(dt, 50, 4096, 3, 16, 4, plan) == 32768 + 33 * 50 * 48 * 4
     # a plan outside its ranges is refused
-    assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, P(shrink_shape=5)) == 0
+    assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, P(shrink_shape=13)) == 0
+    assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, P(shrink_kernel=0, shrink_shape=5)) == 0
     assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, P(shrink_finish=2)) == 0
     assert _lib.lora_shrink_workspace_size_ex(1, 50, 4096, 3, 16, 4, None) == \
         _lib.lora_shrink_workspace_size(1, 50, 4096, 3, 16, 4)
