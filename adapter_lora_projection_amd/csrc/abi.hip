@@ -362,84 +362,64 @@ lora_status mlp_forward(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32
                         const void* b_down, void* out, int64_t ldo, void* e_save, void* v_save,
                         int64_t lde, void* workspace, size_t workspace_bytes, void* stream);
 
-// Workspace of the LoRA MLP backward: byte offsets of the transposed / scaled LoRA operands, the
-// recomputed LoRA-A products, the gradient intermediates and the partial sums.
+// Workspace of the LoRA MLP backward: byte offsets of the scaled / padded / transposed LoRA
+// operands, the LoRA-A products and their gradients, the gradient intermediates and the partial
+// sums.
 struct MlpBwdLayout {
   int64_t rp;
-  ShrinkWs s_x, r_x;   // [xa_g | xa_u] from x (plans for aligned / unaligned A)
-  ShrinkWs s_w;        // products against operands in the workspace (always aligned): K = H
-  ShrinkWs s_i, r_i;   // products over K = I (xa_d from hmid; dxa_g, dxa_u from de, dv)
-  lmx::ColJobs cj;     // geometry of the sums over tokens (pointers set at call time)
-  size_t sbdt, sbgt, sbut, adt, agut, xa_gu, dxa_d, xa_d, dxa_gu, hmid, dedv, part, colpart, total;
+  lmx::SumJobs in;     // LoRA-A products of x and dout (sums over columns; pointers set per call)
+  lmx::SumJobs both;   // one pass over de, dv, hmid: sums over columns and over tokens
+  lmx::SumJobs cols;   // sums over tokens of x and dout
+  size_t sbdt, sbgt, sbut, adt, adp, agp, aup, agut, xa_gu, dxa_d, xa_d, dxa_gu, hmid, dedv,
+      rowpart, colpart, total;
 };
 
-lmx::ColJobs mlp_bwd_coljobs(int64_t M, int64_t H, int64_t I, int32_t r) {
-  lmx::ColJobs j{};
-  j.n = 6;
-  j.M = int(M);
-  const int64_t C[6] = {H, H, I, I, I, H};
-  int64_t blocks = 0;
-  for (int q = 0; q < 6; ++q) {
-    j.job[q].C = int(C[q]);
-    j.job[q].nq = r;
-    blocks += cdiv(C[q], 1024);
-  }
-  const int64_t jb = cdiv(r, 16);
-  // about 512 workgroups, chunks of at least 64 rows
-  j.chunks = int(std::max<int64_t>(1, std::min<int64_t>(cdiv(512, blocks * jb), M / 64)));
-  return j;
-}
+#ifndef LMX_SUMS_COLS_TARGET
+#define LMX_SUMS_COLS_TARGET 256
+#endif
 
 MlpBwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
-  const Knobs kn;
   MlpBwdLayout L{};
   L.rp = cdiv(r, 32) * 32;
   const int rp = int(L.rp);
-  L.s_x = shrink_ws(kn, LORA_BF16, M, H, 2, rp, 0, prefer_lds(kn, M, H, 2, rp), false);
-  L.r_x = shrink_ws(kn, LORA_BF16, M, H, 2, rp, 0, false, false);
-  L.s_w = shrink_ws(kn, LORA_BF16, M, H, 1, rp, 0, prefer_lds(kn, M, H, 1, rp), false);
-  L.s_i = shrink_ws(kn, LORA_BF16, M, I, 1, rp, 0, prefer_lds(kn, M, I, 1, rp), false);
-  L.r_i = shrink_ws(kn, LORA_BF16, M, I, 1, rp, 0, false, false);
-  L.cj = mlp_bwd_coljobs(M, H, I, r);
+  const int JB = int(cdiv(r, 16));
+  int64_t rf[3] = {0, 0, 0}, cf[3] = {0, 0, 0};
+  auto init = [&](lmx::SumJobs& j, int n) { j.n = n; j.M = int(M); j.JB = JB; };
+  auto job = [](lmx::SumJob& j, int64_t C, int nr, int nh) { j.C = int(C); j.nr = nr; j.nh = nh; };
+  // Two workgroups per compute unit (their LDS allows two) where the partials are a small part
+  // of the bytes read; one per compute unit for the sums over tokens of x and dout alone, whose
+  // row chunks each add nh x 64 bytes of partials per column, so the chunks stay long.
+  init(L.in, 2);
+  job(L.in.job[0], H, 2, 0);  // x: xa_g, xa_u
+  job(L.in.job[1], H, 1, 0);  // dout: dxa_d
+  lmx::plan_sums(L.in, 512, &rf[0], &cf[0]);
+  init(L.both, 3);
+  for (int q = 0; q < 3; ++q) job(L.both.job[q], I, 1, 1);  // de, dv, hmid
+  lmx::plan_sums(L.both, 512, &rf[1], &cf[1]);
+  init(L.cols, 2);
+  job(L.cols.job[0], H, 0, 2);  // x: dA_g, dA_u
+  job(L.cols.job[1], H, 0, 1);  // dout: dB_d
+  lmx::plan_sums(L.cols, LMX_SUMS_COLS_TARGET, &rf[2], &cf[2]);
   size_t off = 0;
-  L.sbdt = off; off += align256(size_t(r) * H * 2);
-  L.sbgt = off; off += align256(size_t(r) * I * 2);
-  L.sbut = off; off += align256(size_t(r) * I * 2);
-  L.adt = off; off += align256(size_t(I) * L.rp * 2);
-  L.agut = off; off += align256(size_t(H) * 2 * L.rp * 2);
-  L.xa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
-  L.dxa_d = off; off += align256(size_t(M) * L.rp * 2);
-  L.xa_d = off; off += align256(size_t(M) * L.rp * 2);
-  L.dxa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
-  L.hmid = off; off += align256(size_t(M) * I * 2);
-  L.dedv = off; off += align256(size_t(M) * 2 * I * 2);
-  size_t sp = 0;
-  for (const ShrinkWs* w : {&L.s_x, &L.r_x, &L.s_w, &L.s_i, &L.r_i}) sp = std::max(sp, part_bytes(*w));
-  L.part = off; off += align256(sp);
-  L.colpart = off; off += align256(lmx::colred_partial_floats(L.cj) * 4);
+  auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
+  L.sbdt = take(size_t(rp) * H * 2);
+  L.sbgt = take(size_t(rp) * I * 2);
+  L.sbut = take(size_t(rp) * I * 2);
+  L.adt = take(size_t(I) * rp * 2);
+  L.adp = take(size_t(rp) * I * 2);
+  L.agp = take(size_t(rp) * H * 2);
+  L.aup = take(size_t(rp) * H * 2);
+  L.agut = take(size_t(H) * 2 * rp * 2);
+  L.xa_gu = take(size_t(M) * 2 * rp * 2);
+  L.dxa_d = take(size_t(M) * rp * 2);
+  L.xa_d = take(size_t(M) * rp * 2);
+  L.dxa_gu = take(size_t(M) * 2 * rp * 2);
+  L.hmid = take(size_t(M) * I * 2);
+  L.dedv = take(size_t(M) * 2 * I * 2);
+  L.rowpart = take(size_t(std::max({rf[0], rf[1], rf[2]})) * 4);
+  L.colpart = take(size_t(std::max({cf[0], cf[1], cf[2]})) * 4);
   L.total = off;
   return L;
-}
-
-// One dense LoRA-A product h = round(x A^T) (one segment; S slices of padded rank rp, true rank
-// r): the LDS-staged plan when A is aligned, else the register-ring plan.
-hipError_t dense_shrink(const void* x, int64_t ldx, int64_t K, int S, const void* const* A,
-                        int64_t lda, int64_t M, int rp, int r, void* h, int64_t ldh,
-                        const ShrinkWs& s_al, const ShrinkWs& s_un, void* part, hipStream_t st) {
-  bool al = true;
-  for (int q = 0; q < S; ++q) al = al && al16(A[q]);
-  const ShrinkWs& sp = al ? s_al : s_un;
-  lmx::ShrinkArgs a{};
-  a.x = x; a.ldx = ldx; a.K = K; a.S = S; a.R = rp; a.G = 1; a.T = int(M);
-  a.dense_rank = r; a.w_a = A[0]; a.lda = lda;
-  for (int q = 0; q < S; ++q) a.w_a_slice[q] = A[q];
-  a.h = h; a.ldh = ldh;
-  a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp; a.sk_unit = sp.unit;
-  a.part = static_cast<float*>(part);
-  lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
-  hipError_t e = lmx::launch_shrink(LORA_BF16, a, plan, st);
-  if (e == hipSuccess && sp.q > 0) e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st);
-  return e;
 }
 
 // The shared body of lora_linear_fused (P = 1) and lora_qkv_fused (P = 3).
@@ -938,33 +918,56 @@ lora_status lora_mlp_backward(lora_dtype dtype, int64_t M, int64_t H, int64_t I,
   const int rp = int(L.rp);
   uint16_t *sbdt = W(L.sbdt), *sbgt = W(L.sbgt), *sbut = W(L.sbut), *adt = W(L.adt);
   uint16_t *agut = W(L.agut), *xa_gu = W(L.xa_gu), *dxa_d = W(L.dxa_d), *xa_d = W(L.xa_d);
-  uint16_t *dxa_gu = W(L.dxa_gu), *hmid = W(L.hmid), *dedv = W(L.dedv);
-  void* part = ws + L.part;
-  // 1. operands: s B_d^T [r][H], s B_g^T, s B_u^T [r][I]; A_d^T [I][rp]; [A_g^T | A_u^T] [H][2 rp]
+  uint16_t *dxa_gu = W(L.dxa_gu), *hmid = W(L.hmid), *dedv = W(L.dedv), *adp = W(L.adp);
+  uint16_t *agp = W(L.agp), *aup = W(L.aup);
+  float* rowpart = reinterpret_cast<float*>(ws + L.rowpart);
+  float* colpart = reinterpret_cast<float*>(ws + L.colpart);
+  auto sum_job = [](lmx::SumJob& j, const uint16_t* P, int64_t ldp, const uint16_t* R0,
+                    const uint16_t* R1, const uint16_t* Q0, const uint16_t* Q1, int64_t ldq) {
+    j.P = P; j.ldp = ldp; j.R[0] = R0; j.R[1] = R1; j.ldr = j.C;
+    j.Q[0] = Q0; j.Q[1] = Q1; j.ldq = ldq;
+  };
+  auto red_job = [](lmx::RedJob& j, const float* src, int64_t pstride, int np, void* out,
+                    int64_t osa, int64_t osj, int A, int J, int r, float sc) {
+    j.src = src; j.pstride = pstride; j.np = np; j.out = static_cast<uint16_t*>(out);
+    j.osa = osa; j.osj = osj; j.A = A; j.J = J; j.r = r; j.scale = sc;
+  };
+  const int JB = L.both.JB;
+  auto ncb = [](const lmx::SumJobs& j, int q) { return j.blk0[q + 1] - j.blk0[q]; };
+  // 1. operands, rank rows past r zero: s B_d^T [rp][H]; s B_g^T, s B_u^T, A_d [rp][I];
+  //    A_g, A_u [rp][H]; A_d^T [I][rp]; [A_g^T | A_u^T] [H][2 rp]
   {
     lmx::TJobs t{};
-    t.n = 6;
-    t.job[0] = {u16(b_down), r, sbdt, H, r, int(H), 0, int(H), scale};
-    t.job[1] = {u16(b_gate), r, sbgt, I, r, int(I), 0, int(I), scale};
-    t.job[2] = {u16(b_up), r, sbut, I, r, int(I), 0, int(I), scale};
-    t.job[3] = {u16(a_down), I, adt, rp, int(I), rp, 0, r, 1.0f};
-    t.job[4] = {u16(a_gate), H, agut, 2 * rp, int(H), rp, 0, r, 1.0f};
-    t.job[5] = {u16(a_up), H, agut + rp, 2 * rp, int(H), rp, 0, r, 1.0f};
+    t.n = 9;
+    t.job[0] = {u16(b_down), r, sbdt, H, rp, int(H), 0, int(H), r, scale, false};
+    t.job[1] = {u16(b_gate), r, sbgt, I, rp, int(I), 0, int(I), r, scale, false};
+    t.job[2] = {u16(b_up), r, sbut, I, rp, int(I), 0, int(I), r, scale, false};
+    t.job[3] = {u16(a_down), I, adt, rp, int(I), rp, 0, r, int(I), 1.0f, false};
+    t.job[4] = {u16(a_gate), H, agut, 2 * rp, int(H), rp, 0, r, int(H), 1.0f, false};
+    t.job[5] = {u16(a_up), H, agut + rp, 2 * rp, int(H), rp, 0, r, int(H), 1.0f, false};
+    t.job[6] = {u16(a_down), I, adp, I, rp, int(I), 0, int(I), r, 1.0f, true};
+    t.job[7] = {u16(a_gate), H, agp, H, rp, int(H), 0, int(H), r, 1.0f, true};
+    t.job[8] = {u16(a_up), H, aup, H, rp, int(H), 0, int(H), r, 1.0f, true};
     if (lmx::launch_small_transposes(t, st) != hipSuccess) return LORA_EHIP;
   }
-  // 2. [xa_g | xa_u] = round(x [A_g; A_u]^T)
+  // 2. [xa_g | xa_u] = round(x [A_g; A_u]^T) and dxa_d = round(dout (s B_d)): sums over the
+  //    columns of x and dout, then their fixed-order reduction (with the rank padding zeroed)
   {
-    const void* A[2] = {a_gate, a_up};
-    if (dense_shrink(x, ldx, H, 2, A, H, M, rp, r, xa_gu, 2 * rp, L.s_x, L.r_x, part, st) != hipSuccess)
-      return LORA_EHIP;
+    lmx::SumJobs j = L.in;
+    sum_job(j.job[0], u16(x), ldx, agp, aup, nullptr, nullptr, 0);
+    sum_job(j.job[1], u16(dout), lddo, sbdt, nullptr, nullptr, nullptr, 0);
+    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+    const int64_t rs = M * JB * 16;
+    const int nx = ncb(j, 0), nd = ncb(j, 1);
+    lmx::RedJobs rj{};
+    rj.n = 3;
+    rj.JB = JB;
+    red_job(rj.job[0], rowpart + j.job[0].rp0, rs, nx, xa_gu, 2 * rp, 1, int(M), rp, r, 1.0f);
+    red_job(rj.job[1], rowpart + j.job[0].rp0 + nx * rs, rs, nx, xa_gu + rp, 2 * rp, 1, int(M), rp, r, 1.0f);
+    red_job(rj.job[2], rowpart + j.job[1].rp0, rs, nd, dxa_d, rp, 1, int(M), rp, r, 1.0f);
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
   }
-  // 3. dxa_d = round(dout (s B_d))
-  {
-    const void* A[1] = {sbdt};
-    if (dense_shrink(dout, lddo, H, 1, A, H, M, rp, r, dxa_d, rp, L.s_w, L.s_w, part, st) != hipSuccess)
-      return LORA_EHIP;
-  }
-  // 4. dhmid = dout W_d + dxa_d A_d with the SwiGLU backward in the epilogue:
+  // 3. dhmid = dout W_d + dxa_d A_d with the SwiGLU backward in the epilogue:
   //    hmid = round(silu(e) v), de = round(dhmid v silu'(e)), dv = round(dhmid silu(e))
   {
     lmx::GemmArgs g{};
@@ -976,39 +979,45 @@ lora_status lora_mlp_backward(lora_dtype dtype, int64_t M, int64_t H, int64_t I,
     g.M = int(M); g.N = int(I); g.K = int(H); g.K2 = rp;
     if (lmx::launch_gemm_lora(g, lmx::kGemmSwigluBwd, st) != hipSuccess) return LORA_EHIP;
   }
-  // 5. xa_d = round(hmid A_d^T)
+  // 4. one pass over de, dv and hmid: the LoRA-A products of the next layer down the chain
+  //    (dxa_g = de (s B_g), dxa_u = dv (s B_u), xa_d = hmid A_d^T: sums over columns) and the
+  //    weight-gradient sums over tokens (dB_g = s de^T xa_g, dB_u = s dv^T xa_u,
+  //    dA_d = dxa_d^T hmid), then their fixed-order reduction
   {
-    const void* A[1] = {a_down};
-    if (dense_shrink(hmid, I, I, 1, A, I, M, rp, r, xa_d, rp, L.s_i, L.r_i, part, st) != hipSuccess)
-      return LORA_EHIP;
+    lmx::SumJobs j = L.both;
+    sum_job(j.job[0], dedv, 2 * I, sbgt, nullptr, xa_gu, nullptr, 2 * rp);
+    sum_job(j.job[1], dedv + I, 2 * I, sbut, nullptr, xa_gu + rp, nullptr, 2 * rp);
+    sum_job(j.job[2], hmid, I, adp, nullptr, dxa_d, nullptr, rp);
+    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+    const int nc = ncb(j, 0);
+    const int64_t rstride = M * JB * 16, cstride = I * JB * 16;
+    lmx::RedJobs rj{};
+    rj.n = 6;
+    rj.JB = JB;
+    red_job(rj.job[0], rowpart + j.job[0].rp0, rstride, nc, dxa_gu, 2 * rp, 1, int(M), rp, r, 1.0f);
+    red_job(rj.job[1], rowpart + j.job[1].rp0, rstride, nc, dxa_gu + rp, 2 * rp, 1, int(M), rp, r, 1.0f);
+    red_job(rj.job[2], rowpart + j.job[2].rp0, rstride, nc, xa_d, rp, 1, int(M), rp, r, 1.0f);
+    red_job(rj.job[3], colpart + j.job[0].cp0, cstride, j.chunks, db_gate, r, 1, int(I), r, r, scale);
+    red_job(rj.job[4], colpart + j.job[1].cp0, cstride, j.chunks, db_up, r, 1, int(I), r, r, scale);
+    red_job(rj.job[5], colpart + j.job[2].cp0, cstride, j.chunks, da_down, 1, I, int(I), r, r, 1.0f);
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
   }
-  // 6. dxa_g = round(de (s B_g)), dxa_u = round(dv (s B_u))
+  // 5. sums over tokens of x and dout: dA_g = dxa_g^T x, dA_u = dxa_u^T x, dB_d = s dout^T xa_d
   {
-    const void* Ag[1] = {sbgt};
-    const void* Au[1] = {sbut};
-    if (dense_shrink(dedv, 2 * I, I, 1, Ag, I, M, rp, r, dxa_gu, 2 * rp, L.s_i, L.s_i, part, st) != hipSuccess ||
-        dense_shrink(dedv + I, 2 * I, I, 1, Au, I, M, rp, r, dxa_gu + rp, 2 * rp, L.s_i, L.s_i, part, st) != hipSuccess)
-      return LORA_EHIP;
+    lmx::SumJobs j = L.cols;
+    sum_job(j.job[0], u16(x), ldx, nullptr, nullptr, dxa_gu, dxa_gu + rp, 2 * rp);
+    sum_job(j.job[1], u16(dout), lddo, nullptr, nullptr, xa_d, nullptr, rp);
+    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+    const int64_t cstride = H * JB * 16, hstride = int64_t(j.chunks) * cstride;
+    lmx::RedJobs rj{};
+    rj.n = 3;
+    rj.JB = JB;
+    red_job(rj.job[0], colpart + j.job[0].cp0, cstride, j.chunks, da_gate, 1, H, int(H), r, r, 1.0f);
+    red_job(rj.job[1], colpart + j.job[0].cp0 + hstride, cstride, j.chunks, da_up, 1, H, int(H), r, r, 1.0f);
+    red_job(rj.job[2], colpart + j.job[1].cp0, cstride, j.chunks, db_down, r, 1, int(H), r, r, scale);
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
   }
-  // 7. LoRA weight gradients (sums over the M tokens)
-  {
-    lmx::ColJobs j = L.cj;
-    auto set = [&](int q, const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, void* out,
-                   int64_t osc, int64_t osj, float sc) {
-      j.job[q].P = P; j.job[q].ldp = ldp; j.job[q].Q = Q; j.job[q].ldq = ldq;
-      j.job[q].out = static_cast<uint16_t*>(out); j.job[q].osc = osc; j.job[q].osj = osj;
-      j.job[q].scale = sc;
-    };
-    set(0, u16(x), ldx, dxa_gu, 2 * rp, da_gate, 1, H, 1.0f);          // dA_g = dxa_g^T x
-    set(1, u16(x), ldx, dxa_gu + rp, 2 * rp, da_up, 1, H, 1.0f);       // dA_u = dxa_u^T x
-    set(2, dedv, 2 * I, xa_gu, 2 * rp, db_gate, r, 1, scale);          // dB_g = s de^T xa_g
-    set(3, dedv + I, 2 * I, xa_gu + rp, 2 * rp, db_up, r, 1, scale);   // dB_u = s dv^T xa_u
-    set(4, hmid, I, dxa_d, rp, da_down, 1, I, 1.0f);                   // dA_d = dxa_d^T hmid
-    set(5, u16(dout), lddo, xa_d, rp, db_down, r, 1, scale);           // dB_d = s dout^T xa_d
-    if (lmx::launch_colred(j, reinterpret_cast<float*>(ws + L.colpart), st) != hipSuccess)
-      return LORA_EHIP;
-  }
-  // 8. dx = round(de W_g + dv W_u + dxa_g A_g + dxa_u A_u)
+  // 6. dx = round(de W_g + dv W_u + dxa_g A_g + dxa_u A_u)
   {
     lmx::GemmArgs g{};
     g.A = dedv; g.lda = 2 * I; g.W0 = u16(w_gu_t); g.W1 = u16(w_gu_t); g.ldw = 2 * I;

@@ -67,19 +67,22 @@ struct ScaleJobs {
 // The three scaled copies in one launch (same scale and rank).
 hipError_t launch_scale_lora_b(const ScaleJobs& jobs, float scale, int r, hipStream_t st);
 
-// Transposed, scaled, zero-padded copies of small LoRA operands, up to 6 in one launch:
-// dst[i][c] = round(scale * src[c - c0][i]) for c0 <= c < c0 + cn, else 0, for i < rows,
-// c < cols (bf16).
+// Small LoRA operand copies, up to 10 in one launch, bf16, for i < rows and c < cols:
+//   transposed (plain = false): dst[i][c] = round(scale * src[c - c0][i]) for c0 <= c < c0 + cn
+//   and i < rv, else 0;
+//   row copy (plain = true):    dst[i][c] = round(scale * src[i][c - c0]) under the same bounds.
+// (lds is the source row pitch in both forms.)
 struct TJob {
   const uint16_t* src;
   int64_t lds;
   uint16_t* dst;
   int64_t ldd;
-  int rows, cols, c0, cn;
+  int rows, cols, c0, cn, rv;
   float scale;
+  bool plain;
 };
 struct TJobs {
-  TJob job[6];
+  TJob job[10];
   int n;
 };
 hipError_t launch_small_transposes(const TJobs& jobs, hipStream_t st);
@@ -88,25 +91,50 @@ hipError_t launch_small_transposes(const TJobs& jobs, hipStream_t st);
 hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int rows,
                             int cols, hipStream_t st);
 
-// Sums over tokens for the LoRA weight gradients, up to 6 in one pass:
-// out[c * osc + j * osj] = round(scale * sum_m P[m][c] * Q[m][j]) for c < C, j < nq,
-// computed as fp32 partial sums over row chunks (part, chunks x ceil(nq/16) x C x 16 floats per
-// job) and a fixed-order reduction. C is a multiple of 4; P rows 8-byte aligned.
-struct ColJob {
+// Sums over one pass of a bf16 matrix P [M][C] (row pitch ldp), up to 4 matrices per launch, in
+// fp32:
+//   row side, R_h for h < nr <= 2:   Drow_h[m][j] = sum_c P[m][c] R_h[j][c]   (R_h [16 JB][C], pitch ldr)
+//   column side, Q_h for h < nh <= 2: Dcol_h[c][j] = sum_m P[m][c] Q_h[m][j]   (Q_h [M], pitch ldq)
+// for j < 16 JB, JB = the launch's rank blocks of 16; nr + nh >= 1. Results are partial sums:
+// the row side per block of 512 columns, rowpart + rp0 + h * (ncb * M * JB * 16):
+// [ncb = ceil(C / 512)][M][JB][16]; the column side per chunk of rows,
+// colpart + cp0 + h * (chunks * C * JB * 16): [chunks][C][JB][16]. C is a multiple of 32; P, R
+// and Q rows are 16-byte aligned and Q_h[m][16 jb .. 16 jb + 15] readable for every jb < JB.
+struct SumJob {
   const uint16_t* P;
   int64_t ldp;
-  const uint16_t* Q;
+  const uint16_t* R[2];
+  int64_t ldr;
+  const uint16_t* Q[2];
   int64_t ldq;
+  int C, nr, nh;
+  int64_t rp0, cp0;  // float offsets of the job's partials in rowpart / colpart
+};
+struct SumJobs {
+  SumJob job[4];
+  int n, M, JB, chunks, rows_per;
+  int blk0[5];  // first workgroup (grid x) of each job: ceil(C / 512) column blocks per job
+};
+// Chooses chunks / rows_per / blk0 and the partial offsets for about `target` workgroups;
+// returns the floats of (rowpart, colpart).
+void plan_sums(SumJobs& j, int target, int64_t* row_floats, int64_t* col_floats);
+hipError_t launch_sums(const SumJobs& jobs, float* rowpart, float* colpart, hipStream_t st);
+
+// Fixed-order reduction of partial planes into bf16 results, up to 6 outputs per launch:
+//   out[a * osa + j * osj] = round(scale * sum_{p < np} src[p * pstride + (a * JB) * 16 + j])
+// for a < A and j < r, and 0 for r <= j < J (zero padding of a rank-padded operand).
+struct RedJob {
+  const float* src;
+  int64_t pstride;
   uint16_t* out;
-  int64_t osc, osj;
-  int C, nq;
+  int64_t osa, osj;
+  int A, J, r, np;
   float scale;
 };
-struct ColJobs {
-  ColJob job[6];
-  int n, M, chunks;
+struct RedJobs {
+  RedJob job[6];
+  int n, JB;
 };
-size_t colred_partial_floats(const ColJobs& jobs);
-hipError_t launch_colred(const ColJobs& jobs, float* part, hipStream_t st);
+hipError_t launch_reduce_sums(const RedJobs& jobs, hipStream_t st);
 
 }  // namespace lmx
