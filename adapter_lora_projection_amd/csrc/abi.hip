@@ -481,25 +481,41 @@ lora_status linear_fused(lora_dtype dtype, int64_t M, int64_t K, const int64_t* 
       return LORA_EHIP;
   }
   // 3. out_p = round(x W_p^T + s xa_p B_p^T) with LoRA in K: one launch over the P column
-  //    groups (query, key and value share the pass over x and fill the chip together)
-  {
+  //    groups (query, key and value share the pass over x and fill the chip together), or the
+  //    first group alone and then the others when that finishes sooner (at M = 4096 the query
+  //    fills exactly one round of 256-row tiles and key + value one round of 128-row tiles,
+  //    where the single launch would leave a half-empty second round)
+  int first = 0;  // groups [0, first) go in a launch of their own
+  if (P > 1) {
+    int nb[3], all = 0, rest = 0;
+    for (int p = 0; p < P; ++p) { nb[p] = int(cdiv(N[p], 256)); all += nb[p]; }
+    rest = all - nb[0];
+    const double one = lmx::gemm_plain_cost(int(M), all, nullptr);
+    const double split = lmx::gemm_plain_cost(int(M), nb[0], nullptr) + lmx::gemm_plain_cost(int(M), rest, nullptr);
+    if (split + 0.05 < one) first = 1;
+  }
+  const int bounds[3] = {0, first, P};  // launch i covers groups [bounds[i], bounds[i + 1])
+  for (int li = first > 0 ? 0 : 1; li < 2; ++li) {
+    const int g0 = bounds[li], g1 = bounds[li + 1];
     lmx::GemmArgs g{};
-    g.A = u16(x); g.lda = ldx; g.W0 = u16(w[0]); g.W1 = u16(w[0]); g.ldw = K;
-    g.A2 = xa; g.lda2 = P * rp;
-    g.B2 = reinterpret_cast<const uint16_t*>(ws + L.lb[0]); g.ldb2 = rp;
-    g.C = static_cast<uint16_t*>(out[0]); g.ldc = ldo[0];
-    g.M = int(M); g.N = int(N[0]); g.K = int(K); g.K2 = int(rp);
-    if (P > 1) {
-      g.ngroups = P;
+    g.A = u16(x); g.lda = ldx; g.W0 = u16(w[g0]); g.W1 = u16(w[g0]); g.ldw = K;
+    g.A2 = xa + g0 * rp; g.lda2 = P * rp;
+    g.B2 = reinterpret_cast<const uint16_t*>(ws + L.lb[g0]); g.ldb2 = rp;
+    g.C = static_cast<uint16_t*>(out[g0]); g.ldc = ldo[g0];
+    g.M = int(M); g.N = int(N[g0]); g.K = int(K); g.K2 = int(rp);
+    if (g1 - g0 > 1) {
+      g.A2 = xa;
+      g.ngroups = g1 - g0;
       g.gblk[0] = 0;
-      for (int p = 0; p < P; ++p) {
-        g.gW[p] = u16(w[p]);
-        g.gB2[p] = reinterpret_cast<const uint16_t*>(ws + L.lb[p]);
-        g.ga2[p] = p * rp;
-        g.gC[p] = static_cast<uint16_t*>(out[p]);
-        g.gldc[p] = ldo[p];
-        g.gN[p] = int(N[p]);
-        g.gblk[p + 1] = g.gblk[p] + int(cdiv(N[p], 256));
+      for (int q = 0; q < g1 - g0; ++q) {
+        const int p = g0 + q;
+        g.gW[q] = u16(w[p]);
+        g.gB2[q] = reinterpret_cast<const uint16_t*>(ws + L.lb[p]);
+        g.ga2[q] = p * rp;
+        g.gC[q] = static_cast<uint16_t*>(out[p]);
+        g.gldc[q] = ldo[p];
+        g.gN[q] = int(N[p]);
+        g.gblk[q + 1] = g.gblk[q] + int(cdiv(N[p], 256));
       }
     }
     if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;

@@ -18,7 +18,8 @@
 //   4. LoRA-A product of hmid for down -> xa_d [M][rp];
 //   5. down GEMM over K = I + rp -> out.
 //
-// GEMM main loop: 256x256x32 block stages, 8 waves of 128x64, v_mfma_f32_32x32x16_bf16, both
+// GEMM main loop: 256x256x32 block stages (128x256 in the plain mode when shorter tiles finish
+// a launch sooner), 8 waves of 128x64 (64x64), v_mfma_f32_32x32x16_bf16, both
 // operands K-contiguous ([rows][K] row-major, as nn.Linear stores them) loaded straight into
 // LDS (global_load_lds_dwordx4) three stages deep, with XOR-swizzled 64-byte rows so 16-byte
 // fragment reads are bank-conflict free; fragment reads of the next k slice overlap the MFMAs.
@@ -35,14 +36,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int kBM = 256;  // rows of A per block
 constexpr int kBR = 256;  // rows of W per block (B operand)
 constexpr int kBK = 32;   // K per stage (64 bytes per row)
 #ifndef LMX_GEMM_STAGES
 #define LMX_GEMM_STAGES 3
 #endif
 constexpr int kStages = LMX_GEMM_STAGES;  // LDS buffers (more in flight per compute unit measured slower)
-constexpr int kStageElems = (kBM + kBR) * kBK;  // elements per stage (32 KiB)
 // Waves per 256 x 256 block: 8 (two per SIMD, each 128 x 64 or 128 gate + 128 up rows x 32)
 // measured 5% faster on the fused MLP, 7% on the attention projections and 9% on the backward
 // than 4 waves of 128 x 128 (one per SIMD, latency hidden by the software pipeline alone).
@@ -73,15 +72,20 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 
 }  // namespace
 
-template <int MODE, int NW>
+template <int MODE, int NW, int BM>
 __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
   constexpr bool SWIGLU = MODE == kGemmSwiglu || MODE == kGemmSwigluSave;
-  // NW waves in a 2 x (NW / 2) grid: each owns 128 rows and 256 / (NW / 2) of the block's
+  // NW waves in a 2 x (NW / 2) grid: each owns BM / 2 rows and 256 / (NW / 2) of the block's
   // B rows (for SwiGLU, matching gate and up halves so a lane holds g and u of one output).
   static_assert(NW == 4 || NW == 8, "wave grid");
+  static_assert(BM == 256 || (BM == 128 && MODE == kGemmPlain), "row tile");
   constexpr int WCOLS = NW / 2;
-  constexpr int RPW = 256 / NW;          // rows of A (and of W) each wave loads per stage
-  constexpr int LPW = RPW / 16;          // its 16-row load instructions per operand and stage
+  constexpr int RB = BM / 64;            // 32-row blocks of A per wave
+  constexpr int RPWA = BM / NW;          // rows of A each wave loads per stage
+  constexpr int LPWA = RPWA / 16;        // its 16-row load instructions per stage
+  constexpr int RPW = 256 / NW;          // rows of W each wave loads per stage
+  constexpr int LPW = RPW / 16;
+  constexpr int kStageElems = (BM + kBR) * kBK;  // elements per stage (32 KiB at BM = 256)
   constexpr int GCB = 4 / WCOLS;         // SwiGLU: gate (and up) 32-column blocks per wave
   constexpr int CBN = SWIGLU ? 2 * GCB : 8 / WCOLS;  // 32-column blocks per wave
   constexpr int NT = NW * 64;
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
   // by 4 out of the XCD's L2. Otherwise column blocks walk fastest inside groups of 8 row blocks.
   const bool grouped = MODE == kGemmPlain && p.ngroups > 1;  // uniform
   const int nbn = SWIGLU ? (p.N + 127) / 128 : (grouped ? p.gblk[p.ngroups] : (p.N + 255) / 256);
-  const int nbm = (p.M + kBM - 1) / kBM;
+  const int nbm = (p.M + BM - 1) / BM;
   int bm, bn;
   if (nbm % 16 == 0 && nbn % 16 == 0) {
     const int id = int(blockIdx.x);
@@ -138,10 +142,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
       }
     }
   }
-  const int m0 = bm * kBM;
+  const int m0 = bm * BM;
   const int n0 = SWIGLU ? bn * 128 : bn * 256;
 
-  // DMA mapping: wave w fills tile rows [RPW w, RPW w + RPW) of A and of W, 16 rows per
+  // DMA mapping: wave w fills tile rows [RPWA w, RPWA w + RPWA) of A and [RPW w, RPW w + RPW)
+  // of W, 16 rows per
   // instruction; lane L covers row 16 i + L / 4 and LDS slot L % 4, which holds global chunk
   // swz(row, slot). Stages past K read the LoRA columns (A2, B2).
   const int drow = lane >> 2, dslot = lane & 3;
@@ -160,13 +165,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
   // address each 16-row load group as a wave-uniform base plus one loop-invariant per-lane byte
   // offset: the lane's row inside the group (drow) and its swizzled chunk, which do not depend
   // on the group (row % 16 == drow and swz(row, c) only reads bits 2..3 of the row).
-  const bool full = m0 + kBM <= pM && n0 + (SWIGLU ? 128 : 256) <= pN;  // uniform
+  const bool full = m0 + BM <= pM && n0 + (SWIGLU ? 128 : 256) <= pN;  // uniform
   const int swb = swz(drow, dslot) * 16;
   const uint32_t voA = uint32_t(drow * plda * 2 + swb), voW = uint32_t(drow * pldw * 2 + swb);
   const uint32_t voA2 = uint32_t(drow * plda2 * 2 + swb), voB2 = uint32_t(drow * pldb2 * 2 + swb);
   auto issue = [&](auto sc, int kt) {
     uint16_t* sa = stage(sc);
-    uint16_t* sb = sa + kBM * kBK;
+    uint16_t* sb = sa + BM * kBK;
     const bool lora = kt >= nk1;
     const int koff = (lora ? kt - nk1 : kt) * kBK;
     if (full) {
@@ -174,8 +179,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
       const int64_t lda = lora ? plda2 : plda;
       const uint32_t voa = lora ? voA2 : voA, vow = lora ? voB2 : voW;
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int g = w * RPW + i * 16;  // first row of the load group in the tile
+      for (int i = 0; i < LPWA; ++i) {
+        const int g = w * RPWA + i * 16;  // first row of the load group in the tile
         dma16_saddr(abase + int64_t(m0 + g) * lda * 2, voa, lds_addr(sa + g * kBK));
       }
 #pragma unroll
@@ -199,11 +204,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
     const uint16_t* abase = lora ? pA2 : pA;
     const int64_t lda = lora ? plda2 : plda;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int row = w * RPW + i * 16 + drow;
+    for (int i = 0; i < LPWA; ++i) {
+      const int row = w * RPWA + i * 16 + drow;
       const int kk = koff + swz(row, dslot) * 8;
       dma16(abase + int64_t(min(m0 + row, pM - 1)) * lda + kk,
-            lds_addr(sa + (w * RPW + i * 16) * kBK));
+            lds_addr(sa + (w * RPWA + i * 16) * kBK));
     }
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -232,9 +237,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
                        : wj * (256 / WCOLS) + cb * 32;
   const int lr = lane & 31, lc = lane >> 5;  // MFMA operand row and chunk-in-slice
 
-  f32x16_t acc[4][CBN];
+  f32x16_t acc[RB][CBN];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x16_t{};
 
@@ -242,14 +247,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
   // second 16-wide k slice while the MFMAs of the first run; then wait for stage kt+1's loads and
   // meet at the barrier (which also certifies every wave is done reading stage kt), refill stage
   // kt's buffer with stage kt+kStages, read stage kt+1's first slice and run the MFMAs of the second.
-  uint4 fa0[4], fb0[CBN], fa1[4], fb1[CBN];
+  uint4 fa0[RB], fb0[CBN], fa1[RB], fb1[CBN];
   auto read = [&](const uint16_t* sbase, int ks, uint4* fa, uint4* fb) {
     const uint16_t* sa = sbase;
-    const uint16_t* sb = sbase + kBM * kBK;
+    const uint16_t* sb = sbase + BM * kBK;
     const int chunk = ks * 2 + lc;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int row = wi * 128 + rb * 32 + lr;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = wi * (BM / 2) + rb * 32 + lr;
       fa[rb] = *reinterpret_cast<const uint4*>(sa + row * kBK + swz(row, chunk) * 8);
     }
 #pragma unroll
@@ -260,13 +265,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
   };
   auto mma_all = [&](const uint4* fa, const uint4* fb) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = mma32(fa[rb], fb[cb], acc[rb][cb]);
   };
-  // wait until at most `younger` stages of this wave's loads are outstanding (2 LPW loads per
-  // stage).
-  constexpr int LPS = 2 * LPW;
+  // wait until at most `younger` stages of this wave's loads are outstanding (LPWA + LPW loads
+  // per stage).
+  constexpr int LPS = LPWA + LPW;
   auto wait_stages = [&](int younger) {
     static_assert(kStages <= 5, "wait table");
     if (younger >= 4) vm_wait<4 * LPS>();
@@ -402,8 +407,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_lora_kernel(GemmArgs p) {
     }(std::make_integer_sequence<int, 4>{});
   } else {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int rbase = m0 + wi * 128 + rb * 32;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rbase = m0 + wi * (BM / 2) + rb * 32;
 #pragma unroll
       for (int cb = 0; cb < CBN; ++cb) {
         const int n = col_base + cb * 32 + lr;
@@ -449,22 +454,38 @@ hipError_t launch_scale_lora_b(const ScaleJobs& jobs, float scale, int r, hipStr
   return hipGetLastError();
 }
 
+// Plain-mode launch cost in units of one round of 256-row tiles over the chip's 256 compute
+// units: ceil(workgroups / 256) rounds of 256-row tiles, or rounds of 128-row tiles at 0.66 of
+// that (their measured time per tile at the q/k/v projection shapes).
+double gemm_plain_cost(int M, int nbn, bool* half) {
+  const int64_t wg256 = int64_t((M + 255) / 256) * nbn, wg128 = int64_t((M + 127) / 128) * nbn;
+  const double c256 = double((wg256 + 255) / 256), c128 = 0.66 * double((wg128 + 255) / 256);
+  if (half) *half = c128 < c256;
+  return c128 < c256 ? c128 : c256;
+}
+
 hipError_t launch_gemm_lora(const GemmArgs& a, int mode, hipStream_t st) {
   const bool swiglu = mode == kGemmSwiglu || mode == kGemmSwigluSave;
-  const int nbm = (a.M + kBM - 1) / kBM;
   const int nbn = swiglu ? (a.N + 127) / 128
                          : (mode == kGemmPlain && a.ngroups > 1 ? a.gblk[a.ngroups] : (a.N + 255) / 256);
-  dim3 grid(nbm * nbn);
+  // plain mode: 128-row tiles where they finish the launch sooner (more, shorter tiles fill the
+  // last round of workgroups)
+  bool half = false;
+  if (mode == kGemmPlain) gemm_plain_cost(a.M, nbn, &half);
+  dim3 grid(unsigned(int64_t(half ? (a.M + 127) / 128 : (a.M + 255) / 256) * nbn));
   constexpr int W = kGemmWaves;
   dim3 block(64 * W);
   switch (mode) {
-    case kGemmPlain: hipLaunchKernelGGL((gemm_lora_kernel<kGemmPlain, W>), grid, block, 0, st, a); break;
-    case kGemmSwiglu: hipLaunchKernelGGL((gemm_lora_kernel<kGemmSwiglu, W>), grid, block, 0, st, a); break;
+    case kGemmPlain:
+      if (half) hipLaunchKernelGGL((gemm_lora_kernel<kGemmPlain, W, 128>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((gemm_lora_kernel<kGemmPlain, W, 256>), grid, block, 0, st, a);
+      break;
+    case kGemmSwiglu: hipLaunchKernelGGL((gemm_lora_kernel<kGemmSwiglu, W, 256>), grid, block, 0, st, a); break;
     case kGemmSwigluSave:
-      hipLaunchKernelGGL((gemm_lora_kernel<kGemmSwigluSave, W>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_lora_kernel<kGemmSwigluSave, W, 256>), grid, block, 0, st, a);
       break;
     case kGemmSwigluBwd:
-      hipLaunchKernelGGL((gemm_lora_kernel<kGemmSwigluBwd, W>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_lora_kernel<kGemmSwigluBwd, W, 256>), grid, block, 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }

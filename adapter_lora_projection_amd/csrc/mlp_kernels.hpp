@@ -50,6 +50,9 @@ struct GemmArgs {
 enum GemmMode { kGemmPlain = 0, kGemmSwiglu = 1, kGemmSwigluSave = 2, kGemmSwigluBwd = 3 };
 
 hipError_t launch_gemm_lora(const GemmArgs& a, int mode, hipStream_t st);
+// Estimated time of a plain-mode launch over M rows and nbn 256-column blocks, in rounds of
+// 256-row tiles; *half (if given) tells whether the launch takes 128-row tiles.
+double gemm_plain_cost(int M, int nbn, bool* half = nullptr);
 
 // One scaled copy: dst[i][col0 + j] = round(scale * src[i][j]) for j < r, rows i < n; every
 // other column of the dst rows [0, ld_dst) is written as 0.

@@ -27,6 +27,7 @@ def _dev(c):
     (257, 512, 288, 40, 33, 1.5),      # rank padded to 64, non-power-of-two scale
     (1, 32, 32, 32, 1, 4.0),
     (512, 256, 512, 256, 64, 0.5),
+    (650, 256, 7680, 1280, 16, 4.0),   # 40 column blocks: the 128-row tiles fill the chip better
 ])
 def test_qkv_and_o_small(M, H, Nq, Nkv, r, scale):
     alp = __import__("adapter_lora_projection_amd")
@@ -71,3 +72,18 @@ def test_qwen3_8b_attention_projections_sampled():
                                     ("v", v, c.w_v, c.a_v, c.b_v, c.x), ("o", o, c.w_o, c.a_o, c.b_o, q.cpu())):
         ref = oracle.lora_linear_rows(rows, xin, w, a, b, c.scale, "bf16")
         assert_close_lowp(got.cpu()[rows], ref, f"{name} sampled rows")
+
+
+def test_linear_128_row_tiles_ragged():
+    """One projection whose 256-row tiles would fill under half of the chip's workgroup slots
+    (3 x 40 blocks), so the launch takes 128-row tiles; M = 650 leaves a ragged last tile."""
+    alp = __import__("adapter_lora_projection_amd")
+    c = li.config_qkv(seed=71, M=650, H=256, Nq=7680, Nkv=1280, r=16, scale=2.0)
+    d = _dev(c)
+    w = torch.cat([d["w_q"], d["w_k"], d["w_v"]]).contiguous()
+    b = torch.cat([d["b_q"], d["b_k"], d["b_v"]]).contiguous()
+    y = alp.linear_fused(d["x"], w, d["a_q"], b, c.scale)
+    torch.cuda.synchronize()
+    ref = oracle.lora_linear(c.x, torch.cat([c.w_q, c.w_k, c.w_v]), c.a_q,
+                             torch.cat([c.b_q, c.b_k, c.b_v]), c.scale, "bf16")
+    assert_close_lowp(y.cpu(), ref, "linear with 128-row tiles")
