@@ -171,12 +171,14 @@ int shrink_lds_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t
   if (pub && nblk == 3) {
     // Three column blocks (rank 16 over three slices, the decode projections): the shortest
     // tiles whose grid fits in one round of 256 workgroups. Kernel durations on the decode
-    // sweep (rocprofv3, each call after a 512 MiB read): 32-position tiles, 2 waves, 4 stages
-    // 21.3 / 21.5 / 21.8 us at 2048 / 4096 / 6144 tokens; at 8192 (260 such tiles) 48-position
-    // tiles, 3 waves, 6 stages 23.5 us, against 26.1 us for 64-position and 39 us for
-    // 128-position tiles. Shorter tiles re-read the A rows from the L2 more often but keep more
-    // compute units streaming x.
-    for (int v : {8, 12, 7})
+    // sweep (rocprofv3, each call after a 512 MiB device write, so the caches hold dirty lines
+    // as after the expand that precedes a shrink): 32-position tiles, 2 waves, 6 stages
+    // 22.6 / 23.5 / 26.4 us at 2048 / 4096 / 6144 tokens (4 stages: 24.1 / 26.2 / 28.1; 8
+    // stages no better); at 8192 (260 such tiles) 48-position tiles, 3 waves, 6 stages 32.1 us,
+    // against 35.9 us for 64-position tiles (after a 512 MiB read instead: 23.5 and 26.1 us,
+    // 39 us for 128-position tiles). Shorter tiles re-read the A rows from the L2 more often
+    // but keep more compute units streaming x.
+    for (int v : {9, 12, 7})
       if (cdiv(T, lmx::shrink_lds_bm(v)) + G <= 256) return v;
     return 1;
   }

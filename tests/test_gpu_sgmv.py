@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import lora_inputs as li
+from adapter_lora_projection_amd import _lib
 import oracle
 from tests.parity import assert_close_lowp, check_h, check_y, f64, to_dev
 
@@ -175,14 +176,14 @@ def test_shared_work_split(wgs, dtype, finish):
 
 @pytest.mark.parametrize("finish", [0, 1])
 @pytest.mark.parametrize("wgs", [0, 5, 300])
-@pytest.mark.parametrize("sv", range(13))
+@pytest.mark.parametrize("sv", range(_lib.LORA_SHRINK_LDS_SHAPES))
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_lds_shrink_shapes(sv, wgs, dtype, finish):
     """The LDS-staged shrink in every shape (2..12 column blocks per workgroup, so the 6 blocks
-    here are split over 3, 2, 2, 1 and 1 workgroups; tiles of 128 or 64 positions; 3 or 4
-    stages), one workgroup per tile or the work shared over 5 or 300 workgroups (pieces added by
-    a second launch or in the same launch); K = 1032 ends in a stage with one valid 8-element
-    chunk; ragged tile ends; rank 0, 1, 7, 17 and 32 adapters."""
+    here are split over 3, 2, 2, 1 and 1 workgroups; tiles of 128, 64, 48 or 32 positions; 3 to 6
+    stages; 2 to 4 waves), one workgroup per tile or the work shared over 5 or 300 workgroups
+    (pieces added by a second launch or in the same launch); K = 1032 ends in a stage with one
+    valid 8-element chunk; ragged tile ends; rank 0, 1, 7, 17 and 32 adapters."""
     c = li.make_sgmv(f"lds_{dtype}", seed=44, T=301, K=1032, S=3, R=32, L=5,
                      slice_offsets=[0, 130, 131, 333], dtype=dtype, ranks=[32, 7, 1, 0, 17])
     print("case", c.name, sv, wgs, finish, flush=True)
