@@ -3,9 +3,11 @@
 Tolerances (stated by the workload definition and restated here):
 * bf16 / fp16 outputs: |gpu - ref| <= 1e-2 + 1e-2 * |ref|, where ref is the oracle value rounded
   once to the storage type.
-* fp32 outputs: |gpu - oracle| <= 1e-5 * M per element, where M is the magnitude the sum is
-  conditioned on (sum of |terms|, plus |y_in| for expand), computed by the oracle on absolute
-  values; this equals 1e-5 * |oracle| when nothing cancels.
+* fp32 outputs: |gpu - oracle| <= 1e-5 * |oracle| per element, relaxed to 1e-5 * M only where
+  the sum cancels (|oracle| < M / 2), M being the magnitude the sum is conditioned on (sum of
+  |terms|, plus |y_in| for expand), computed by the oracle on absolute values. Where |oracle| is
+  small against M, the fp32 evaluation's own rounding (which scales with M, not with the result)
+  can exceed 1e-5 * |oracle| for a correct kernel; everywhere else the plain relative bar holds.
 * bf16 gradients of the MLP backward (sums whose terms carry bf16-stored factors, such as
   dA = dxa^T x over 4096 tokens): |gpu - ref| <= 1e-2 + 1e-2 |ref| + 2u * RSS, with u = 2^-8 the
   unit roundoff of bf16 and RSS the root-sum-square of the sum's terms, from the oracle's own
@@ -114,10 +116,13 @@ def backward_rss(x, dout, w, inter, scale, rows=None):
 def assert_close_f32(got, ref, mag, what=""):
     g = f64(got)
     r = f64(ref)
-    bad = ~(np.abs(g - r) <= 1e-5 * mag)
+    m = np.asarray(mag, dtype=np.float64)
+    bar = 1e-5 * np.where(np.abs(r) >= 0.5 * m, np.abs(r), m)
+    bad = ~(np.abs(g - r) <= bar)
     if bad.any():
         idx = np.argwhere(bad)[:5]
-        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside 1e-5*M; first "
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside 1e-5*|ref| (1e-5*M "
+                             f"where |ref| < M/2); first "
                              f"{[(tuple(i), g[tuple(i)], r[tuple(i)], mag[tuple(i)]) for i in idx]}")
 
 
