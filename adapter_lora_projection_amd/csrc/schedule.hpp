@@ -44,10 +44,11 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* to
 }
 
 // Finds tile `t` (segment-major, BM rows) by scanning seg_indptr. Result in `out` (LDS),
-// out->g = -1 when t is past the last tile. Every thread must call it. Each thread loads its
-// segment's bounds, adapter, rank and (when `scalings` is non-null) scaling up front, so the
-// winning thread can publish the whole record without another dependent load.
-template <int NT>
+// out->g = -1 when t is past the last tile. Every thread must call it. RANK: the winning thread
+// also loads the adapter's rank and (when `scalings` is non-null) scaling into the record, one
+// more dependent load before the record is published; without it they are left 0 and the
+// caller loads them itself, off the chain that leads to its operand loads.
+template <int NT, bool RANK = true>
 __device__ __forceinline__ void find_tile_inline(const int* __restrict__ seg_indptr,
                                                  const int* __restrict__ weight_indices,
                                                  const int* __restrict__ lora_ranks,
@@ -73,8 +74,8 @@ __device__ __forceinline__ void find_tile_inline(const int* __restrict__ seg_ind
       out->m0 = lo + k * BM;
       out->mlen = min(BM, len - k * BM);
       out->a = a;
-      out->r = lora_ranks[a];
-      out->sigma = scalings != nullptr ? scalings[a] : 0.f;
+      out->r = RANK ? lora_ranks[a] : 0;
+      out->sigma = (RANK && scalings != nullptr) ? scalings[a] : 0.f;
     }
     carry += total;
     if (t < carry) break;  // uniform: carry and t are the same in every thread
@@ -126,8 +127,9 @@ __global__ __launch_bounds__(NT) void schedule_kernel(const int* __restrict__ se
   if (threadIdx.x == 0) *count = carry;
 }
 
-// Tile for this workgroup: from the prebuilt list when `tiles` is non-null, else inline.
-template <int NT>
+// Tile for this workgroup: from the prebuilt list when `tiles` is non-null, else inline. RANK as
+// for find_tile_inline.
+template <int NT, bool RANK = true>
 __device__ __forceinline__ void get_tile(const int* __restrict__ seg_indptr,
                                          const int* __restrict__ weight_indices,
                                          const int* __restrict__ lora_ranks,
@@ -140,38 +142,63 @@ __device__ __forceinline__ void get_tile(const int* __restrict__ seg_indptr,
       if (t < *tile_count) {
         const int4 v = tiles[t];
         out->g = v.x; out->m0 = v.y; out->mlen = v.z; out->a = v.w;
-        out->r = lora_ranks[v.w];
-        out->sigma = scalings != nullptr ? scalings[v.w] : 0.f;
+        out->r = RANK ? lora_ranks[v.w] : 0;
+        out->sigma = (RANK && scalings != nullptr) ? scalings[v.w] : 0.f;
       } else {
         out->g = -1;
       }
     }
     __syncthreads();
   } else {
-    find_tile_inline<NT>(seg_indptr, weight_indices, lora_ranks, scalings, G, BM, t, out,
-                         scan_scratch);
+    find_tile_inline<NT, RANK>(seg_indptr, weight_indices, lora_ranks, scalings, G, BM, t, out,
+                               scan_scratch);
   }
 }
 
-// Column block b of the per-slice blocking (blocks never straddle a slice boundary):
-// returns false when b is past the last block. Uniform loads of slice_offsets.
-__device__ __forceinline__ bool find_nblock(const int* __restrict__ slice_offsets, int S, int BN,
-                                            int b, int* s_out, int* n0_out, int* nlen_out) {
-  int lo = slice_offsets[0];
-  for (int s = 0; s < S; ++s) {
-    const int hi = slice_offsets[s + 1];
-    const int len = max(hi - lo, 0);
-    const int nb = (len + BN - 1) / BN;
-    if (b < nb) {
-      *s_out = s;
-      *n0_out = lo + b * BN;
-      *nlen_out = min(BN, len - b * BN);
-      return true;
-    }
-    b -= nb;
-    lo = hi;
+// The adapter's rank and scaling of a tile found without them (get_tile<NT, false>). Operand
+// loads issued before their first use do not wait for these two loads.
+__device__ __forceinline__ void tile_rank(const int* __restrict__ lora_ranks,
+                                          const float* __restrict__ scalings, Tile* t) {
+  const int a = __builtin_amdgcn_readfirstlane(t->a);
+  t->r = lora_ranks[a];
+  t->sigma = scalings != nullptr ? scalings[a] : 0.f;
+}
+
+// Column blocks from slice bounds held one slice per lane (S <= 64): slice_lanes loads them
+// (before the tile search, so the loads overlap its own), find_nblock_lanes finds block b with
+// a wave prefix sum. Same blocking as find_nblock.
+struct SliceLane {
+  int lo, hi;
+};
+__device__ __forceinline__ SliceLane slice_lanes(const int* __restrict__ slice_offsets, int S) {
+  const int k = int(threadIdx.x) & 63;
+  SliceLane v{0, 0};
+  if (k < S) {
+    v.lo = slice_offsets[k];
+    v.hi = slice_offsets[k + 1];
   }
-  return false;
+  return v;
+}
+__device__ __forceinline__ bool find_nblock_lanes(SliceLane v, int S, int BN, int b, int* s_out,
+                                                  int* n0_out, int* nlen_out) {
+  const int k = int(threadIdx.x) & 63;
+  const int len = k < S ? max(v.hi - v.lo, 0) : 0;
+  const int nb = (len + BN - 1) / BN;
+  int incl = nb;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (k >= d) incl += o;
+  }
+  const int excl = incl - nb;
+  const unsigned long long hit = __ballot(k < S && b >= excl && b < incl);
+  if (hit == 0) return false;
+  const int ks = __ffsll(hit) - 1;
+  const int lo = __shfl(v.lo, ks, 64), ln = __shfl(len, ks, 64), ex = __shfl(excl, ks, 64);
+  *s_out = ks;
+  *n0_out = lo + (b - ex) * BN;
+  *nlen_out = min(BN, ln - (b - ex) * BN);
+  return true;
 }
 
 }  // namespace lmx

@@ -34,15 +34,18 @@ namespace lmx {
 // ------------------------------------------------------------------------------------ shrink
 
 // Tile t of a shrink call: from the segment schedule, or rows [t*BM, (t+1)*BM) of the single
-// dense segment (internal mode, seg_indptr null). Every thread must call it.
+// dense segment (internal mode, seg_indptr null). Every thread must call it. The adapter's rank
+// is loaded after the search and first needed by the stores: operand loads read the padded rank
+// (shrink_rows) and do not wait for it.
 template <int NT>
 __device__ __forceinline__ Tile shrink_tile(const ShrinkArgs& p, int BM, int t, Tile* s_tile,
                                             int* s_scan) {
   Tile tile;
   if (p.seg_indptr != nullptr) {
-    get_tile<NT>(p.seg_indptr, p.weight_indices, p.lora_ranks, nullptr, p.G, BM, p.tiles,
-                 p.tile_count, t, s_tile, s_scan);
+    get_tile<NT, false>(p.seg_indptr, p.weight_indices, p.lora_ranks, nullptr, p.G, BM, p.tiles,
+                        p.tile_count, t, s_tile, s_scan);
     tile = *s_tile;
+    if (tile.g >= 0) tile_rank(p.lora_ranks, nullptr, &tile);
   } else {
     tile.g = t * BM < p.T ? 0 : -1;
     tile.m0 = t * BM;
@@ -52,6 +55,13 @@ __device__ __forceinline__ Tile shrink_tile(const ShrinkArgs& p, int BM, int t, 
     tile.sigma = 0.f;
   }
   return tile;
+}
+
+// A rows of each slice the operand loads may read: the padded rank R when A is the stacked
+// [L][S*R][K] array (every padded row exists; rows at or past the adapter's rank only feed
+// outputs that are stored as zeros), the true rank for the per-slice A arrays of dense mode.
+__device__ __forceinline__ int shrink_rows(const ShrinkArgs& p, const Tile& tile) {
+  return p.seg_indptr != nullptr ? p.R : tile.r;
 }
 
 // Planes of tile t in a shared-work shrink: its (tile, step) units [t * nunits, (t+1) * nunits)
@@ -154,7 +164,7 @@ __device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& ti
   const int lane = threadIdx.x & 63, w = wave_id();
   const int li = lane & 15, lg = lane >> 4;
   const int a = tile.a;
-  const int r = tile.r;
+  const int r = shrink_rows(p, tile);
   const int NB = (p.R + 15) >> 4;  // 16-column blocks per slice
   const int nblk = p.S * NB;
   const int K = int(p.K);
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
     if (tile.g < 0) break;  // past the last tile (uniform over the workgroup)
     const int j = int(blockIdx.x) - int((int64_t(t) * nsteps) / p.sk_q);
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
-    if (tile.r > 0) {
+    {  // (a rank-0 tile stores nothing: every column is at or past its rank)
       f32x4_t sums[NOUT];
       shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, int(blockIdx.y), k0, k1, s_red, sums);
       store(tile, int(blockIdx.y), sums, slot);
@@ -461,19 +471,18 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
   const S* __restrict__ wb = reinterpret_cast<const S*>(p.w_b);
   S* __restrict__ y = reinterpret_cast<S*>(p.y);
 
-  // A operand: h row of token c of the tile (constant over the chunks)
+  // A operand: h row of token c of the tile (constant over the chunks), read over the padded
+  // rank; the adapter's rank masks it once the first chunks are in flight
+  Frag<S, ALB> hf[JS];
   uint4 hv[JS];
   {
     const bool ok = c < tile.mlen;
     const S* hrow = hbuf + int64_t(tile.m0 + (ok ? c : 0)) * p.ldh + s * p.R;
-    Frag<S, ALB> hf[JS];
 #pragma unroll
     for (int js = 0; js < JS; ++js) {
       const int j = js * KSTEP + g * EPF;
-      hf[js].fetch(hrow + j, r - j, hrow);
+      hf[js].fetch(hrow + j, p.R - j, hrow);
     }
-#pragma unroll
-    for (int js = 0; js < JS; ++js) hv[js] = hf[js].masked(r - (js * KSTEP + g * EPF));
   }
   // output rows of tokens 4g .. 4g+3
   S* yrow[4];
@@ -501,7 +510,7 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
 #pragma unroll
       for (int js = 0; js < JS; ++js) {
         const int j = js * KSTEP + g * EPF;
-        br[d][js][q].fetch(brow + j, in ? r - j : 0, brow);
+        br[d][js][q].fetch(brow + j, in ? p.R - j : 0, brow);
       }
     }
     const int c0 = cbase + 4 * c;
@@ -566,6 +575,9 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
   [&]<int... dd>(std::integer_sequence<int, dd...>) {
     ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
   }(std::make_integer_sequence<int, D>{});
+  if (r <= 0) return;  // a rank-0 adapter leaves y untouched
+#pragma unroll
+  for (int js = 0; js < JS; ++js) hv[js] = hf[js].masked(r - (js * KSTEP + g * EPF));
   const int nfull = nci / D;
   for (int gi = 0; gi < nfull; ++gi) {
     [&]<int... dd>(std::integer_sequence<int, dd...>) {
@@ -610,18 +622,16 @@ __device__ __forceinline__ void expand_body_wide(const ExpandArgs& p, const Tile
   const S* __restrict__ wb = reinterpret_cast<const S*>(p.w_b);
   S* __restrict__ y = reinterpret_cast<S*>(p.y);
 
+  Frag<S, ALB> hf[JS];  // over the padded rank; masked by the rank after the ring prologue
   uint4 hv[JS];
   {
     const bool ok = c < tile.mlen;
     const S* hrow = hbuf + int64_t(tile.m0 + (ok ? c : 0)) * p.ldh + s * p.R;
-    Frag<S, ALB> hf[JS];
 #pragma unroll
     for (int js = 0; js < JS; ++js) {
       const int j = js * KSTEP + g * EPF;
-      hf[js].fetch(hrow + j, r - j, hrow);
+      hf[js].fetch(hrow + j, p.R - j, hrow);
     }
-#pragma unroll
-    for (int js = 0; js < JS; ++js) hv[js] = hf[js].masked(r - (js * KSTEP + g * EPF));
   }
   S* yrow[4];
   bool tok_ok[4];
@@ -647,7 +657,7 @@ __device__ __forceinline__ void expand_body_wide(const ExpandArgs& p, const Tile
 #pragma unroll
       for (int js = 0; js < JS; ++js) {
         const int j = js * KSTEP + g * EPF;
-        br[d][js][q].fetch(brow + j, in ? r - j : 0, brow);
+        br[d][js][q].fetch(brow + j, in ? p.R - j : 0, brow);
       }
     }
     const int c0 = cbase + 8 * c;
@@ -700,6 +710,9 @@ __device__ __forceinline__ void expand_body_wide(const ExpandArgs& p, const Tile
   [&]<int... dd>(std::integer_sequence<int, dd...>) {
     ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
   }(std::make_integer_sequence<int, D>{});
+  if (r <= 0) return;  // a rank-0 adapter leaves y untouched
+#pragma unroll
+  for (int js = 0; js < JS; ++js) hv[js] = hf[js].masked(r - (js * KSTEP + g * EPF));
   const int nfull = nci / D;
   for (int gi = 0; gi < nfull; ++gi) {
     [&]<int... dd>(std::integer_sequence<int, dd...>) {
@@ -761,19 +774,18 @@ __device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Ti
   const int nend = nb0 + nblen;
   const int nchunks = (nblen + CW - 1) / CW;
   const int nci = w < nchunks ? (nchunks - w + NW - 1) / NW : 0;
-  const int jv = r - 4 * g;  // valid ranks of this lane's 4
+  int jv = 0;  // valid ranks of this lane's 4 (set once the first loads are in flight)
 
   const S* __restrict__ hbuf = reinterpret_cast<const S*>(p.h);
   const S* __restrict__ wb = reinterpret_cast<const S*>(p.w_b);
   S* __restrict__ y = reinterpret_cast<S*>(p.y);
 
+  Frag8<S, ALB> hf;  // over the padded rank; masked by the rank after the ring prologue
   uint2 hv;
   {
     const bool ok = c < tile.mlen;
     const S* hrow = hbuf + int64_t(tile.m0 + (ok ? c : 0)) * p.ldh + s * p.R;
-    Frag8<S, ALB> hf;
-    hf.fetch(hrow + 4 * g, jv, hrow);
-    hv = mask4(hf.raw(), jv);
+    hf.fetch(hrow + 4 * g, p.R - 4 * g, hrow);
   }
   S* yrow[4];
   bool tok_ok[4];
@@ -796,7 +808,7 @@ __device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Ti
     for (int q = 0; q < 8; ++q) {
       const int col = cbase + 8 * c + q;
       const S* brow = bblk + int64_t((in && col < nend) ? col : nb0) * p.ldb;
-      br[d][q].fetch(brow + 4 * g, in ? jv : 0, brow);
+      br[d][q].fetch(brow + 4 * g, in ? p.R - 4 * g : 0, brow);
     }
     const int c0 = cbase + 8 * c;
 #pragma unroll
@@ -843,6 +855,9 @@ __device__ __forceinline__ void expand_body_wide16(const ExpandArgs& p, const Ti
   [&]<int... dd>(std::integer_sequence<int, dd...>) {
     ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
   }(std::make_integer_sequence<int, D>{});
+  if (r <= 0) return;  // a rank-0 adapter leaves y untouched
+  jv = r - 4 * g;
+  hv = mask4(hf.raw(), jv);
   const int nfull = nci / D;
   for (int gi = 0; gi < nfull; ++gi) {
     [&]<int... dd>(std::integer_sequence<int, dd...>) {
@@ -867,12 +882,17 @@ __global__ __launch_bounds__(NW * 64) void expand_kernel(ExpandArgs p) {
   __shared__ Tile s_tile;
   __shared__ int s_scan[NW];
 
-  get_tile<NT>(p.seg_indptr, p.weight_indices, p.lora_ranks, p.scalings, p.G, BM, p.tiles,
-               p.tile_count, int(blockIdx.x), &s_tile, s_scan);
-  const Tile tile = s_tile;
-  if (tile.g < 0 || tile.r <= 0) return;  // a rank-0 adapter leaves y untouched
+  // The slice bounds, the tile search and then the rank: each load is issued as early as its
+  // address is known, so the operand loads wait for one round trip less (a rank-0 adapter is
+  // skipped inside the body, after its first loads, and leaves y untouched).
+  const SliceLane sl = slice_lanes(p.slice_offsets, p.S);
+  get_tile<NT, false>(p.seg_indptr, p.weight_indices, p.lora_ranks, p.scalings, p.G, BM, p.tiles,
+                      p.tile_count, int(blockIdx.x), &s_tile, s_scan);
+  Tile tile = s_tile;
+  if (tile.g < 0) return;
+  tile_rank(p.lora_ranks, p.scalings, &tile);
   int s, nb0, nblen;
-  if (!find_nblock(p.slice_offsets, p.S, p.BN, int(blockIdx.y), &s, &nb0, &nblen)) return;
+  if (!find_nblock_lanes(sl, p.S, p.BN, int(blockIdx.y), &s, &nb0, &nblen)) return;
   if constexpr (WIDE && ALY && DT != DT_F32) {
     // 16-byte pieces when the block starts on a 16-byte boundary (rows are 16-byte aligned)
     if ((nb0 * int(sizeof(typename Traits<DT>::store_t))) % 16 == 0) {
@@ -918,12 +938,15 @@ __global__ __launch_bounds__(256) void expand_shared_kernel(ExpandArgs p) {
   __shared__ int s_scan[NW];
   __shared__ __align__(16) uint2 bsh[2][8 * PQ];
 
-  get_tile<NT>(p.seg_indptr, p.weight_indices, p.lora_ranks, p.scalings, p.G, BM, p.tiles,
-               p.tile_count, int(blockIdx.x), &s_tile, s_scan);
-  const Tile tile = s_tile;
-  if (tile.g < 0 || tile.r <= 0) return;  // a rank-0 adapter leaves y untouched
+  // loads issued as early as their addresses are known (see expand_kernel)
+  const SliceLane sl = slice_lanes(p.slice_offsets, p.S);
+  get_tile<NT, false>(p.seg_indptr, p.weight_indices, p.lora_ranks, p.scalings, p.G, BM, p.tiles,
+                      p.tile_count, int(blockIdx.x), &s_tile, s_scan);
+  Tile tile = s_tile;
+  if (tile.g < 0) return;
+  tile_rank(p.lora_ranks, p.scalings, &tile);
   int s, nb0, nblen;
-  if (!find_nblock(p.slice_offsets, p.S, p.BN, int(blockIdx.y), &s, &nb0, &nblen)) return;
+  if (!find_nblock_lanes(sl, p.S, p.BN, int(blockIdx.y), &s, &nb0, &nblen)) return;
   const int w = wave_id();
   const int mw = tile.mlen - 16 * w;  // tokens of this wave (uniform over the wave; may be <= 0)
   if ((nb0 * int(sizeof(S))) % 16 != 0) {
@@ -940,20 +963,18 @@ __global__ __launch_bounds__(256) void expand_shared_kernel(ExpandArgs p) {
   const float sigma = tile.sigma;
   const int nend = nb0 + nblen;
   const int nchunks = (nblen + CW - 1) / CW;
-  const int jv = r - 4 * g;
 
   const S* __restrict__ hbuf = reinterpret_cast<const S*>(p.h);
   const S* __restrict__ wb = reinterpret_cast<const S*>(p.w_b);
   S* __restrict__ y = reinterpret_cast<S*>(p.y);
 
-  // A operand: h row of this wave's token c (ranks 4g .. 4g+3)
-  uint2 hv;
+  // A operand: h row of this wave's token c (ranks 4g .. 4g+3 of the padded rank; the rank
+  // masks it after the first y loads are in flight)
+  Frag8<S, ALB> hf;
   {
     const bool ok = c < mw;
     const S* hrow = hbuf + int64_t(ok ? tile.m0 + 16 * w + c : tile.m0) * p.ldh + s * p.R;
-    Frag8<S, ALB> hf;
-    hf.fetch(hrow + 4 * g, jv, hrow);
-    hv = mask4(hf.raw(), jv);
+    hf.fetch(hrow + 4 * g, p.R - 4 * g, hrow);
   }
   S* yrow[4];
   bool tok_ok[4];
@@ -969,7 +990,7 @@ __global__ __launch_bounds__(256) void expand_shared_kernel(ExpandArgs p) {
   // fragment groups 2h and 2h+1 of product q = row & 7 for lane c = row >> 3.
   const int lrow = t >> 1, lhalf = t & 1;
   const int slot = (lrow & 7) * PQ + 32 * lhalf + (lrow >> 3);
-  const int lvalid = r - 8 * lhalf;
+  int lvalid = 0;  // valid ranks of the piece (set once the first loads are in flight)
   const S* bblk = wb + int64_t(tile.a) * p.N * p.ldb + 8 * lhalf;
   auto bload = [&](int i) -> uint4 {
     const int col = nb0 + i * CW + lrow;
@@ -998,6 +1019,10 @@ __global__ __launch_bounds__(256) void expand_shared_kernel(ExpandArgs p) {
       (yfetch(std::integral_constant<int, dd>{}, dd), ...);
     }(std::make_integer_sequence<int, D>{});
   }
+  __builtin_amdgcn_sched_barrier(0);
+  if (r <= 0) return;  // uniform: a rank-0 adapter leaves y untouched
+  lvalid = r - 8 * lhalf;
+  const uint2 hv = mask4(hf.raw(), r - 4 * g);
   bput(0, bnext);
   bnext = bload(1);
   __syncthreads();

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(ShrinkArgs p) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int j = 16 * b + CPW * w + c;
-      arow[c] = base + int64_t(j < tile.r ? j : 0) * p.lda;
+      arow[c] = base + int64_t(j < shrink_rows(p, tile) ? j : 0) * p.lda;
     }
   }
 
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(ShrinkArgs p) {
   for (int t = 0; t < BM; ++t)
 #pragma unroll
     for (int c = 0; c < CPW; ++c) acc[t][c] = 0.f;
-  if (16 * b + CPW * w < tile.r) {  // uniform per wave: this wave has a column inside the rank
+  if (16 * b + CPW * w < shrink_rows(p, tile)) {  // uniform per wave: a column inside the rows
     for (int k = 8 * lane; k < K; k += 512) {
       uint4 av[CPW], xv[BM];
 #pragma unroll

@@ -11,8 +11,8 @@
 // bank-conflict free. Each of the 4 waves owns BMG / 4 groups of 16 positions across all NC
 // columns: no reduction between waves, and every A chunk loaded is shared by the whole tile.
 //
-// Rows past the tile and rank columns past the adapter's rank load a valid row of the same
-// operand (their outputs are never stored); reduction indices past K load a block of zeros.
+// Rows past the tile and rank columns past the A rows that exist (shrink_rows) load a valid row
+// of the same operand (their outputs are never stored); reduction indices past K load a block of zeros.
 // Requires 16-byte aligned x and A rows and K a multiple of 8 (the host checks).
 //
 // Work split: direct (sk_q == 0, one workgroup per tile over all of K) or shared (the
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
         const int blk = int(blockIdx.y) * NCB + (n >> 4);
         const int s = blk / NB, b = blk - (blk / NB) * NB;
         const int j = 16 * b + (n & 15);
-        const bool ok = blk < nblk && j < tile.r;
+        const bool ok = blk < nblk && j < shrink_rows(p, tile);
         const int ss = ok ? s : 0;
         const void* own = nullptr;
 #pragma unroll
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
     if (tile.g < 0) break;  // past the last tile (uniform over the workgroup)
     const int j = int(blockIdx.x) - int((int64_t(t) * nunits) / p.sk_q);
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
-    if (tile.r > 0) piece(tile, k0, k1, slot);
+    piece(tile, k0, k1, slot);  // (a rank-0 tile stores nothing)
     if (p.counters != nullptr)
       sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, int(blockIdx.y),
                          int(gridDim.y), &s_last);
