@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <initializer_list>
 #include <cstdint>
 #include <mutex>
 
@@ -115,15 +116,11 @@ int expand_bn(const Knobs& kn, int64_t T, int32_t G, int64_t N, int bm, int wave
 // waves splitting K, while that grid stays within two workgroups per compute unit; beyond that
 // two token groups sharing each A fragment over 3 column blocks (x read once per tile), or 4
 // when the slices have 4 or fewer blocks that 3 does not divide. The 2-deep operand ring
-// measured faster than 4-deep. `pub`: the shrink entry point (the internal dense products keep
-// the rule they were tuned with: two token groups from 2048 rows).
-int shrink_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t G, bool pub) {
+// measured faster than 4-deep.
+int shrink_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t G) {
   if (kn.shape >= 0 && kn.shape < lmx::num_shrink_variants()) return kn.shape;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  if (nblk % 3 == 0) {
-    if (!pub) return T <= 2048 ? 2 : 4;
-    return (cdiv(T, 16) + G) * nblk <= 512 ? 2 : 4;
-  }
+  if (nblk % 3 == 0) return (cdiv(T, 16) + G) * nblk <= 512 ? 2 : 4;
   return nblk <= 4 ? 1 : 4;
 }
 
@@ -165,10 +162,10 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // The LDS-staged shrink covers the 16-bit types whose x and A rows are 16-byte aligned and
 // whose K is a multiple of 8; its shape is the smallest column-block count that holds every
 // block of the slices (or 12 blocks per workgroup beyond that).
-int shrink_lds_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t G, bool pub) {
+int shrink_lds_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t G) {
   if (kn.shape >= 0 && kn.shape < lmx::num_shrink_lds_variants()) return kn.shape;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  if (pub && nblk == 3) {
+  if (nblk == 3) {
     // Three column blocks (rank 16 over three slices, the decode projections): the shortest
     // tiles whose grid fits in one round of 256 workgroups. Kernel durations on the decode
     // sweep (rocprofv3, each call after a 512 MiB device write, so the caches hold dirty lines
@@ -194,18 +191,11 @@ int shrink_lds_variant(const Knobs& kn, int64_t T, int32_t S, int32_t R, int32_t
 // Which shrink kernel to run when the LDS-staged one is eligible (event timings and rocprofv3
 // sweeps on MI355X). The LDS-staged kernel's direct-to-LDS loads fetch whole 128-byte row
 // chunks (the register ring's MFMA-layout loads take 64 bytes from each of 16 rows, and its
-// address path stalls on the L1), and each A chunk is shared by the whole tile. Internal dense
-// products (fused MLP, projections, backward): from T * K = 16 Mi elements with few column
-// blocks, as tuned with their shared-work second launch. Shrink entry point: with three column
-// blocks from 8 Mi elements (the short-tile shapes, see shrink_lds_variant); otherwise when even
-// the register ring's wider shape would need a second round of workgroups and T * K is large.
-bool prefer_lds(const Knobs& kn, int64_t T, int64_t K, int32_t S, int32_t R) {
-  if (kn.family >= 0) return kn.family == 1;
-  const int64_t nblk = int64_t(S) * ((R + 15) / 16);
-  return T * K >= (int64_t(16) << 20) && nblk <= 4;
-}
-
-bool prefer_lds_pub(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+// address path stalls on the L1), and each A chunk is shared by the whole tile: with three
+// column blocks from 8 Mi elements (the short-tile shapes, see shrink_lds_variant); otherwise
+// when even the register ring's wider shape would need a second round of workgroups and T * K
+// is large.
+bool prefer_lds(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, int32_t R,
                     int32_t G) {
   if (kn.family >= 0) return kn.family == 1;
   const int64_t nblk = int64_t(S) * ((R + 15) / 16);
@@ -214,14 +204,14 @@ bool prefer_lds_pub(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S,
   // against 21.0 us)
   if (nblk == 3) return T * K >= (int64_t(8) << 20);
   if (T * K < (int64_t(16) << 20) || nblk > 4) return false;
-  const int v = shrink_variant(kn, T, S, R, G, true);
+  const int v = shrink_variant(kn, T, S, R, G);
   const int64_t ring_wgs = (cdiv(T, lmx::shrink_plan_bm(dtype, v)) + G) *
                            cdiv(nblk, lmx::shrink_plan_cb(dtype, v));
   return ring_wgs > 256;
 }
 
 ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, int32_t R,
-                   int32_t G, bool lds, bool in_launch_ok, bool gemv = false) {
+                   int32_t G, bool lds, bool gemv = false) {
   ShrinkWs w{};
   w.lds = lds;
   w.gemv = gemv;
@@ -240,13 +230,13 @@ ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, 
     return w;
   }
   if (lds) {
-    w.variant = shrink_lds_variant(kn, T, S, R, G, in_launch_ok);
+    w.variant = shrink_lds_variant(kn, T, S, R, G);
     w.bm = lmx::shrink_lds_bm(w.variant);
     w.unit = lmx::kShrinkLdsUnit;
     gy = cdiv(nblk, lmx::shrink_lds_ncb(w.variant));
     frags = (w.bm + 16 * lmx::shrink_lds_ncb(w.variant)) / 8;  // 1 KiB loads per stage
   } else {
-    w.variant = shrink_variant(kn, T, S, R, G, in_launch_ok);
+    w.variant = shrink_variant(kn, T, S, R, G);
     w.bm = lmx::shrink_plan_bm(dtype, w.variant);
     w.unit = dtype == LORA_F32 ? 16 : 32;
     gy = cdiv(nblk, lmx::shrink_plan_cb(dtype, w.variant));
@@ -256,14 +246,14 @@ ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, 
   w.bound = cdiv(T, w.bm) + G;
   const int64_t nsteps = cdiv(K, w.unit);
   // Shared (tile, step) work pays when one workgroup per tile leaves most compute units idle and
-  // each workgroup would stream a lot. With the in-launch completion (arrival counters; the
-  // shrink entry point) it costs three dependent memory round trips instead of a second launch:
-  // measured on the decode sweep it pays only below about 48 direct workgroups (50 tokens: 24
-  // workgroups 14.9 us, 192 sharing 12.0 us, cold calls), with 64 workgroups per grid row; the
-  // LDS-staged kernel runs direct there (8192 tokens: 52 us against 55 us shared). The internal
-  // dense products keep their second launch and the rule they were tuned with.
+  // each workgroup would stream a lot. With the in-launch completion (arrival counters) it costs
+  // three dependent memory round trips instead of a second launch: measured on the decode sweep
+  // it pays only below about 48 direct workgroups (50 tokens: 24 workgroups 14.9 us, 192 sharing
+  // 12.0 us, cold calls), with 64 workgroups per grid row; the LDS-staged kernel runs direct
+  // there (8192 tokens: 52 us against 55 us shared). An explicit plan may ask for the second
+  // launch instead (finish 0) or for a split the counters cannot cover.
   const int64_t direct_wgs = w.bound * gy;
-  const bool counters_fit = in_launch_ok && w.bound * gy <= kMaxCounters;
+  const bool counters_fit = w.bound * gy <= kMaxCounters;
   w.in_launch = kn.finish >= 0 ? (kn.finish == 1 && counters_fit) : counters_fit;
   bool shared;
   int64_t pdef;
@@ -296,38 +286,53 @@ ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, 
 
 lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_EHIP; }
 
-// Bytes of a plan's partial planes (zero in direct mode), for the internal layouts that place
-// them in a section of their own.
-size_t part_bytes(const ShrinkWs& w) { return w.q > 0 ? w.total - w.part : 0; }
-
 // Workspace of the fused MLP: byte offsets of its six sections (256-byte aligned).
+// Workgroups of the sums kernel launches (two fit per compute unit): about 512 where the
+// partials are a small part of the bytes moved; 256 for the sums over tokens of x and dout
+// alone, whose row chunks each add nh x 64 bytes of partials per column.
+#ifndef LMX_SUMS_COLS_TARGET
+#define LMX_SUMS_COLS_TARGET 256
+#endif
+#ifndef LMX_SUMS_ROWS_TARGET
+#define LMX_SUMS_ROWS_TARGET 512
+#endif
+
 struct MlpLayout {
   int64_t rp;           // rank rounded up to 32
-  ShrinkWs s_gu, s_d;   // plans of the two LoRA-A products (dense mode, one segment)
-  ShrinkWs r_gu, r_d;   // the same with the register-ring kernel (unaligned A pointers)
-  size_t xa_gu, lb_gu, hmid, xa_d, lb_d, part, total;
+  lmx::SumJobs gu, dn;  // the LoRA-A products of x (gate, up) and of hmid (down)
+  size_t xa_gu, lb_gu, hmid, xa_d, lb_d, apad, rowpart, total;
 };
 
+// LoRA-A products h = round(P A^T) through the sums kernel's row side read 16 * ceil(r / 16) rows
+// of each A: the caller's A when its rank is a multiple of 16 and its rows are 16-byte aligned,
+// else a zero-padded copy in the workspace.
+bool lora_a_in_place(int32_t r, std::initializer_list<const void*> as) {
+  if (r % 16 != 0) return false;
+  for (const void* a : as)
+    if (!al16(a)) return false;
+  return true;
+}
+
 MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
-  const Knobs kn;
   MlpLayout L{};
   L.rp = cdiv(r, 32) * 32;
-  // dense mode has no segments: the tile bound is ceil(M / BM)
-  // plans for both shrink families (the LDS-staged one needs aligned A pointers, known only
-  // at call time); the partials section fits either
-  L.s_gu = shrink_ws(kn, LORA_BF16, M, H, 2, int(L.rp), 0, prefer_lds(kn, M, H, 2, int(L.rp)), false);
-  L.s_d = shrink_ws(kn, LORA_BF16, M, I, 1, int(L.rp), 0, prefer_lds(kn, M, I, 1, int(L.rp)), false);
-  L.r_gu = shrink_ws(kn, LORA_BF16, M, H, 2, int(L.rp), 0, false, false);
-  L.r_d = shrink_ws(kn, LORA_BF16, M, I, 1, int(L.rp), 0, false, false);
+  const int JB = int(cdiv(r, 16));
+  int64_t rf1 = 0, cf1 = 0, rf2 = 0, cf2 = 0;
+  L.gu.n = 1; L.gu.M = int(M); L.gu.JB = JB;
+  L.gu.job[0].C = int(H); L.gu.job[0].nr = 2; L.gu.job[0].nh = 0;
+  lmx::plan_sums(L.gu, LMX_SUMS_ROWS_TARGET, &rf1, &cf1);
+  L.dn.n = 1; L.dn.M = int(M); L.dn.JB = JB;
+  L.dn.job[0].C = int(I); L.dn.job[0].nr = 1; L.dn.job[0].nh = 0;
+  lmx::plan_sums(L.dn, 512, &rf2, &cf2);
   size_t off = 0;
-  L.xa_gu = off; off += align256(size_t(M) * 2 * L.rp * 2);
-  L.lb_gu = off; off += align256(size_t(2 * I) * 2 * L.rp * 2);
-  L.hmid = off; off += align256(size_t(M) * I * 2);
-  L.xa_d = off; off += align256(size_t(M) * L.rp * 2);
-  L.lb_d = off; off += align256(size_t(H) * L.rp * 2);
-  L.part = off;
-  off += align256(std::max(std::max(part_bytes(L.s_gu), part_bytes(L.s_d)),
-                           std::max(part_bytes(L.r_gu), part_bytes(L.r_d))));
+  auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
+  L.xa_gu = take(size_t(M) * 2 * L.rp * 2);
+  L.lb_gu = take(size_t(2 * I) * 2 * L.rp * 2);
+  L.hmid = take(size_t(M) * I * 2);
+  L.xa_d = take(size_t(M) * L.rp * 2);
+  L.lb_d = take(size_t(H) * L.rp * 2);
+  L.apad = take(size_t(16 * JB) * (2 * H + I) * 2);  // [A_g | A_u | A_d] padded copies
+  L.rowpart = take(size_t(std::max(rf1, rf2)) * 4);
   L.total = off;
   return L;
 }
@@ -337,22 +342,25 @@ MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
 struct LinearLayout {
   int64_t rp;
   int P;
-  ShrinkWs s, r;  // LoRA-A product plans: LDS-staged / register-ring (unaligned A pointers)
-  size_t xa, lb[3], part, total;
+  lmx::SumJobs xs;  // the LoRA-A products of x, one row-side operand per projection
+  size_t xa, lb[3], apad, rowpart, total;
 };
 
 LinearLayout linear_layout(int64_t M, int64_t K, const int64_t* N, int P, int32_t r) {
-  const Knobs kn;
   LinearLayout L{};
   L.rp = cdiv(r, 32) * 32;
   L.P = P;
-  L.s = shrink_ws(kn, LORA_BF16, M, K, P, int(L.rp), 0, prefer_lds(kn, M, K, P, int(L.rp)), false);
-  L.r = shrink_ws(kn, LORA_BF16, M, K, P, int(L.rp), 0, false, false);
+  const int JB = int(cdiv(r, 16));
+  int64_t rf = 0, cf = 0;
+  L.xs.n = 1; L.xs.M = int(M); L.xs.JB = JB;
+  L.xs.job[0].C = int(K); L.xs.job[0].nr = P; L.xs.job[0].nh = 0;
+  lmx::plan_sums(L.xs, LMX_SUMS_ROWS_TARGET, &rf, &cf);
   size_t off = 0;
-  L.xa = off; off += align256(size_t(M) * P * L.rp * 2);
-  for (int p = 0; p < P; ++p) { L.lb[p] = off; off += align256(size_t(N[p]) * L.rp * 2); }
-  L.part = off;
-  off += align256(std::max(part_bytes(L.s), part_bytes(L.r)));
+  auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
+  L.xa = take(size_t(M) * P * L.rp * 2);
+  for (int p = 0; p < P; ++p) L.lb[p] = take(size_t(N[p]) * L.rp * 2);
+  L.apad = take(size_t(16 * JB) * K * P * 2);
+  L.rowpart = take(size_t(rf) * 4);
   L.total = off;
   return L;
 }
@@ -376,10 +384,6 @@ struct MlpBwdLayout {
       rowpart, colpart, total;
 };
 
-#ifndef LMX_SUMS_COLS_TARGET
-#define LMX_SUMS_COLS_TARGET 256
-#endif
-
 MlpBwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   MlpBwdLayout L{};
   L.rp = cdiv(r, 32) * 32;
@@ -394,7 +398,7 @@ MlpBwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int32_t r) {
   init(L.in, 2);
   job(L.in.job[0], H, 2, 0);  // x: xa_g, xa_u
   job(L.in.job[1], H, 1, 0);  // dout: dxa_d
-  lmx::plan_sums(L.in, 512, &rf[0], &cf[0]);
+  lmx::plan_sums(L.in, LMX_SUMS_ROWS_TARGET, &rf[0], &cf[0]);
   init(L.both, 3);
   for (int q = 0; q < 3; ++q) job(L.both.job[q], I, 1, 1);  // de, dv, hmid
   lmx::plan_sums(L.both, 512, &rf[1], &cf[1]);
@@ -465,22 +469,41 @@ lora_status linear_fused(lora_dtype dtype, int64_t M, int64_t K, const int64_t* 
       jobs.job[p] = {u16(b[p]), r, reinterpret_cast<uint16_t*>(ws + L.lb[p]), rp, int(N[p]), 0};
     if (lmx::launch_scale_lora_b(jobs, scale, r, st) != hipSuccess) return LORA_EHIP;
   }
-  // 2. [xa_0 | .. | xa_{P-1}] = round(x [A_0; ..]^T) in one pass over x (dense shrink, P slices)
+  // 2. [xa_0 | .. | xa_{P-1}] = round(x [A_0; ..]^T) in one pass over x: the sums kernel's row
+  //    side with one operand per projection, then the fixed-order reduction (rank padding zeroed)
   {
-    bool al = true;
-    for (int p = 0; p < P; ++p) al = al && al16(a[p]);
-    const ShrinkWs& sp = al ? L.s : L.r;
-    lmx::ShrinkArgs sa{};
-    sa.x = x; sa.ldx = ldx; sa.K = K; sa.S = P; sa.R = int(rp); sa.G = 1; sa.T = int(M);
-    sa.dense_rank = r; sa.w_a = a[0]; sa.lda = K;
-    for (int p = 0; p < P; ++p) sa.w_a_slice[p] = a[p];
-    sa.h = xa; sa.ldh = P * rp;
-    sa.sk_q = sp.q; sa.sk_tiles = int(sp.bound); sa.sk_mp = sp.mp; sa.sk_unit = sp.unit;
-    sa.part = reinterpret_cast<float*>(ws + L.part);
-    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
-    if (lmx::launch_shrink(LORA_BF16, sa, plan, st) != hipSuccess) return LORA_EHIP;
-    if (sp.q > 0 && lmx::launch_shrink_sk_reduce(LORA_BF16, sa, sp.bm, st) != hipSuccess)
-      return LORA_EHIP;
+    const int JB = L.xs.JB;
+    const uint16_t* ap[3] = {nullptr, nullptr, nullptr};
+    const bool in_place = P == 1 ? lora_a_in_place(r, {a[0]}) : lora_a_in_place(r, {a[0], a[1], a[2]});
+    if (in_place) {
+      for (int p = 0; p < P; ++p) ap[p] = u16(a[p]);
+    } else {
+      lmx::TJobs t{};
+      t.n = P;
+      for (int p = 0; p < P; ++p) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(ws + L.apad) + int64_t(p) * 16 * JB * K;
+        t.job[p] = {u16(a[p]), K, dst, K, 16 * JB, int(K), 0, int(K), r, 1.0f, true};
+        ap[p] = dst;
+      }
+      if (lmx::launch_small_transposes(t, st) != hipSuccess) return LORA_EHIP;
+    }
+    lmx::SumJobs j = L.xs;
+    j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].ldr = K;
+    for (int p = 0; p < 3; ++p) j.job[0].R[p] = ap[p];
+    float* rowpart = reinterpret_cast<float*>(ws + L.rowpart);
+    if (lmx::launch_sums(j, rowpart, rowpart, st) != hipSuccess) return LORA_EHIP;
+    const int64_t rs = M * JB * 16;
+    const int nc = j.blk0[1] - j.blk0[0];
+    lmx::RedJobs rj{};
+    rj.n = P;
+    rj.JB = JB;
+    for (int p = 0; p < P; ++p) {
+      lmx::RedJob& q = rj.job[p];
+      q.src = rowpart + j.job[0].rp0 + p * nc * rs; q.pstride = rs; q.np = nc;
+      q.out = xa + p * rp; q.osa = P * rp; q.osj = 1; q.A = int(M); q.J = int(rp); q.r = r;
+      q.scale = 1.0f;
+    }
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
   }
   // 3. out_p = round(x W_p^T + s xa_p B_p^T) with LoRA in K: one launch over the P column
   //    groups (query, key and value share the pass over x and fill the chip together), or the
@@ -549,8 +572,8 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   const bool aligned = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
   const bool gemv = kn.family == 2 && dtype != LORA_F32 && aligned && K % 8 == 0;
   const bool lds = !gemv && dtype != LORA_F32 && aligned && K % 8 == 0 &&
-                   prefer_lds_pub(kn, int(dtype), T, K, S, R, G);
-  const ShrinkWs ws = shrink_ws(kn, int(dtype), T, K, S, R, G, lds, true, gemv);
+                   prefer_lds(kn, int(dtype), T, K, S, R, G);
+  const ShrinkWs ws = shrink_ws(kn, int(dtype), T, K, S, R, G, lds, gemv);
   const int variant = ws.variant;
   const int bm = ws.bm;
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total)) return LORA_EWORKSPACE;
@@ -612,10 +635,10 @@ size_t lora_shrink_workspace_size_ex(lora_dtype dtype, int64_t T, int64_t K, int
   if (!knobs_valid(kn)) return 0;
   // the kernel family depends on pointer alignment, which the query does not see: cover each
   // family the call may take
-  const size_t reg = shrink_ws(kn, int(dtype), T, K, S, R, G, false, true).total;
+  const size_t reg = shrink_ws(kn, int(dtype), T, K, S, R, G, false).total;
   if (dtype == LORA_F32 || K % 8 != 0 || kn.family == 0) return reg;
-  if (kn.family == 2) return std::max(reg, shrink_ws(kn, int(dtype), T, K, S, R, G, false, true, true).total);
-  return std::max(reg, shrink_ws(kn, int(dtype), T, K, S, R, G, true, true).total);
+  if (kn.family == 2) return std::max(reg, shrink_ws(kn, int(dtype), T, K, S, R, G, false, true).total);
+  return std::max(reg, shrink_ws(kn, int(dtype), T, K, S, R, G, true).total);
 }
 
 size_t lora_shrink_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
@@ -807,22 +830,43 @@ lora_status mlp_forward(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32
     jobs.job[2] = {u16(b_down), r, lb_d, rp, int(H), 0};
     if ((e = lmx::launch_scale_lora_b(jobs, scale, r, st)) != hipSuccess) return LORA_EHIP;
   }
-  // 2. [xa_g | xa_u] = round(x [A_g; A_u]^T), ranks padded with zeros to rp
-  {
-    lmx::ShrinkArgs a{};
-    a.x = x; a.ldx = ldx; a.K = H; a.S = 2; a.R = int(rp); a.G = 1; a.T = int(M);
-    a.dense_rank = r; a.w_a_slice[0] = a_gate; a.w_a_slice[1] = a_up; a.w_a = a_gate; a.lda = H;
-    a.h = xa_gu; a.ldh = 2 * rp;
-    // x is 16-byte aligned with a 16-byte row stride (checked above); A rows are H long, H % 32 == 0
-    const bool al = al16(a_gate) && al16(a_up);
-    const ShrinkWs& sp = al ? L.s_gu : L.r_gu;
-    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp; a.sk_unit = sp.unit;
-    a.part = reinterpret_cast<float*>(ws + L.part);
-    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
-    if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
-    if (sp.q > 0 && (e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st)) != hipSuccess)
-      return LORA_EHIP;
+  // LoRA-A operands for the sums kernel: in place, or zero-padded copies (rank rows past r)
+  const int JB = L.gu.JB;
+  const uint16_t *ag = u16(a_gate), *au = u16(a_up), *ad = u16(a_down);
+  if (!lora_a_in_place(r, {a_gate, a_up, a_down})) {
+    uint16_t* pad = reinterpret_cast<uint16_t*>(ws + L.apad);
+    uint16_t *pg = pad, *pu = pad + int64_t(16 * JB) * H, *pd = pad + int64_t(16 * JB) * 2 * H;
+    lmx::TJobs t{};
+    t.n = 3;
+    t.job[0] = {ag, H, pg, H, 16 * JB, int(H), 0, int(H), r, 1.0f, true};
+    t.job[1] = {au, H, pu, H, 16 * JB, int(H), 0, int(H), r, 1.0f, true};
+    t.job[2] = {ad, I, pd, I, 16 * JB, int(I), 0, int(I), r, 1.0f, true};
+    if ((e = lmx::launch_small_transposes(t, st)) != hipSuccess) return LORA_EHIP;
+    ag = pg; au = pu; ad = pd;
   }
+  float* rowpart = reinterpret_cast<float*>(ws + L.rowpart);
+  // h = round(P A^T) of rp padded columns (zeros past r) from the sums kernel's row side
+  auto lora_a = [&](const lmx::SumJobs& plan, const uint16_t* P, int64_t ldp, int64_t C,
+                    const uint16_t* A0, const uint16_t* A1, uint16_t* h, int64_t ldh) -> bool {
+    lmx::SumJobs j = plan;
+    j.job[0].P = P; j.job[0].ldp = ldp; j.job[0].ldr = C;
+    j.job[0].R[0] = A0; j.job[0].R[1] = A1; j.job[0].R[2] = nullptr;
+    if (lmx::launch_sums(j, rowpart, rowpart, st) != hipSuccess) return false;
+    const int64_t rs = M * JB * 16;
+    const int nc = j.blk0[1] - j.blk0[0];
+    lmx::RedJobs rj{};
+    rj.n = j.job[0].nr;
+    rj.JB = JB;
+    for (int q = 0; q < rj.n; ++q) {
+      lmx::RedJob& o = rj.job[q];
+      o.src = rowpart + j.job[0].rp0 + q * nc * rs; o.pstride = rs; o.np = nc;
+      o.out = h + q * rp; o.osa = ldh; o.osj = 1; o.A = int(M); o.J = int(rp); o.r = r;
+      o.scale = 1.0f;
+    }
+    return lmx::launch_reduce_sums(rj, st) == hipSuccess;
+  };
+  // 2. [xa_g | xa_u] = round(x [A_g; A_u]^T), ranks padded with zeros to rp (one pass over x)
+  if (!lora_a(L.gu, u16(x), ldx, H, ag, au, xa_gu, 2 * rp)) return LORA_EHIP;
   // 3. hmid = round(silu(x W_g^T + s xa_g B_g^T) * (x W_u^T + s xa_u B_u^T))
   {
     lmx::GemmArgs g{};
@@ -834,20 +878,7 @@ lora_status mlp_forward(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32
     if ((e = lmx::launch_gemm_lora(g, mode, st)) != hipSuccess) return LORA_EHIP;
   }
   // 4. xa_d = round(hmid A_d^T)
-  {
-    lmx::ShrinkArgs a{};
-    a.x = hmid; a.ldx = I; a.K = I; a.S = 1; a.R = int(rp); a.G = 1; a.T = int(M);
-    a.dense_rank = r; a.w_a_slice[0] = a_down; a.w_a = a_down; a.lda = I;
-    a.h = xa_d; a.ldh = rp;
-    const bool al = al16(a_down);
-    const ShrinkWs& sp = al ? L.s_d : L.r_d;
-    a.sk_q = sp.q; a.sk_tiles = int(sp.bound); a.sk_mp = sp.mp; a.sk_unit = sp.unit;
-    a.part = reinterpret_cast<float*>(ws + L.part);
-    lmx::ShrinkPlan plan{sp.variant, sp.grid_x, al, sp.lds};
-    if ((e = lmx::launch_shrink(LORA_BF16, a, plan, st)) != hipSuccess) return LORA_EHIP;
-    if (sp.q > 0 && (e = lmx::launch_shrink_sk_reduce(LORA_BF16, a, sp.bm, st)) != hipSuccess)
-      return LORA_EHIP;
-  }
+  if (!lora_a(L.dn, hmid, I, I, ad, nullptr, xa_d, rp)) return LORA_EHIP;
   // 5. out = round(hmid W_d^T + s xa_d B_d^T)
   {
     lmx::GemmArgs g{};
@@ -942,7 +973,7 @@ lora_status lora_mlp_backward(lora_dtype dtype, int64_t M, int64_t H, int64_t I,
   float* colpart = reinterpret_cast<float*>(ws + L.colpart);
   auto sum_job = [](lmx::SumJob& j, const uint16_t* P, int64_t ldp, const uint16_t* R0,
                     const uint16_t* R1, const uint16_t* Q0, const uint16_t* Q1, int64_t ldq) {
-    j.P = P; j.ldp = ldp; j.R[0] = R0; j.R[1] = R1; j.ldr = j.C;
+    j.P = P; j.ldp = ldp; j.R[0] = R0; j.R[1] = R1; j.R[2] = nullptr; j.ldr = j.C;
     j.Q[0] = Q0; j.Q[1] = Q1; j.ldq = ldq;
   };
   auto red_job = [](lmx::RedJob& j, const float* src, int64_t pstride, int np, void* out,

@@ -89,7 +89,7 @@ hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int
 // operands, one per column 8t + i, each holding that column's four rows; B is the heads' Q rows
 // 4g .. 4g+3 at rank column t. MFMA i thus sums P[m][8t + i] Q[m][j] over the step's rows for
 // t = 0..15, and its accumulator lives for the whole chunk.
-// Row side, R_h for h < nr <= 2 (v_mfma_f32_16x16x32_bf16): A is the step's 16 rows with 32
+// Row side, R_h for h < nr <= 3 (v_mfma_f32_16x16x32_bf16): A is the step's 16 rows with 32
 // columns per k block, B the R_h rows (rank) over the same columns, held in registers for the
 // whole chunk; each wave's sum over its 128 columns goes to LDS and the next step adds the 4
 // waves in order and stores the block's partial row.
@@ -105,7 +105,7 @@ constexpr int kSumStages = 3;
 constexpr int kSumPitch = kSumCols * 2 + 16;               // bytes per LDS row of P
 constexpr int kSumQOff = kSumRows * kSumPitch;             // Q rows: [16][2 heads][16] bf16
 constexpr int kSumStageBytes = kSumQOff + kSumRows * 64;
-constexpr int kSumRedBytes = 2 * 2 * kSumWaves * 256 * 4;  // row-side sums: 2 steps x 2 heads
+constexpr int kSumRedBytes = 2 * 3 * kSumWaves * 256 * 4;  // row-side sums: 2 steps x 3 heads
 constexpr int kSumPLoads = kSumRows / kSumWaves;           // P loads per wave and step
 
 __device__ __forceinline__ f32x4_t mma16x16x16(uint2 a, uint2 b, f32x4_t c) {
@@ -185,9 +185,9 @@ __global__ __launch_bounds__(kSumThreads) void sums_kernel(SumJobs jobs, float* 
 
   // row side: rows 16 jbk + t of each R over the wave's columns, k block kb = columns
   // 32 kb + 8 g ..
-  uint4 rreg[2][4];
+  uint4 rreg[3][4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < 3; ++h) {
     if (h < jb.nr) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -209,9 +209,9 @@ __global__ __launch_bounds__(kSumThreads) void sums_kernel(SumJobs jobs, float* 
     const int rho = tid >> 4, j = tid & 15;
     const int m = m0 + kSumRows * s + rho;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 3; ++h) {
       if (h < jb.nr) {
-        const float* rr = red + ((s & 1) * 2 + h) * kSumWaves * 256 + (j + 16 * (rho >> 2)) * 4 + (rho & 3);
+        const float* rr = red + ((s & 1) * 3 + h) * kSumWaves * 256 + (j + 16 * (rho >> 2)) * 4 + (rho & 3);
         float sum = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kSumWaves; ++ww) sum += rr[ww * 256];
@@ -274,19 +274,20 @@ __global__ __launch_bounds__(kSumThreads) void sums_kernel(SumJobs jobs, float* 
 
     // row side
     if (jb.nr > 0) {
-      f32x4_t ar[2] = {f32x4_t{}, f32x4_t{}};
+      f32x4_t ar[3] = {f32x4_t{}, f32x4_t{}, f32x4_t{}};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         if (cw + 32 * kb < C) {  // uniform
           const uint4 a = *reinterpret_cast<const uint4*>(st + t * kSumPitch + (128 * w + 32 * kb + 8 * g) * 2);
           ar[0] = mma_step<DT_BF16>(a, rreg[0][kb], ar[0]);
           if (jb.nr > 1) ar[1] = mma_step<DT_BF16>(a, rreg[1][kb], ar[1]);
+          if (jb.nr > 2) ar[2] = mma_step<DT_BF16>(a, rreg[2][kb], ar[2]);
         }
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 3; ++h)
         if (h < jb.nr)
-          *reinterpret_cast<f32x4_t*>(red + (((s & 1) * 2 + h) * kSumWaves + w) * 256 + lane * 4) = ar[h];
+          *reinterpret_cast<f32x4_t*>(red + (((s & 1) * 3 + h) * kSumWaves + w) * 256 + lane * 4) = ar[h];
       if (s > 0) store_rows(s - 1);
     }
   }

@@ -8,14 +8,14 @@
 // Launches on the caller's stream:
 //   1. the scaled LoRA-B operands s*B_g, s*B_u, s*B_d in bf16, zero padded (small; exact when s
 //      is a power of two, as alpha / rank usually is);
-//   2. LoRA-A products of x for gate and up (the dense mode of the shrink kernel, both slices in
-//      one pass over x) -> xa_gu [M][2*rp] = [xa_g | xa_u] (rp = rank rounded up to 32);
+//   2. LoRA-A products of x for gate and up (the row side of the sums kernel, both in one pass
+//      over x, and its reduce) -> xa_gu [M][2*rp] = [xa_g | xa_u] (rp = rank rounded up to 32);
 //   3. gate/up GEMM over K = H + 2*rp: the last 2*rp reduction columns are [xa_g | xa_u] against
 //      [s*B_g | 0] for gate rows and [0 | s*B_u] for up rows, so the LoRA term accumulates with
 //      the base product. One workgroup computes 256 rows x 128 output columns of BOTH
 //      projections (its B tile holds the 128 gate rows then the 128 up rows), so every lane
 //      holds g and u of the same outputs and the epilogue stores hmid = silu(g) * u in bf16;
-//   4. LoRA-A product of hmid for down -> xa_d [M][rp];
+//   4. LoRA-A product of hmid for down (sums kernel and reduce) -> xa_d [M][rp];
 //   5. down GEMM over K = I + rp -> out.
 //
 // GEMM main loop: 256x256x32 block stages (128x256 in the plain mode when shorter tiles finish

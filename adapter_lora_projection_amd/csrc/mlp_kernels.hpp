@@ -96,7 +96,7 @@ hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int
 
 // Sums over one pass of a bf16 matrix P [M][C] (row pitch ldp), up to 4 matrices per launch, in
 // fp32:
-//   row side, R_h for h < nr <= 2:   Drow_h[m][j] = sum_c P[m][c] R_h[j][c]   (R_h [16 JB][C], pitch ldr)
+//   row side, R_h for h < nr <= 3:   Drow_h[m][j] = sum_c P[m][c] R_h[j][c]   (R_h [16 JB][C], pitch ldr)
 //   column side, Q_h for h < nh <= 2: Dcol_h[c][j] = sum_m P[m][c] Q_h[m][j]   (Q_h [M], pitch ldq)
 // for j < 16 JB, JB = the launch's rank blocks of 16; nr + nh >= 1. Results are partial sums:
 // the row side per block of 512 columns, rowpart + rp0 + h * (ncb * M * JB * 16):
@@ -106,7 +106,7 @@ hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int
 struct SumJob {
   const uint16_t* P;
   int64_t ldp;
-  const uint16_t* R[2];
+  const uint16_t* R[3];
   int64_t ldr;
   const uint16_t* Q[2];
   int64_t ldq;

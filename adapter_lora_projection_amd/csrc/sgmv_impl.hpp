@@ -33,35 +33,18 @@ namespace lmx {
 
 // ------------------------------------------------------------------------------------ shrink
 
-// Tile t of a shrink call: from the segment schedule, or rows [t*BM, (t+1)*BM) of the single
-// dense segment (internal mode, seg_indptr null). Every thread must call it. The adapter's rank
-// is loaded after the search and first needed by the stores: operand loads read the padded rank
-// (shrink_rows) and do not wait for it.
+// Tile t of a shrink call, from the segment schedule. Every thread must call it. The adapter's
+// rank is loaded after the search and first needed by the stores: operand loads read the padded
+// rank (every padded row of the stacked A exists; rows at or past the adapter's rank only feed
+// outputs that are stored as zeros) and do not wait for it.
 template <int NT>
 __device__ __forceinline__ Tile shrink_tile(const ShrinkArgs& p, int BM, int t, Tile* s_tile,
                                             int* s_scan) {
-  Tile tile;
-  if (p.seg_indptr != nullptr) {
-    get_tile<NT, false>(p.seg_indptr, p.weight_indices, p.lora_ranks, nullptr, p.G, BM, p.tiles,
-                        p.tile_count, t, s_tile, s_scan);
-    tile = *s_tile;
-    if (tile.g >= 0) tile_rank(p.lora_ranks, nullptr, &tile);
-  } else {
-    tile.g = t * BM < p.T ? 0 : -1;
-    tile.m0 = t * BM;
-    tile.mlen = min(BM, p.T - tile.m0);
-    tile.a = 0;
-    tile.r = p.dense_rank;
-    tile.sigma = 0.f;
-  }
+  get_tile<NT, false>(p.seg_indptr, p.weight_indices, p.lora_ranks, nullptr, p.G, BM, p.tiles,
+                      p.tile_count, t, s_tile, s_scan);
+  Tile tile = *s_tile;
+  if (tile.g >= 0) tile_rank(p.lora_ranks, nullptr, &tile);
   return tile;
-}
-
-// A rows of each slice the operand loads may read: the padded rank R when A is the stacked
-// [L][S*R][K] array (every padded row exists; rows at or past the adapter's rank only feed
-// outputs that are stored as zeros), the true rank for the per-slice A arrays of dense mode.
-__device__ __forceinline__ int shrink_rows(const ShrinkArgs& p, const Tile& tile) {
-  return p.seg_indptr != nullptr ? p.R : tile.r;
 }
 
 // Planes of tile t in a shared-work shrink: its (tile, step) units [t * nunits, (t+1) * nunits)
@@ -164,7 +147,7 @@ __device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& ti
   const int lane = threadIdx.x & 63, w = wave_id();
   const int li = lane & 15, lg = lane >> 4;
   const int a = tile.a;
-  const int r = shrink_rows(p, tile);
+  const int r = p.R;  // rows of A the loads may read (the rank applies in the stores)
   const int NB = (p.R + 15) >> 4;  // 16-column blocks per slice
   const int nblk = p.S * NB;
   const int K = int(p.K);
@@ -194,13 +177,7 @@ __device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& ti
     col_ok[cb] = (blk < nblk) && (j < r);
     any_col |= (blk < nblk) && (16 * b < r);
     const int ss = blk < nblk ? s : 0;
-    // (a constant-index selection: a runtime index into the argument block would make the
-    // compiler copy the whole block to scratch memory)
-    const void* own = nullptr;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) own = (ss == q) ? p.w_a_slice[q] : own;
-    const S* slice_base = own != nullptr ? reinterpret_cast<const S*>(own)
-                                         : wa + int64_t(a * p.S + ss) * p.R * p.lda;
+    const S* slice_base = wa + int64_t(a * p.S + ss) * p.R * p.lda;
     arow[cb] = slice_base + int64_t(col_ok[cb] ? j : 0) * p.lda;
   }
 

@@ -18,12 +18,7 @@ struct ShrinkArgs {
   const int* tile_count;  // its length (device), when tiles is non-null
   int64_t K, ldx, lda, ldh;
   int S, R, G;
-  // Internal dense mode (used by the fused MLP): seg_indptr == nullptr means one segment over
-  // all T rows with adapter 0 of rank `dense_rank`; permutation == nullptr means identity; a
-  // non-null w_a_slice[s] replaces the stacked layout for slice s (R rows of stride lda).
-  int T;
-  int dense_rank;
-  const void* w_a_slice[4];
+  int T;  // tokens (rows of x and of h); permutation == nullptr means the identity
   // Stream-K mode when sk_q > 0: the work [0, sk_tiles * steps) is cut into ranges of sk_q
   // steps, one per workgroup x; the pieces go to part[plane < sk_mp][T][S*R] (fp32, rows by
   // sorted position) and launch_shrink_sk_reduce adds them into h.

@@ -11,8 +11,8 @@
 // instructions (v_dot2, fp32 sums); the 64 partial sums of each product are then added across
 // the wave with butterfly shuffles in a fixed order, and lane 0 of each 16-lane group rounds and
 // stores. Requires 16-byte aligned x and A rows and K a multiple of 8 (the host checks); rows
-// past the tile and rank columns past the adapter's rank read a valid row whose products are
-// never stored.
+// past the tile and rank columns past the padded rank read a valid row whose products are never
+// stored (columns at or past the adapter's rank are stored as zeros).
 #include "sgmv_impl.hpp"  // shrink_tile
 
 namespace lmx {
@@ -60,15 +60,11 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(ShrinkArgs p) {
   }
   const S* arow[CPW];
   {
-    const void* own = nullptr;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) own = (s == q) ? p.w_a_slice[q] : own;
-    const S* base = own != nullptr ? reinterpret_cast<const S*>(own)
-                                   : wa + int64_t(tile.a * p.S + s) * p.R * p.lda;
+    const S* base = wa + int64_t(tile.a * p.S + s) * p.R * p.lda;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int j = 16 * b + CPW * w + c;
-      arow[c] = base + int64_t(j < shrink_rows(p, tile) ? j : 0) * p.lda;
+      arow[c] = base + int64_t(j < p.R ? j : 0) * p.lda;
     }
   }
 
@@ -77,7 +73,7 @@ __global__ __launch_bounds__(256) void shrink_gemv_kernel(ShrinkArgs p) {
   for (int t = 0; t < BM; ++t)
 #pragma unroll
     for (int c = 0; c < CPW; ++c) acc[t][c] = 0.f;
-  if (16 * b + CPW * w < shrink_rows(p, tile)) {  // uniform per wave: a column inside the rows
+  if (16 * b + CPW * w < p.R) {  // uniform per wave: this wave has a column inside the padded rank
     for (int k = 8 * lane; k < K; k += 512) {
       uint4 av[CPW], xv[BM];
 #pragma unroll

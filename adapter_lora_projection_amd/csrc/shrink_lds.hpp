@@ -11,8 +11,8 @@
 // bank-conflict free. Each of the 4 waves owns BMG / 4 groups of 16 positions across all NC
 // columns: no reduction between waves, and every A chunk loaded is shared by the whole tile.
 //
-// Rows past the tile and rank columns past the A rows that exist (shrink_rows) load a valid row
-// of the same operand (their outputs are never stored); reduction indices past K load a block of zeros.
+// Rows past the tile and rank columns past the padded rank load a valid row of the same operand
+// (their outputs are never stored; rows at or past the adapter's rank are stored as zeros); reduction indices past K load a block of zeros.
 // Requires 16-byte aligned x and A rows and K a multiple of 8 (the host checks).
 //
 // Work split: direct (sk_q == 0, one workgroup per tile over all of K) or shared (the
@@ -87,14 +87,9 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
         const int blk = int(blockIdx.y) * NCB + (n >> 4);
         const int s = blk / NB, b = blk - (blk / NB) * NB;
         const int j = 16 * b + (n & 15);
-        const bool ok = blk < nblk && j < shrink_rows(p, tile);
+        const bool ok = blk < nblk && j < p.R;
         const int ss = ok ? s : 0;
-        const void* own = nullptr;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) own = (ss == q) ? p.w_a_slice[q] : own;
-        const S* slice_base = own != nullptr ? reinterpret_cast<const S*>(own)
-                                             : wa + int64_t(tile.a * p.S + ss) * p.R * p.lda;
-        src[ii] = slice_base + int64_t(ok ? j : 0) * p.lda;
+        src[ii] = wa + (int64_t(tile.a * p.S + ss) * p.R + (ok ? j : 0)) * p.lda;
       }
     }
     // Reduction indices past K read a block of zeros (both operands, so no garbage enters).
