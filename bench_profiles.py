@@ -110,7 +110,7 @@ def label_dispatches(disp: list[tuple[str, tuple]]) -> list[str]:
         i += 1
     labels, in_sweep = [], True
     for name, grid in disp:
-        if "gemm_lora_kernel" in name or "embedding" in name or "colred" in name or "scale_lora_b" in name:
+        if "gemm_lora_kernel" in name or "embedding" in name or "sums_kernel" in name or "scale_lora_b" in name:
             in_sweep = False
         if in_sweep and (name, grid) in keymap:
             labels.append(" / ".join(keymap[(name, grid)]))
@@ -224,7 +224,7 @@ def main() -> int:
     mf = counter_per_label(os.path.join(d, "pmc_mfma", "m_counter_collection.csv"))
     lines = ["| kernel | workgroups | workload | median MfmaUtil % |", "|---|---:|---|---:|"]
     for (name, grid, lab), v in sorted(mf.items(), key=lambda kv: kv[0][0]):
-        if "gemm" in name or "colred" in name or "shrink_lds" in name:
+        if "gemm" in name or "sums_kernel" in name or "shrink_lds" in name:
             lines.append(f"| `{name}` | {grid[0] * grid[1]} | {lab} | {v:.1f} |")
     with open(os.path.join(HERE, "profiles", "mfma_utilisation.md"), "w") as f:
         f.write("# MFMA utilisation of the GEMM launches: fused MLP forward, training forward, backward, "
