@@ -601,7 +601,7 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   if (ws.q > 0) a.part = reinterpret_cast<float*>(wsb + ws.part);
   if (ws.q > 0 && ws.in_launch) a.counters = reinterpret_cast<int*>(wsb);
 #ifndef LMX_NO_XCD_ROWS
-  if (!ws.lds && !ws.gemv && ws.q == 0 && ws.gy > 1) a.xcd_rows = ws.gy;
+  if (!ws.gemv && ws.q == 0 && (ws.lds || ws.gy > 1)) a.xcd_rows = ws.gy;
 #endif
   lmx::ShrinkPlan splan{variant, ws.grid_x, aligned, ws.lds, ws.gemv};
   if (lmx::launch_shrink(int(dtype), a, splan, st) != hipSuccess) return LORA_EHIP;

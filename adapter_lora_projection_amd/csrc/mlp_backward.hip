@@ -119,7 +119,7 @@ void plan_sums(SumJobs& j, int target, int64_t* row_floats, int64_t* col_floats)
   j.blk0[0] = 0;
   for (int q = 0; q < j.n; ++q) j.blk0[q + 1] = j.blk0[q] + (j.job[q].C + kSumCols - 1) / kSumCols;
   const int blocks = j.blk0[j.n] * j.JB;
-  const int steps = (j.M + kSumRows - 1) / kSumRows;
+  const int steps = std::max(1, (j.M + kSumRows - 1) / kSumRows);
   int chunks = std::max(1, (target + blocks / 2) / std::max(blocks, 1));
   chunks = std::min(chunks, steps);
   j.rows_per = ((steps + chunks - 1) / chunks) * kSumRows;

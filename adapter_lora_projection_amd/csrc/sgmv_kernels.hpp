@@ -30,8 +30,9 @@ struct ShrinkArgs {
   // exit; the last workgroup to store a piece of a tile adds the tile's planes into h in the
   // same launch (no launch_shrink_sk_reduce).
   int* counters;
-  // Register-ring direct mode only: > 0 launches a one-dimensional grid that gives the xcd_rows
-  // column-block groups of a tile to consecutive workgroups of one XCD (0: a 2-D grid).
+  // Direct mode only (register-ring and LDS-staged kernels): > 0 launches a one-dimensional grid
+  // that gives each XCD a contiguous range of tiles, the xcd_rows column-block groups of a tile
+  // on consecutive workgroups of that XCD (0: a 2-D grid).
   int xcd_rows;
 };
 

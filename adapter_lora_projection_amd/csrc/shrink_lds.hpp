@@ -62,8 +62,9 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
   // this wave's load instructions per stage (uniform: the waits below are immediates)
   const bool hi = (TOT % NW == 0) || w < TOT % NW;
 
-  // One piece: stages [u0, u1) of `tile`; the sums go to h (slot == nullptr) or a partial plane.
-  auto piece = [&](const Tile& tile, int64_t u0, int64_t u1, float* slot) {
+  // One piece: stages [u0, u1) of `tile` for column-block group `by`; the sums go to h
+  // (slot == nullptr) or a partial plane.
+  auto piece = [&](const Tile& tile, int by, int64_t u0, int64_t u1, float* slot) {
     // DMA sources of this lane: instruction i = w + NW * ii fills stage rows 8 i .. 8 i + 7;
     // this lane writes row rb = 8 i + lane / 8, 16-byte slot lane % 8, which holds chunk
     // (lane % 8) ^ (rb % 8) of the source row. A row past the tile or past the adapter's rank
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
         src[ii] = x + int64_t(tok) * p.ldx;
       } else if (i < TOT) {
         const int n = rb - BM;
-        const int blk = int(blockIdx.y) * NCB + (n >> 4);
+        const int blk = by * NCB + (n >> 4);
         const int s = blk / NB, b = blk - (blk / NB) * NB;
         const int j = 16 * b + (n & 15);
         const bool ok = blk < nblk && j < p.R;
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
       if (m >= tile.mlen) continue;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int blk = int(blockIdx.y) * NCB + cb;
+        const int blk = by * NCB + cb;
         if (blk >= nblk) continue;
         const int s = blk / NB, b = blk - (blk / NB) * NB;
         if (slot != nullptr) {
@@ -179,9 +180,20 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
   };
 
   if (p.sk_q == 0) {
-    const Tile tile = shrink_tile<NT>(p, BM, int(blockIdx.x), &s_tile, s_scan);
+    // Direct mode; with p.xcd_rows > 0 the grid is one-dimensional and workgroup L (which runs
+    // on XCD L % 8) takes tile (L % 8) * tpx + (L / 8) / xcd_rows, grid row (L / 8) % xcd_rows:
+    // each XCD a contiguous eighth of the segment-major tiles, so the tiles of one segment
+    // (one adapter's A rows) read them from one or two XCDs' L2.
+    int tx = int(blockIdx.x), by = int(blockIdx.y);
+    if (p.xcd_rows > 0) {
+      const int Lw = int(blockIdx.x);
+      const int tpx = (int(gridDim.x) / 8) / p.xcd_rows;
+      tx = (Lw % 8) * tpx + (Lw / 8) / p.xcd_rows;
+      by = (Lw / 8) % p.xcd_rows;
+    }
+    const Tile tile = shrink_tile<NT>(p, BM, tx, &s_tile, s_scan);
     if (tile.g < 0) return;
-    piece(tile, 0, nunits, nullptr);
+    piece(tile, by, 0, nunits, nullptr);
     return;
   }
   const int64_t units = int64_t(p.sk_tiles) * nunits;
@@ -195,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
     if (tile.g < 0) break;  // past the last tile (uniform over the workgroup)
     const int j = int(blockIdx.x) - int((int64_t(t) * nunits) / p.sk_q);
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
-    piece(tile, k0, k1, slot);  // (a rank-0 tile stores nothing)
+    piece(tile, int(blockIdx.y), k0, k1, slot);  // (a rank-0 tile stores nothing)
     if (p.counters != nullptr)
       sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, int(blockIdx.y),
                          int(gridDim.y), &s_last);
@@ -225,11 +237,19 @@ template <int DT>
 hipError_t launch_shrink_lds_dt(const ShrinkArgs& a, const ShrinkPlan& plan, hipStream_t st) {
   const int NB = (a.R + 15) / 16;
   const int nblk = a.S * NB;
+  // direct mode with XCD-contiguous tiles (see the kernel): a one-dimensional grid
+  auto grid = [&](int ncb) {
+    const int gy = (nblk + ncb - 1) / ncb;
+    if (a.xcd_rows > 0) return dim3(unsigned((plan.grid_x + 7) / 8 * 8 * gy), 1);
+    return dim3(unsigned(plan.grid_x), unsigned(gy));
+  };
+  if (a.xcd_rows > 0 && a.sk_q != 0) return hipErrorInvalidValue;
   switch (plan.variant) {
 #define X(V, BMG, NCB, NS, NW)                                                               \
     case V:                                                                                  \
-      hipLaunchKernelGGL((shrink_lds_kernel<DT, BMG, NCB, NS, NW>),                         \
-                         dim3(plan.grid_x, (nblk + NCB - 1) / NCB), dim3(NW * 64), 0, st, a); \
+      if (a.xcd_rows > 0 && a.xcd_rows != (nblk + NCB - 1) / NCB) return hipErrorInvalidValue; \
+      hipLaunchKernelGGL((shrink_lds_kernel<DT, BMG, NCB, NS, NW>), grid(NCB), dim3(NW * 64), 0, \
+                         st, a);                                                             \
       return hipGetLastError();
     LMX_SHRINK_LDS_VARIANTS(X)
 #undef X
