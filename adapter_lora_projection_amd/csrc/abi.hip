@@ -258,8 +258,12 @@ ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, 
   bool shared;
   int64_t pdef;
   if (w.in_launch) {
+    // eight pieces per tile: every piece lies inside one tile when the step count divides by 8
+    // (pieces that straddle two tiles pay two searches and two completions; rocprofv3, each call
+    // after a 512 MiB write: 128 tokens, 12 tiles, 96 workgroups per grid row 10.9 us against
+    // 13.0 us for 64 and 15.2 us for 128; 50 tokens, 8 tiles, 64 workgroups 9.9 us)
     shared = !lds && direct_wgs < 48;
-    pdef = std::max<int64_t>(1, 192 / gy);
+    pdef = std::max<int64_t>(1, w.bound * 8);
   } else {
     shared = lds ? direct_wgs < 256
                  : direct_wgs < 128 && nsteps * frags * 1024 >= (int64_t(512) << 10);
