@@ -258,12 +258,18 @@ ShrinkWs shrink_ws(const Knobs& kn, int dtype, int64_t T, int64_t K, int32_t S, 
   bool shared;
   int64_t pdef;
   if (w.in_launch) {
-    // eight pieces per tile: every piece lies inside one tile when the step count divides by 8
-    // (pieces that straddle two tiles pay two searches and two completions; rocprofv3, each call
-    // after a 512 MiB write: 128 tokens, 12 tiles, 96 workgroups per grid row 10.9 us against
-    // 13.0 us for 64 and 15.2 us for 128; 50 tokens, 8 tiles, 64 workgroups 9.9 us)
-    shared = !lds && direct_wgs < 48;
-    pdef = std::max<int64_t>(1, w.bound * 8);
+    // k = 2, 4 or 8 pieces per tile (every piece inside one tile when the step count divides by
+    // k: pieces that straddle two tiles pay two searches and two completions), the largest with
+    // at most about 320 workgroups; direct below 2. rocprofv3, each call after a 512 MiB write
+    // (decode sweep, 3 column blocks): 50 tokens k = 8, 192 workgroups 9.9 us; 128 tokens k = 8,
+    // 288 workgroups 10.9 us (64 per grid row, straddling: 13.0 us); 256 tokens k = 4, 240
+    // workgroups 10.1 us (direct 12.9 us, k = 8 11.3 us); 512 tokens k = 2, 216 workgroups
+    // 12.2 us (direct 13.3 us); 1024 tokens direct 13.5 us (k = 2: 17.3 us).
+    int64_t k = 1;
+    if (!lds)
+      while (k < 8 && direct_wgs * k * 2 <= 320) k *= 2;
+    shared = k > 1;
+    pdef = w.bound * k;
   } else {
     shared = lds ? direct_wgs < 256
                  : direct_wgs < 128 && nsteps * frags * 1024 >= (int64_t(512) << 10);
