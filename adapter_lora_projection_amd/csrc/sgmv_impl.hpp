@@ -105,26 +105,50 @@ __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, i
   const int W = nb * 16;
   const int n = tile.mlen * W;
   const int64_t plane = int64_t(p.T) * SR;
-  for (int e = int(threadIdx.x); e < n; e += NT) {
-    const int m = e / W, rem = e - (e / W) * W;
-    const int blk = b0 + (rem >> 4);
-    const int s = blk / NB, c = 16 * (blk - (blk / NB) * NB) + (rem & 15);
-    if (c >= p.R) continue;
-    S v = S(0);
-    if (c < tile.r) {
-      const float* src = p.part + int64_t(tile.m0 + m) * SR + s * p.R + c;
-      float acc = 0.f;
-      for (int q0 = 0; q0 < np; q0 += 8) {
-        float b[8];
+  // EU outputs per thread per pass with all their plane loads in flight (the loads go to the
+  // device coherence point; one output at a time would pay a full memory round trip each)
+  constexpr int EU = 4;
+  for (int e0 = int(threadIdx.x); e0 < n; e0 += NT * EU) {
+    int64_t off[EU], hoff[EU];
+    bool live[EU], has[EU];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = (q0 + i < np) ? part_load(src + (q0 + i) * plane) : 0.f;
+    for (int u = 0; u < EU; ++u) {
+      const int e = e0 + u * NT;
+      live[u] = false;
+      has[u] = false;
+      off[u] = 0;
+      hoff[u] = 0;
+      if (e < n) {
+        const int m = e / W, rem = e - (e / W) * W;
+        const int blk = b0 + (rem >> 4);
+        const int s = blk / NB, c = 16 * (blk - (blk / NB) * NB) + (rem & 15);
+        if (c < p.R) {
+          live[u] = true;
+          has[u] = c < tile.r;
+          off[u] = int64_t(tile.m0 + m) * SR + s * p.R + c;
+          hoff[u] = int64_t(tile.m0 + m) * p.ldh + s * p.R + c;
+        }
+      }
+    }
+    float acc[EU];
+#pragma unroll
+    for (int u = 0; u < EU; ++u) acc[u] = 0.f;
+    for (int q0 = 0; q0 < np; q0 += 8) {
+      float b[EU][8];
+#pragma unroll
+      for (int u = 0; u < EU; ++u)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (q0 + i < np) acc = (q0 + i == 0) ? b[i] : acc + b[i];
-      }
-      v = Tr::from_f32(acc);
+          b[u][i] = (has[u] && q0 + i < np) ? part_load(p.part + off[u] + (q0 + i) * plane) : 0.f;
+#pragma unroll
+      for (int u = 0; u < EU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (q0 + i < np) acc[u] = (q0 + i == 0) ? b[u][i] : acc[u] + b[u][i];
     }
-    reinterpret_cast<S*>(p.h)[int64_t(tile.m0 + m) * p.ldh + s * p.R + c] = v;
+#pragma unroll
+    for (int u = 0; u < EU; ++u)
+      if (live[u]) reinterpret_cast<S*>(p.h)[hoff[u]] = has[u] ? Tr::from_f32(acc[u]) : S(0);
   }
 }
 
