@@ -76,8 +76,13 @@ __device__ __forceinline__ float part_load(const float* q) {
 // the order of arrival (so the result does not depend on timing), rounds once, writes h with
 // exact zeros in the rank padding, and sets the counter back to zero, so every counter is zero
 // again when the launch ends. A rank-0 tile stores no pieces: its plane-0 workgroup writes its
-// zero rows.
-template <int DT, int NT>
+// zero rows. EU outputs per thread and pass keep their plane loads in flight together (the loads
+// go to the device coherence point; one output at a time pays a full memory round trip each):
+// the LDS-staged kernel's long tiles take 4, which took its 2048-token, four-piece split from
+// 26.8 to 19.1 us; the register ring takes 1, since the 32 extra load addresses doubled its
+// registers (78 -> 154 VGPRs, 6 -> 3 waves per SIMD) and its 288-workgroup decode grid at
+// 128 tokens then needed a second round (10.1 -> 13.6 us).
+template <int DT, int NT, int EU>
 __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, int np, int CBY,
                           int by, int ny, int* s_last) {
   using Tr = Traits<DT>;
@@ -105,9 +110,6 @@ __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, i
   const int W = nb * 16;
   const int n = tile.mlen * W;
   const int64_t plane = int64_t(p.T) * SR;
-  // EU outputs per thread per pass with all their plane loads in flight (the loads go to the
-  // device coherence point; one output at a time would pay a full memory round trip each)
-  constexpr int EU = 4;
   for (int e0 = int(threadIdx.x); e0 < n; e0 += NT * EU) {
     int64_t off[EU], hoff[EU];
     bool live[EU], has[EU];
@@ -397,8 +399,8 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
       store(tile, int(blockIdx.y), sums, slot);
     }
     if (p.counters != nullptr)
-      sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nsteps, p.sk_q), CB, int(blockIdx.y),
-                        int(gridDim.y), &s_last);
+      sk_finish<DT, NT, 1>(p, tile, t, j, sk_pieces(t, nsteps, p.sk_q), CB, int(blockIdx.y),
+                           int(gridDim.y), &s_last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }

@@ -209,8 +209,8 @@ __global__ __launch_bounds__(NW * 64) void shrink_lds_kernel(ShrinkArgs p) {
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
     piece(tile, int(blockIdx.y), k0, k1, slot);  // (a rank-0 tile stores nothing)
     if (p.counters != nullptr)
-      sk_finish<DT, NT>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, int(blockIdx.y),
-                         int(gridDim.y), &s_last);
+      sk_finish<DT, NT, 4>(p, tile, t, j, sk_pieces(t, nunits, p.sk_q), NCB, int(blockIdx.y),
+                            int(gridDim.y), &s_last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }
