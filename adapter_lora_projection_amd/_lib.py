@@ -41,6 +41,10 @@ SIGNATURES = {
     "lora_expand": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _i64,
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
     "lora_expand_workspace_size": (_sz, [_i32, _i64, _i32, _i32, _i32, _i64]),
+    "lora_shrink_expand": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp,
+                                  _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
+                                  _i64, _vp, _sz, _vp]),
+    "lora_shrink_expand_workspace_size": (_sz, [_i32, _i64, _i64, _i32, _i32, _i32, _i64]),
     "lora_schedule_tiles": (_i32, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                    _sz, _vp]),
     "lora_shrink_ex": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
@@ -184,6 +188,23 @@ def lora_expand(dtype, T, S, R, L, G, N, h, ldh, w_b, ldb, slice_offsets, seg_in
 
 def lora_expand_workspace_size(dtype, T, S, R, G, N) -> int:
     return int(lib().lora_expand_workspace_size(dtype, T, S, R, G, N))
+
+
+def lora_shrink_expand(dtype, T, K, S, R, L, G, N, x, ldx, w_a, lda, w_b, ldb, slice_offsets,
+                       seg_indptr, weight_indices, permutation, lora_ranks, scalings, h, ldh, y,
+                       ldy, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_shrink_expand(dtype, T, K, S, R, L, G, N, _p(x), ldx, _p(w_a), lda, _p(w_b),
+                                  ldb, _p(slice_offsets), _p(seg_indptr), _p(weight_indices),
+                                  _p(permutation), _p(lora_ranks), _p(scalings), _p(h), ldh,
+                                  _p(y), ldy, _p(workspace), workspace_bytes, stream)
+    _check("lora_shrink_expand", st)
+
+
+def lora_shrink_expand_workspace_size(dtype, T, K, S, R, G, N) -> int:
+    return int(lib().lora_shrink_expand_workspace_size(dtype, T, K, S, R, G, N))
+
+
+LORA_SHRINK_EXPAND_FLAG_OFFSET = 32764  # byte offset of the wait-bound flag in the workspace
 
 
 def lora_schedule_tiles(T, G, BM, method, seg_indptr, weight_indices, lora_ranks, tiles,

@@ -620,6 +620,52 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   return LORA_OK;
 }
 
+// Workspace of lora_shrink_expand. Single launch: every counter sits in the leading 32 KiB that
+// every call leaves zero, at offsets that do not depend on the sizes, so calls of any size can
+// share one workspace: the shrink's arrival counters in [0, 16 KiB), the per-tile done counters
+// from 28 KiB, the wait-bound flag in the last int; the shrink's partial planes follow as in
+// lora_shrink's own layout. Two launches: the shrink's workspace, then the expand's at
+// expand_off. The query covers both, since the choice depends on pointer alignment.
+constexpr size_t kPairFlagOffset = kCounterBytes - 4;
+static_assert(kPairFlagOffset == LORA_SHRINK_EXPAND_FLAG_OFFSET, "flag offset of the header");
+constexpr int64_t kPairArrivalInts = 4096;
+// Each arrival counter of the single launch on a 64-byte line of its own: expand waves poll them
+// while shrink pieces count in on them.
+constexpr int kPairCounterShift = 4;
+constexpr size_t kPairDoneOffset = 28672;
+constexpr int64_t kPairMaxTiles = 192;
+static_assert(kPairArrivalInts * 4 <= kPairDoneOffset &&
+              kPairDoneOffset + kPairMaxTiles * 4 <= kPairFlagOffset, "pair counter layout");
+
+struct PairWs {
+  ShrinkWs sw;           // the single launch's shrink plan
+  bool shape_ok;         // sizes allow the single launch (alignment is checked per call)
+  size_t single_total;
+  size_t expand_off, two_total;
+};
+
+PairWs pair_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t G) {
+  PairWs w{};
+  const Knobs kn;
+  // Single launch: 16-bit types at decode sizes, where lora_shrink takes the 1x1x8x2 register
+  // ring (K % 8 == 0 with aligned rows: the LDS-staged family is not preferred there) from the
+  // inline search, and lora_expand the 64-column, 4-wave, 2-deep form over 16-token tiles.
+  w.shape_ok = (dtype == LORA_BF16 || dtype == LORA_F16) && T < 1024 && K % 8 == 0 &&
+               G <= kInlineMaxSegments && R <= 32 &&
+               !prefer_lds(kn, dtype, T, K, S, R, G);
+  if (w.shape_ok) {
+    w.sw = shrink_ws(kn, dtype, T, K, S, R, G, false);
+    w.shape_ok = w.sw.variant == 2 && w.sw.sched == 0 && w.sw.bound <= kPairMaxTiles &&
+                 (w.sw.bound * w.sw.gy << kPairCounterShift) <= kPairArrivalInts && w.sw.q > 0 &&
+                 w.sw.in_launch;
+  }
+  if (w.shape_ok) w.single_total = std::max(w.sw.total, kCounterBytes);
+  const size_t st = lora_shrink_workspace_size_ex(lora_dtype(dtype), T, K, S, R, G, nullptr);
+  w.expand_off = align256(st);
+  w.two_total = w.expand_off + schedule_bytes(T, G, 16);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -765,6 +811,99 @@ lora_status lora_expand(lora_dtype dtype, int64_t T, int32_t S, int32_t R, int32
   return lora_expand_ex(dtype, T, S, R, L, G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
                         weight_indices, permutation, lora_ranks, scalings, y, ldy, nullptr,
                         workspace, workspace_bytes, stream);
+}
+
+size_t lora_shrink_expand_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S,
+                                         int32_t R, int32_t G, int64_t N) {
+  (void)N;
+  if (T <= 0 || G <= 0 || K <= 0 || S <= 0 || R <= 0 || !valid_dtype(dtype)) return 0;
+  const PairWs w = pair_ws(int(dtype), T, K, S, R, G);
+  return std::max(std::max(w.single_total, w.two_total), kCounterBytes);
+}
+
+lora_status lora_shrink_expand(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                               int32_t L, int32_t G, int64_t N, const void* x, int64_t ldx,
+                               const void* w_a, int64_t lda, const void* w_b, int64_t ldb,
+                               const int32_t* slice_offsets, const int32_t* seg_indptr,
+                               const int32_t* weight_indices, const int32_t* permutation,
+                               const int32_t* lora_ranks, const float* scalings, void* h,
+                               int64_t ldh, void* y, int64_t ldy, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return LORA_EUNSUPPORTED;
+  if (T < 0 || G < 0 || S < 1 || R < 1 || N < 0) return LORA_EINVAL;
+  if (T == 0 || G == 0) return LORA_OK;
+  if (K < 1 || L < 1) return LORA_EINVAL;
+  const size_t need = lora_shrink_expand_workspace_size(dtype, T, K, S, R, G, N);
+  if (workspace == nullptr || workspace_bytes < need || !al16(workspace)) return LORA_EWORKSPACE;
+  const PairWs w = pair_ws(int(dtype), T, K, S, R, G);
+  const int e = esize(dtype);
+  const bool aligned_x = al16(x) && al16(w_a) && (ldx * e) % 16 == 0 && (lda * e) % 16 == 0;
+  const bool aligned_b = al16(h) && al16(w_b) && (ldh * e) % 16 == 0 && (ldb * e) % 16 == 0 &&
+                         (int64_t(R) * e) % 16 == 0;
+  const bool aligned_y = al16(y) && (ldy * e) % 16 == 0;
+  char* wsb = static_cast<char*>(workspace);
+  // Column blocks of the single launch's expand workgroups (8 waves of 64-column chunks): the
+  // library's usual width, widened until the shrink and expand grids are resident together (two
+  // 512-thread workgroups per compute unit). Where even the widest blocks leave workgroups for a
+  // second round, those would start their loads only after the shrink (1000 tokens: 34.6 us
+  // against 29.3 us for two launches, cold calls), so the call makes two launches instead.
+  const ShrinkWs& ws = w.sw;
+  int bn = 0;
+  bool single = w.shape_ok && aligned_x && aligned_b && N > 0;
+  if (single) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return LORA_EHIP;
+    const int64_t swgs = int64_t(ws.grid_x) * ws.gy;
+    bn = expand_bn(Knobs{}, T, G, N, 16, 8, 64, false);
+    while (bn < 4096 && swgs + ws.bound * (cdiv(N, bn) + S) > 2 * int64_t(cus)) bn += 512;
+    single = swgs + ws.bound * (cdiv(N, bn) + S) <= 2 * int64_t(cus);
+  }
+  if (!single) {
+    // two launches, exactly lora_shrink then lora_expand
+    const lora_status st = lora_shrink(dtype, T, K, S, R, L, G, x, ldx, w_a, lda, seg_indptr,
+                                       weight_indices, permutation, lora_ranks, h, ldh, workspace,
+                                       w.expand_off, stream);
+    if (st != LORA_OK) return st;
+    return lora_expand(dtype, T, S, R, L, G, N, h, ldh, w_b, ldb, slice_offsets, seg_indptr,
+                       weight_indices, permutation, lora_ranks, scalings, y, ldy,
+                       wsb + w.expand_off, workspace_bytes - w.expand_off, stream);
+  }
+  // the argument checks of both calls
+  if (S > kMaxSlices || R > kMaxRank) return LORA_EUNSUPPORTED;
+  if (T >= INT_MAX || K >= INT_MAX || N >= INT_MAX / 2 || G >= INT_MAX / 2)
+    return LORA_EUNSUPPORTED;
+  if (!x || !w_a || !w_b || !slice_offsets || !seg_indptr || !weight_indices || !lora_ranks ||
+      !scalings || !h || !y)
+    return LORA_EINVAL;
+  if (ldx < K || lda < K || ldh < int64_t(S) * R || ldb < R || ldy < N) return LORA_EINVAL;
+  if (int64_t(S) * R * T * 16 >= int64_t(1) << 62) return LORA_EUNSUPPORTED;
+  if (cdiv(N, bn) + S > 65535) return LORA_EUNSUPPORTED;
+
+  lmx::ShrinkArgs a{};
+  a.x = x; a.w_a = w_a; a.seg_indptr = seg_indptr; a.weight_indices = weight_indices;
+  a.permutation = permutation; a.lora_ranks = lora_ranks; a.h = h;
+  a.K = K; a.ldx = ldx; a.lda = lda; a.ldh = ldh; a.S = S; a.R = R; a.G = G; a.T = int(T);
+  a.sk_q = ws.q; a.sk_tiles = int(ws.bound); a.sk_mp = ws.mp; a.sk_unit = ws.unit;
+  a.part = reinterpret_cast<float*>(wsb + ws.part);
+  a.counters = reinterpret_cast<int*>(wsb);
+  a.ctr_shift = kPairCounterShift;
+  lmx::ExpandArgs b{};
+  b.h = h; b.w_b = w_b; b.slice_offsets = slice_offsets; b.seg_indptr = seg_indptr;
+  b.weight_indices = weight_indices; b.permutation = permutation; b.lora_ranks = lora_ranks;
+  b.scalings = scalings; b.y = y;
+  b.N = N; b.ldh = ldh; b.ldb = ldb; b.ldy = ldy; b.S = S; b.R = R; b.G = G; b.BN = bn;
+  lmx::PairArgs pa{};
+  pa.sgx = ws.grid_x;
+  pa.sgy = ws.gy;
+  pa.shrink_wgs = pa.sgx * pa.sgy;
+  pa.egx = int(ws.bound);
+  pa.egy = int(cdiv(N, bn) + S);
+  pa.done = reinterpret_cast<int*>(wsb + kPairDoneOffset);
+  pa.err = reinterpret_cast<int*>(wsb + kPairFlagOffset);
+  return hip_status(lmx::launch_pair(int(dtype), a, b, pa, K % 32 == 0, aligned_y,
+                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t lora_mlp_workspace_size(lora_dtype dtype, int64_t M, int64_t H, int64_t I, int32_t r) {

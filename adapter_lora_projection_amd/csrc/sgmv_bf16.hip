@@ -20,4 +20,9 @@ hipError_t launch_expand_bf16(const ExpandArgs& a, const ExpandPlan& plan, hipSt
   return launch_expand_dt<DT_BF16>(a, plan, st);
 }
 
+hipError_t launch_pair_bf16(const ShrinkArgs& s, const ExpandArgs& e, const PairArgs& pa,
+                           bool kfull, bool aligned_y, hipStream_t st) {
+  return launch_pair_dt<DT_BF16>(s, e, pa, kfull, aligned_y, st);
+}
+
 }  // namespace lmx

@@ -15,6 +15,10 @@ hipError_t launch_shrink_sk_reduce_f16(const ShrinkArgs& a, int bm, hipStream_t 
 hipError_t launch_shrink_sk_reduce_f32(const ShrinkArgs& a, int bm, hipStream_t st);
 hipError_t launch_expand_f16(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
 hipError_t launch_expand_f32(const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
+hipError_t launch_pair_bf16(const ShrinkArgs& s, const ExpandArgs& e, const PairArgs& pa,
+                            bool kfull, bool aligned_y, hipStream_t st);
+hipError_t launch_pair_f16(const ShrinkArgs& s, const ExpandArgs& e, const PairArgs& pa,
+                           bool kfull, bool aligned_y, hipStream_t st);
 
 // Token rows per tile (16 * token groups) and waves of each kernel shape; these tables mirror the
 // variant lists of sgmv_impl.hpp.
@@ -62,6 +66,15 @@ hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan,
     case DT_F32: return launch_expand_f32(a, plan, st);
     case DT_BF16: return launch_expand_bf16(a, plan, st);
     default: return launch_expand_f16(a, plan, st);
+  }
+}
+
+hipError_t launch_pair(int dtype, const ShrinkArgs& s, const ExpandArgs& e, const PairArgs& pa,
+                       bool kfull, bool aligned_y, hipStream_t st) {
+  switch (dtype) {
+    case DT_BF16: return launch_pair_bf16(s, e, pa, kfull, aligned_y, st);
+    case DT_F16: return launch_pair_f16(s, e, pa, kfull, aligned_y, st);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -20,4 +20,9 @@ hipError_t launch_expand_f16(const ExpandArgs& a, const ExpandPlan& plan, hipStr
   return launch_expand_dt<DT_F16>(a, plan, st);
 }
 
+hipError_t launch_pair_f16(const ShrinkArgs& s, const ExpandArgs& e, const PairArgs& pa,
+                           bool kfull, bool aligned_y, hipStream_t st) {
+  return launch_pair_dt<DT_F16>(s, e, pa, kfull, aligned_y, st);
+}
+
 }  // namespace lmx

@@ -68,6 +68,23 @@ __device__ __forceinline__ float part_load(const float* q) {
   return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Bounded wait of the single-launch shrink + expand for a counter to reach `target` (the whole
+// wave reads the same counter, so the loop is uniform). Shrink workgroups come first in the
+// launch and never wait, so the counters always fill; the bound (one second of the 100 MHz
+// real-time counter) only guarantees that every wave ends: past it the wave sets *err and goes on.
+constexpr uint64_t kPairWaitTicks = 100000000ull;
+__device__ __forceinline__ void wait_count(const int* ctr, int target, int* err) {
+  if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(4);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kPairWaitTicks) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
+}
+
 // Completion of a shared-work shrink inside its own launch (p.counters non-null), called by
 // every thread of the workgroup right after its piece of tile t went to plane j (fp32 sums of
 // the rank columns of this grid row's CBY column blocks). Each workgroup waits until its
@@ -82,7 +99,7 @@ __device__ __forceinline__ float part_load(const float* q) {
 // 26.8 to 19.1 us; the register ring takes 1, since the 32 extra load addresses doubled its
 // registers (78 -> 154 VGPRs, 6 -> 3 waves per SIMD) and its 288-workgroup decode grid at
 // 128 tokens then needed a second round (10.1 -> 13.6 us).
-template <int DT, int NT, int EU>
+template <int DT, int NT, int EU, bool KEEP = false>
 __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, int np, int CBY,
                           int by, int ny, int* s_last) {
   using Tr = Traits<DT>;
@@ -94,10 +111,12 @@ __device__ void sk_finish(const ShrinkArgs& p, const Tile& tile, int t, int j, i
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
     __syncthreads();                // ... and every other thread's
     if (threadIdx.x == 0) {
-      int* ctr = p.counters + int64_t(t) * ny + by;
+      int* ctr = p.counters + ((int64_t(t) * ny + by) << p.ctr_shift);
       const int before = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = before == np - 1;
-      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // (KEEP: the single-launch shrink + expand, whose expand workgroups wait for the count
+      // and clear it)
+      if (last && !KEEP) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *s_last = last;
     }
     __syncthreads();
@@ -313,18 +332,27 @@ __device__ __forceinline__ void shrink_piece(const ShrinkArgs& p, const Tile& ti
 // j = workgroup - first workgroup of the tile, rows = the tile's sorted positions, and the
 // planes are added in order by the tile's last workgroup (sk_finish, with arrival counters) or
 // by shrink_sk_reduce_kernel in a second launch.
-template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL>
-__global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
+template <int MT, int CB, int NW>
+struct ShrinkSmem {
+  Tile tile;
+  int scan[NW];
+  int last;
+  f32x4_t red[(NW > 1) ? NW : 1][CB * MT][64];
+};
+
+// One shrink workgroup (bx, by) of a gdx x gdy grid. KEEP (the single-launch shrink + expand):
+// the arrival counters of a split are left at the piece count for the expand workgroups.
+template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL, bool KEEP>
+__device__ __forceinline__ void shrink_wg(const ShrinkArgs& p, int bx, int by_in, int gdx,
+                                          int gdy, ShrinkSmem<MT, CB, NW>& sm) {
   using Tr = Traits<DT>;
   using S = typename Tr::store_t;
   constexpr int NT = NW * 64;
   constexpr int BM = 16 * MT;
   constexpr int NOUT = (CB * MT + NW - 1) / NW;
-
-  __shared__ Tile s_tile;
-  __shared__ int s_scan[NW];
-  __shared__ int s_last;
-  __shared__ f32x4_t s_red[(NW > 1) ? NW : 1][CB * MT][64];
+  Tile* const s_tile = &sm.tile;
+  int* const s_scan = sm.scan;
+  auto s_red = sm.red;
 
   const int lane = threadIdx.x & 63, w = wave_id();
   const int li = lane & 15, lg = lane >> 4;
@@ -367,14 +395,14 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
     // tiles, each tile's grid rows on consecutive workgroups of that XCD. The tile's x rows then
     // come from the XCD's L2 after the first read, and the tiles of one segment (one adapter's
     // A rows) stay on one or two XCDs.
-    int tx = int(blockIdx.x), by = int(blockIdx.y);
+    int tx = bx, by = by_in;
     if (p.xcd_rows > 0) {
-      const int L = int(blockIdx.x);
-      const int tpx = (int(gridDim.x) / 8) / p.xcd_rows;  // tiles per XCD
+      const int L = bx;
+      const int tpx = (gdx / 8) / p.xcd_rows;  // tiles per XCD
       tx = (L % 8) * tpx + (L / 8) / p.xcd_rows;
       by = (L / 8) % p.xcd_rows;
     }
-    const Tile tile = shrink_tile<NT>(p, BM, tx, &s_tile, s_scan);
+    const Tile tile = shrink_tile<NT>(p, BM, tx, s_tile, s_scan);
     if (tile.g < 0) return;
     f32x4_t sums[NOUT];
     shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, by, 0, int(nsteps), s_red, sums);
@@ -383,27 +411,34 @@ __global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
   }
 
   const int64_t units = int64_t(p.sk_tiles) * nsteps;
-  int64_t u = int64_t(blockIdx.x) * p.sk_q;
+  int64_t u = int64_t(bx) * p.sk_q;
   const int64_t uend = min(u + int64_t(p.sk_q), units);
   while (u < uend) {
     const int t = int(u / nsteps);
     const int k0 = int(u - int64_t(t) * nsteps);
     const int k1 = int(min(nsteps, int64_t(k0) + (uend - u)));
-    const Tile tile = shrink_tile<NT>(p, BM, t, &s_tile, s_scan);
+    const Tile tile = shrink_tile<NT>(p, BM, t, s_tile, s_scan);
     if (tile.g < 0) break;  // past the last tile (uniform over the workgroup)
-    const int j = int(blockIdx.x) - int((int64_t(t) * nsteps) / p.sk_q);
+    const int j = bx - int((int64_t(t) * nsteps) / p.sk_q);
     float* slot = p.part + (int64_t(j) * p.T + tile.m0) * (p.S * p.R);
     {  // (a rank-0 tile stores nothing: every column is at or past its rank)
       f32x4_t sums[NOUT];
-      shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, int(blockIdx.y), k0, k1, s_red, sums);
-      store(tile, int(blockIdx.y), sums, slot);
+      shrink_piece<DT, MT, CB, NW, D, AL, KFULL>(p, tile, by_in, k0, k1, s_red, sums);
+      store(tile, by_in, sums, slot);
     }
     if (p.counters != nullptr)
-      sk_finish<DT, NT, 1>(p, tile, t, j, sk_pieces(t, nsteps, p.sk_q), CB, int(blockIdx.y),
-                           int(gridDim.y), &s_last);
+      sk_finish<DT, NT, 1, KEEP>(p, tile, t, j, sk_pieces(t, nsteps, p.sk_q), CB, by_in, gdy,
+                                &sm.last);
     u += k1 - k0;
     __syncthreads();  // every wave has read the shared tile record before the next search
   }
+}
+
+template <int DT, int MT, int CB, int NW, int D, bool AL, bool KFULL>
+__global__ __launch_bounds__(NW * 64) void shrink_kernel(ShrinkArgs p) {
+  __shared__ ShrinkSmem<MT, CB, NW> sm;
+  shrink_wg<DT, MT, CB, NW, D, AL, KFULL, false>(p, int(blockIdx.x), int(blockIdx.y),
+                                                 int(gridDim.x), int(gridDim.y), sm);
 }
 
 // Adds the stream-K pieces of tile blockIdx.x in workgroup order, rounds once and writes h,
@@ -453,9 +488,15 @@ __global__ __launch_bounds__(256) void shrink_sk_reduce_kernel(ShrinkArgs p, int
 // the 4 consecutive columns cbase + 4c .. +3 of tokens 4g .. 4g+3, and one 8-byte access per token
 // covers 128 contiguous bytes of 4 rows per instruction. y and B of a chunk are fetched together
 // into a D-deep ring, so data are consumed in the order they were requested.
-template <int DT, int NW, int JS, int D, bool ALB, bool ALY>
+//
+// HFn (the single-launch shrink + expand): h is not ready when the wave starts. The wave primes
+// its ring with the first chunks' y and B, then calls hfn(frag) -- with every wave of the
+// workgroup, as it holds barriers -- which waits for the tile's shrink and returns the wave's h
+// fragments; the y and B loads overlap the shrink.
+template <int DT, int NW, int JS, int D, bool ALB, bool ALY, typename HFn = std::nullptr_t>
 __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& tile, int s, int nb0,
-                                            int nblen, int w) {
+                                            int nblen, int w, HFn hfn = nullptr) {
+  constexpr bool PAIR = !std::is_same_v<HFn, std::nullptr_t>;
   using Tr = Traits<DT>;
   using S = typename Tr::store_t;
   constexpr int KSTEP = Tr::kStep;
@@ -478,9 +519,8 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
   // rank; the adapter's rank masks it once the first chunks are in flight
   Frag<S, ALB> hf[JS];
   uint4 hv[JS];
-  {
-    const bool ok = c < tile.mlen;
-    const S* hrow = hbuf + int64_t(tile.m0 + (ok ? c : 0)) * p.ldh + s * p.R;
+  const S* hrow = hbuf + int64_t(tile.m0 + (c < tile.mlen ? c : 0)) * p.ldh + s * p.R;
+  if constexpr (!PAIR) {
 #pragma unroll
     for (int js = 0; js < JS; ++js) {
       const int j = js * KSTEP + g * EPF;
@@ -579,6 +619,13 @@ __device__ __forceinline__ void expand_body(const ExpandArgs& p, const Tile& til
     ((fetch(std::integral_constant<int, dd>{}, dd), __builtin_amdgcn_sched_barrier(0)), ...);
   }(std::make_integer_sequence<int, D>{});
   if (r <= 0) return;  // a rank-0 adapter leaves y untouched
+  if constexpr (PAIR) {
+    static_assert(ALB, "the single-launch form takes h as aligned 16-byte fragments");
+    uint4 fr[JS];
+    hfn(fr);
+#pragma unroll
+    for (int js = 0; js < JS; ++js) hf[js].a = fr[js];
+  }
 #pragma unroll
   for (int js = 0; js < JS; ++js) hv[js] = hf[js].masked(r - (js * KSTEP + g * EPF));
   const int nfull = nci / D;
@@ -1079,6 +1126,106 @@ __global__ __launch_bounds__(256) void expand_shared_kernel(ExpandArgs p) {
   }
 }
 
+// ------------------------------------------------------------- single-launch shrink + expand
+
+// Shrink and expand of one call in one launch, for decode sizes (tiles of 16 sorted positions in
+// both). Workgroups [0, shrink_wgs) are the register-ring shrink (shape 1x1x8x2: one 16-token
+// group, one 16-column block, 8 waves, 2-deep ring) with its (tile, K step) work split into
+// pieces, each stored as fp32 partial sums and counted in on the arrival counter of its (tile,
+// column block); the last piece of each writes h as in lora_shrink and leaves the counter at the
+// piece count. The remaining workgroups are the 64-column expand (8 waves, 2-deep ring) over
+// (tile, column block): each primes its ring with y and B, waits until every piece of its
+// slice's column blocks has arrived, and adds the partial sums itself -- one element of the
+// tile's [16][R] h block per thread, planes added in plane order and rounded once, exactly as
+// the last piece adds them for h -- into LDS, where each wave takes its MFMA fragments. So the
+// expand does not wait for h to be written and read back, and every output is computed with the
+// same operands and instructions as in the separate calls (the column blocking does not enter
+// the arithmetic). The host sizes the column blocks so that the whole grid is resident at once.
+// A tile's expand workgroups count themselves out on its done counter; the last one waits for
+// every column block's pieces (also those of slices no expand workgroup reads) and clears the
+// tile's counters, so the workspace is ready for the next call. A rank-0 tile stores no pieces
+// and its expand workgroups neither wait nor count.
+template <int DT, bool KFULL, bool ALY>
+__global__ __launch_bounds__(512) void pair_kernel(ShrinkArgs ps, ExpandArgs pe, PairArgs pp) {
+  using Tr = Traits<DT>;
+  using S = typename Tr::store_t;
+  constexpr int KSTEP = Tr::kStep;
+  constexpr int EPF = Tr::kPerFrag;
+  __shared__ ShrinkSmem<1, 1, 8> sm;
+  __shared__ __attribute__((aligned(16))) S s_h[16 * KSTEP];  // the tile's h block of one slice
+  const int id = int(blockIdx.x);
+  if (id < pp.shrink_wgs) {
+    shrink_wg<DT, 1, 1, 8, 2, true, KFULL, true>(ps, id % pp.sgx, id / pp.sgx, pp.sgx, pp.sgy, sm);
+    return;
+  }
+  const int e = id - pp.shrink_wgs;
+  const int tx = e % pp.egx, by = e / pp.egx;
+  const SliceLane sl = slice_lanes(pe.slice_offsets, pe.S);
+  get_tile<512, false>(pe.seg_indptr, pe.weight_indices, pe.lora_ranks, pe.scalings, pe.G, 16,
+                       pe.tiles, pe.tile_count, tx, &sm.tile, sm.scan);
+  Tile tile = sm.tile;
+  if (tile.g < 0) return;
+  tile_rank(pe.lora_ranks, pe.scalings, &tile);
+  if (tile.r <= 0) return;
+  const int R = pe.R, NB = (R + 15) >> 4, gy = pp.sgy;
+  const int64_t nsteps = (ps.K + KSTEP - 1) / KSTEP;
+  const int np = sk_pieces(tx, nsteps, ps.sk_q);
+  // counter of column block b of this tile
+  auto ctr = [&](int b) { return ps.counters + ((int64_t(tx) * gy + b) << ps.ctr_shift); };
+  int s, nb0, nblen;
+  const bool has = find_nblock_lanes(sl, pe.S, pe.BN, by, &s, &nb0, &nblen);
+  const int w = wave_id();
+  if (has) {
+    // h fragments of slice s: wait for the pieces of the slice's column blocks, add them
+    auto hfn = [&](uint4 (&fr)[1]) {
+      if (w == 0)
+        for (int b = 0; b < NB; ++b) wait_count(ctr(s * NB + b), np, pp.err);
+      __syncthreads();
+      const int el = int(threadIdx.x);
+      if (el < 16 * R) {
+        const int m = el / R, c = el - (el / R) * R;
+        S v = S(0);
+        if (m < tile.mlen && c < tile.r) {
+          const int64_t plane = int64_t(ps.T) * (ps.S * ps.R);
+          const float* src = ps.part + int64_t(tile.m0 + m) * (ps.S * ps.R) + s * R + c;
+          float acc = 0.f;
+          for (int q0 = 0; q0 < np; q0 += 8) {
+            float bq[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bq[i] = (q0 + i < np) ? part_load(src + (q0 + i) * plane) : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (q0 + i < np) acc = (q0 + i == 0) ? bq[i] : acc + bq[i];
+          }
+          v = Tr::from_f32(acc);
+        }
+        s_h[m * R + c] = v;
+      }
+      __syncthreads();
+      const int lane = threadIdx.x & 63, cl = lane & 15, g = lane >> 4;
+      const int j = g * EPF;  // rank offset of this lane's fragment (JS = 1)
+      fr[0] = j < R ? *reinterpret_cast<const uint4*>(s_h + cl * R + j) : make_uint4(0, 0, 0, 0);
+    };
+    // whole 8-byte y pieces only when the block starts on an 8-byte boundary
+    if (ALY && (nb0 * int(sizeof(S))) % 8 == 0)
+      expand_body<DT, 8, 1, 2, true, ALY>(pe, tile, s, nb0, nblen, w, hfn);
+    else
+      expand_body<DT, 8, 1, 2, true, false>(pe, tile, s, nb0, nblen, w, hfn);
+  }
+  __syncthreads();  // every wave of this workgroup is past its wait
+  if (threadIdx.x == 0) {
+    int* const done = pp.done + tx;
+    const int before = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == pp.egy - 1) {  // the tile's last expand workgroup: no wave waits on it any more
+      for (int b = 0; b < gy; ++b) {
+        wait_count(ctr(b), np, pp.err);  // every piece has counted in: no increment follows
+        __hip_atomic_store(ctr(b), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------ launchers
 
 // Kernel shapes. Shrink: (token groups of 16 per tile, 16-column blocks per workgroup, waves,
@@ -1175,6 +1322,26 @@ static hipError_t launch_expand_shared_t(const ExpandArgs& a, const ExpandPlan& 
   if (!plan.aligned_b || !plan.aligned_y || a.R != 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL((expand_shared_kernel<DT, D, true>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_pair_dt(const ShrinkArgs& s, const ExpandArgs& e, const PairArgs& pa, bool kfull,
+                          bool aligned_y, hipStream_t st) {
+  if constexpr (DT == DT_F32) {
+    return hipErrorInvalidValue;
+  } else {
+    if (e.R > Traits<DT>::kStep || pa.shrink_wgs != pa.sgx * pa.sgy) return hipErrorInvalidValue;
+    const dim3 grid(unsigned(pa.shrink_wgs + pa.egx * pa.egy));
+    if (kfull && aligned_y)
+      hipLaunchKernelGGL((pair_kernel<DT, true, true>), grid, dim3(512), 0, st, s, e, pa);
+    else if (kfull)
+      hipLaunchKernelGGL((pair_kernel<DT, true, false>), grid, dim3(512), 0, st, s, e, pa);
+    else if (aligned_y)
+      hipLaunchKernelGGL((pair_kernel<DT, false, true>), grid, dim3(512), 0, st, s, e, pa);
+    else
+      hipLaunchKernelGGL((pair_kernel<DT, false, false>), grid, dim3(512), 0, st, s, e, pa);
+    return hipGetLastError();
+  }
 }
 
 template <int DT>

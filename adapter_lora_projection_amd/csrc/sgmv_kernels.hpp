@@ -30,10 +30,21 @@ struct ShrinkArgs {
   // exit; the last workgroup to store a piece of a tile adds the tile's planes into h in the
   // same launch (no launch_shrink_sk_reduce).
   int* counters;
+  int ctr_shift;  // counter (tile, grid row) sits at index (tile * rows + row) << ctr_shift
   // Direct mode only (register-ring and LDS-staged kernels): > 0 launches a one-dimensional grid
   // that gives each XCD a contiguous range of tiles, the xcd_rows column-block groups of a tile
   // on consecutive workgroups of that XCD (0: a 2-D grid).
   int xcd_rows;
+};
+
+// Single-launch shrink + expand (decode sizes): workgroups [0, shrink_wgs) run the split shrink
+// grid (sgx x sgy, x fastest; its arrival counters in ShrinkArgs::counters), the rest the 16-token
+// expand grid (egx tiles x egy column blocks).
+struct PairArgs {
+  int shrink_wgs, sgx, sgy;
+  int egx, egy;
+  int* done;  // [tiles bound]: expand workgroups finished with the tile, zero on entry and exit
+  int* err;   // set to 1 if a wait ever exceeded its bound (never cleared by the library)
 };
 
 struct ExpandArgs {
@@ -90,6 +101,11 @@ int shrink_lds_ncb(int variant);          // 16-column blocks per workgroup
 int shrink_lds_bm(int variant);           // positions per tile
 constexpr int kShrinkLdsUnit = 64;        // reduction indices per stage
 hipError_t launch_expand(int dtype, const ExpandArgs& a, const ExpandPlan& plan, hipStream_t st);
+// Single-launch shrink + expand (16-bit types; shrink shape 2, split with in-launch completion,
+// 16-byte aligned x and A rows; 64-column expand with 16-byte aligned h and B rows, padded rank
+// <= 32).
+hipError_t launch_pair(int dtype, const ShrinkArgs& s, const ExpandArgs& e, const PairArgs& pa,
+                       bool kfull, bool aligned_y, hipStream_t st);
 hipError_t launch_schedule(const int* seg_indptr, const int* weight_indices, int G, int BM,
                            int4* tiles, int* count, hipStream_t st);
 hipError_t launch_zero_int(int* p, hipStream_t st);

@@ -147,6 +147,52 @@ def expand(h, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_
     return y
 
 
+def shrink_expand(x, w_a, w_b, slice_offsets, seg_indptr, weight_indices, permutation,
+                  lora_ranks, scalings, y, S: int, R: int, h: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """shrink then expand in one call (``lora_shrink_expand``; one launch at decode sizes).
+    x: [T][K], w_a: [L][S*R][K], w_b: [L][N][R], y: [T][>=N] updated in place. Returns (h, y).
+    workspace: a reusable uint8 buffer of at least the queried size, zero-filled before its
+    first use (a fresh zeroed one otherwise)."""
+    _dev(x, w_a, w_b, slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks,
+         scalings, y, h, workspace)
+    T, K = x.shape
+    ldx = _rows(x, "x")
+    rows, lda = _stacked(w_a, "w_a")
+    if rows != S * R or w_a.shape[2] != K:
+        raise ValueError("w_a must be [L][S*R][K]")
+    N, ldb = _stacked(w_b, "w_b")
+    if w_b.shape[2] != R or w_b.shape[0] != w_a.shape[0]:
+        raise ValueError("w_b must be [L][N][R] with the adapters of w_a")
+    ldy = _rows(y, "y")
+    if y.shape[0] != T or y.shape[1] < N:
+        raise ValueError("y must be [T][>=N]")
+    G = weight_indices.numel()
+    _meta(slice_offsets, S + 1, "slice_offsets")
+    _meta(seg_indptr, G + 1, "seg_indptr")
+    _meta(weight_indices, None, "weight_indices")
+    if permutation is not None:
+        _meta(permutation, T, "permutation")
+    _meta(lora_ranks, w_a.shape[0], "lora_ranks")
+    if scalings.dtype != torch.float32 or scalings.numel() != w_a.shape[0]:
+        raise ValueError("scalings must be float32 [L]")
+    dt = dtype_code(x)
+    if w_a.dtype != x.dtype or w_b.dtype != x.dtype or y.dtype != x.dtype:
+        raise TypeError("x, w_a, w_b and y must share a dtype")
+    if h is None:
+        h = torch.empty((T, S * R), dtype=x.dtype, device=x.device)
+    else:
+        _out(h, (T, S * R), x.dtype, x.device, "h")
+    ldh = _rows(h, "h")
+    nbytes = _lib.lora_shrink_expand_workspace_size(dt, T, K, S, R, G, N)
+    ws = _workspace(nbytes, x.device) if workspace is None else _given_workspace(workspace, nbytes, x.device)
+    _lib.lora_shrink_expand(dt, T, K, S, R, w_a.shape[0], G, N, x, ldx, w_a, lda, w_b, ldb,
+                            slice_offsets, seg_indptr, weight_indices, permutation, lora_ranks,
+                            scalings, h, ldh, y, ldy, ws, 0 if ws is None else ws.numel(),
+                            _stream())
+    return h, y
+
+
 def schedule_tiles(T: int, seg_indptr, weight_indices, lora_ranks, BM: int, method: int = 0) -> torch.Tensor:
     """The device segment schedule as an int32 [count][5] tensor of (g, m0, mlen, a, r)."""
     _dev(seg_indptr, weight_indices, lora_ranks)

@@ -21,10 +21,11 @@ output directories under gpurun_out/):
 Usage: python bench_profiles.py <dir>   (the directory holding the six output folders)
 
 Dispatches of the shrink+expand sweep are named after their workload (shrink_tok<T>,
-expand_tok<T>): the first sweep step of each run (one shrink and one expand per token count, in
-order) fixes which kernel and grid each workload launches; every later dispatch with the same
-kernel and grid gets that name (several names when two workloads launch the same kernel and
-grid). Dispatches after the sweep belong to the objects timed after it (fused MLP, attention
+expand_tok<T>, and pair_tok<T> for the single launch of lora_shrink_expand): the two passes that
+open each benchmark run (lora_shrink and lora_expand per token count, in order, then one
+lora_shrink_expand per token count) fix which kernel and grid each workload launches; every
+later dispatch with the same kernel and grid gets that name (several names when two workloads
+launch the same kernel and grid). Dispatches after the sweep belong to the objects timed after it (fused MLP, attention
 projections, backward, embedding).
 """
 
@@ -93,9 +94,21 @@ def label_dispatches(disp: list[tuple[str, tuple]]) -> list[str]:
     toks = li.SWEEP_TOKENS
     keymap: dict[tuple, list[str]] = defaultdict(list)
     case, stage, i = 0, "shrink", 0
-    # first sweep step: positional
-    while i < len(disp) and case < len(toks):
+    # the opening passes: positional (separate calls, then lora_shrink_expand per case, whose
+    # launches from 1024 tokens repeat the separate calls' kernels and grids)
+    case2 = 0
+    while i < len(disp) and case2 < len(toks):
         name, grid = disp[i]
+        if case >= len(toks):
+            if "pair_kernel" in name:
+                lab = f"pair_tok{toks[case2]}"
+                if lab not in keymap[(name, grid)]:
+                    keymap[(name, grid)].append(lab)
+                case2 += 1
+            elif "expand" in name:
+                case2 += 1
+            i += 1
+            continue
         if any(s in name for s in SGMV_SHRINK) or "sk_reduce" in name or "zero_ints" in name:
             lab = f"shrink_tok{toks[case]}" + (" reduce" if "sk_reduce" in name else "") + \
                   (" counter clear" if "zero_ints" in name else "")
@@ -166,6 +179,7 @@ def main() -> int:
         a = bench.algorithmic(li.sweep_case(T))
         alg[f"shrink_tok{T}"] = a["shrink_bytes"]
         alg[f"expand_tok{T}"] = a["expand_bytes"]
+        alg[f"pair_tok{T}"] = a["shrink_bytes"] + a["expand_bytes"]
 
     table, per_label = trace_table(os.path.join(d, "prof_bench", "bench_kernel_trace.csv"))
     with open(os.path.join(HERE, "profiles", "sgmv_sweep_and_mlp_kernel_trace.md"), "w") as f:
@@ -203,7 +217,7 @@ def main() -> int:
                      f"{'' if a is None else f'{a:,}'} | {ratio} |")
         if a is not None:
             kernels[lab] = {"hbm_bytes_per_launch": int(round(hbm)), "fetch_kib": fk, "write_kib": wk}
-        elif not lab.startswith(("shrink_tok", "expand_tok")):
+        elif not lab.startswith(("shrink_tok", "expand_tok", "pair_tok")):
             mlp_bytes += hbm  # these runs time only the fused MLP after the sweep: one call each
     kernels["mlp_fused"] = {"hbm_bytes_per_launch": int(round(mlp_bytes)),
                             "note": "sum over the launches of one lora_mlp_fused call"}

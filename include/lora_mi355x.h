@@ -236,6 +236,51 @@ lora_status lora_expand_ex(lora_dtype dtype, int64_t T, int32_t S, int32_t R, in
                            size_t workspace_bytes, void* stream);
 
 /*
+ * lora_shrink_expand -- lora_shrink followed by lora_expand on the same segments, in one call
+ * ("Decode LoRA kernels are optimized", Summary: the chunked shrink -> expand pipeline of one
+ * LoRA layer, scheduled on the device with no host synchronisation).
+ *
+ * Writes h exactly as lora_shrink does and updates y exactly as lora_expand does with that h:
+ * every argument has the meaning, layout and range it has there (K, x, w_a, lda as for
+ * lora_shrink; N, w_b, ldb, slice_offsets, scalings, y, ldy as for lora_expand; h is the output
+ * of the first step and the input of the second). Results are bit-identical to the two calls.
+ *
+ * At decode sizes (16-bit types, T < 1024, ceil(T/16) + G <= 192, K % 8 == 0, R <= 32, a slice
+ * layout whose 16-column blocks number a multiple of 3, 16-byte aligned x, w_a, h and w_b rows
+ * and R * element size a multiple of 16 bytes) both steps run in ONE launch: the shrink
+ * workgroups come first and publish each finished tile of h on a per-tile counter in the
+ * workspace; the expand workgroups prime their y and B loads, wait for their tile's h, and
+ * finish. Elsewhere the call makes the two launches of lora_shrink and lora_expand.
+ *
+ *   workspace  device scratch of lora_shrink_expand_workspace_size(...) bytes (never 0 for
+ *              T, G > 0), 16-byte aligned. Its first 32 KiB hold counters and MUST be zero
+ *              before the first call that uses the workspace; every call leaves them zero
+ *              again, so one workspace (sized for the largest call) is reused across calls of
+ *              any size, lora_shrink calls and graph replays with no clearing. Calls that
+ *              overlap in time must not share it.
+ *              The int at byte offset LORA_SHRINK_EXPAND_FLAG_OFFSET is set to 1 if a wait for
+ *              h ever exceeded its one-second bound (the shrink workgroups are dispatched first
+ *              and never wait, so this does not happen; the bound only guarantees that every
+ *              wave ends); the y of that call is then undefined. The library never clears it.
+ *
+ * Errors: as lora_shrink and lora_expand; LORA_EWORKSPACE for a missing, short or misaligned
+ * workspace.
+ */
+#define LORA_SHRINK_EXPAND_FLAG_OFFSET 32764
+
+lora_status lora_shrink_expand(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32_t R,
+                               int32_t L, int32_t G, int64_t N, const void* x, int64_t ldx,
+                               const void* w_a, int64_t lda, const void* w_b, int64_t ldb,
+                               const int32_t* slice_offsets, const int32_t* seg_indptr,
+                               const int32_t* weight_indices, const int32_t* permutation,
+                               const int32_t* lora_ranks, const float* scalings, void* h,
+                               int64_t ldh, void* y, int64_t ldy, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+size_t lora_shrink_expand_workspace_size(lora_dtype dtype, int64_t T, int64_t K, int32_t S,
+                                         int32_t R, int32_t G, int64_t N);
+
+/*
  * lora_mlp_fused -- single-adapter LoRA MLP with fused SwiGLU (bf16).
  *
  *   out = round( hmid W_d^T + scale * xa_d B_d^T ),      xa_d = round( hmid A_d^T ),

@@ -320,3 +320,17 @@ def test_check_metadata_host_validation():
     bad = list(args); bad[12] = None
     assert L.lora_check_metadata(*bad) == _lib.LORA_EWORKSPACE
     assert _lib.lora_check_metadata_workspace_size(8) == 256 + 32
+
+
+def test_shrink_expand_workspace_size():
+    """lora_shrink_expand's workspace covers the two-launch path (the shrink's workspace, then the
+    expand's) and always holds the 32 KiB counter region; T = 0 or G = 0 needs none."""
+    for T, G in ((50, 4), (512, 4), (1024, 4), (8192, 4), (300, 2000)):
+        n = _lib.lora_shrink_expand_workspace_size(1, T, 4096, 3, 16, G, 6144)
+        s = _lib.lora_shrink_workspace_size(1, T, 4096, 3, 16, G)
+        e = _lib.lora_expand_workspace_size(1, T, 3, 16, G, 6144)
+        assert n >= 32768 and n >= ((s + 255) // 256) * 256 + e, (T, G, n, s, e)
+    assert _lib.lora_shrink_expand_workspace_size(1, 0, 4096, 3, 16, 4, 6144) == 0
+    assert _lib.lora_shrink_expand_workspace_size(1, 50, 4096, 3, 16, 0, 6144) == 0
+    assert _lib.lora_shrink_expand_workspace_size(7, 50, 4096, 3, 16, 4, 6144) == 0
+    assert _lib.LORA_SHRINK_EXPAND_FLAG_OFFSET == 32764
