@@ -245,12 +245,15 @@ lora_status lora_expand_ex(lora_dtype dtype, int64_t T, int32_t S, int32_t R, in
  * lora_shrink; N, w_b, ldb, slice_offsets, scalings, y, ldy as for lora_expand; h is the output
  * of the first step and the input of the second). Results are bit-identical to the two calls.
  *
- * At decode sizes (16-bit types, T < 1024, ceil(T/16) + G <= 192, K % 8 == 0, R <= 32, a slice
- * layout whose 16-column blocks number a multiple of 3, 16-byte aligned x, w_a, h and w_b rows
- * and R * element size a multiple of 16 bytes) both steps run in ONE launch: the shrink
- * workgroups come first and publish each finished tile of h on a per-tile counter in the
- * workspace; the expand workgroups prime their y and B loads, wait for their tile's h, and
- * finish. Elsewhere the call makes the two launches of lora_shrink and lora_expand.
+ * At decode sizes both steps run in ONE launch: 16-bit types, T < 1024, ceil(T/16) + G <= 192,
+ * K % 8 == 0, R <= 32, a slice layout whose 16-column blocks number a multiple of 3, 16-byte
+ * aligned x, w_a, h and w_b rows, R * element size a multiple of 16 bytes, lora_shrink splitting
+ * the K reduction of each tile over several workgroups at these sizes, and a grid that is
+ * resident on the GPU all at once. The shrink workgroups come first in the launch and count their
+ * pieces in on per-tile counters in the workspace; the expand workgroups prime their y and B
+ * loads, wait until their tile's pieces are all in, add the pieces themselves (in the order and
+ * with the rounding that give h) and finish. Elsewhere the call makes the two launches of
+ * lora_shrink and lora_expand.
  *
  *   workspace  device scratch of lora_shrink_expand_workspace_size(...) bytes (never 0 for
  *              T, G > 0), 16-byte aligned. Its first 32 KiB hold counters and MUST be zero
