@@ -262,9 +262,11 @@ lora_status lora_expand_ex(lora_dtype dtype, int64_t T, int32_t S, int32_t R, in
  *              any size, lora_shrink calls and graph replays with no clearing. Calls that
  *              overlap in time must not share it.
  *              The int at byte offset LORA_SHRINK_EXPAND_FLAG_OFFSET is set to 1 if a wait for
- *              h ever exceeded its one-second bound (the shrink workgroups are dispatched first
- *              and never wait, so this does not happen; the bound only guarantees that every
- *              wave ends); the y of that call is then undefined. The library never clears it.
+ *              the shrink's pieces ever exceeded its one-second bound (the shrink workgroups are
+ *              dispatched first and never wait, so this does not happen; the bound only
+ *              guarantees that every wave ends); the y of that call is then undefined, its
+ *              counters may be left nonzero, and the workspace must be zero-filled again before
+ *              its next use. The library never clears the flag.
  *
  * Errors: as lora_shrink and lora_expand; LORA_EWORKSPACE for a missing, short or misaligned
  * workspace.
