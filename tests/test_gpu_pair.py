@@ -78,6 +78,23 @@ def _case(kind: str):
     if kind == "rank32":
         return li.make_sgmv("pair_rank32", seed=26, T=64, K=2048, S=3, R=32, L=2,
                             slice_offsets=[0, 2048, 2560, 3072], dtype="bf16", ranks=[32, 19])
+    if kind == "allrank0":  # every adapter of rank 0: no pieces, no waits, y untouched
+        return li.make_sgmv("pair_rank0", seed=28, T=100, K=1024, S=3, R=16, L=3,
+                            slice_offsets=[0, 1024, 1280, 1536], dtype="bf16", ranks=[0, 0, 0])
+    if kind == "manysegs":  # 30 segments (a run of empty ones) over 300 tokens, split shrink
+        import numpy as np
+
+        rng = np.random.default_rng(29)
+        cuts = np.sort(rng.integers(0, 301, size=29))
+        cuts[5:12] = cuts[5]  # a run of empty segments
+        indptr = [0] + [int(v) for v in cuts] + [300]
+        return li.make_sgmv("pair_manysegs", seed=29, T=300, K=1024, S=3, R=16, L=8,
+                            slice_offsets=[0, 1024, 1280, 1536], dtype="bf16",
+                            ranks=[16, 9, 0, 16, 5, 16, 12, 16], fixed_indptr=indptr,
+                            fixed_weight_indices=[int(v) for v in rng.integers(0, 8, size=30)])
+    if kind == "onetoken":
+        return li.make_sgmv("pair_onetoken", seed=30, T=1, K=4096, S=3, R=16, L=2,
+                            slice_offsets=[0, 4096, 5120, 6144], dtype="bf16")
     # sizes that take the two launches
     if kind == "two_T1024":
         return li.sweep_case(1024)
@@ -91,7 +108,8 @@ def _case(kind: str):
 
 
 KINDS = ["sweep50", "sweep128", "sweep256", "sweep512", "direct1000", "f16", "ranks", "identity",
-         "offsets", "kpartial", "rank32", "two_T1024", "two_f32", "two_irregular"]
+         "offsets", "kpartial", "rank32", "allrank0", "manysegs", "onetoken", "two_T1024",
+         "two_f32", "two_irregular"]
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -111,9 +129,11 @@ def test_pair_equals_separate_calls(kind):
     torch.cuda.synchronize()
     assert torch.equal(_bits(h), _bits(h_ref)), "h differs from lora_shrink"
     assert torch.equal(_bits(y), _bits(y_ref)), "y differs from lora_shrink + lora_expand"
+    if kind == "allrank0":
+        assert torch.equal(_bits(y), _bits(y0)) and int(h.count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("kind", ["sweep50", "sweep512", "ranks", "direct1000"])
+@pytest.mark.parametrize("kind", ["sweep50", "sweep512", "ranks", "direct1000", "manysegs"])
 def test_pair_chain_from_x(kind):
     """h against the oracle's shrink and y against the oracle's whole chain from x."""
     c = _case(kind)
