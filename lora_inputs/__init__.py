@@ -263,6 +263,16 @@ def mlp_dout(seed: int = 4, M: int = 4096, H: int = 4096, dtype: str = "bf16") -
     return _normal(rng, (M, H), 1.0, dtype)
 
 
+def projection_douts(seed: int = 5, M: int = 4096, widths=(4096, 1024, 1024, 4096),
+                     dtype: str = "bf16") -> list:
+    """Seeded upstream gradients of projection outputs for the backward, each dout ~ N(0,1)
+    [M][N] for N in ``widths`` (query, key, value and output projections by default), drawn in
+    that order from their own stream (seed, 1) so the forward inputs of the same seed are
+    unchanged."""
+    rng = np.random.default_rng([seed, 1])
+    return [_normal(rng, (M, n), 1.0, dtype) for n in widths]
+
+
 @dataclass
 class QkvCase:
     """Single-adapter LoRA attention projections of one x (nn.Linear [out][in] layouts)."""
