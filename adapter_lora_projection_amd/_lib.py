@@ -45,6 +45,10 @@ SIGNATURES = {
                                   _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                                   _i64, _vp, _sz, _vp]),
     "lora_shrink_expand_workspace_size": (_sz, [_i32, _i64, _i64, _i32, _i32, _i32, _i64]),
+    "lora_linear_prepare_backward": (_i32, [_i32, _i64, _i64, _vp, _vp, _vp]),
+    "lora_linear_backward": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp,
+                                    _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "lora_linear_backward_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
     "lora_schedule_tiles": (_i32, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                    _sz, _vp]),
     "lora_shrink_ex": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
@@ -202,6 +206,23 @@ def lora_shrink_expand(dtype, T, K, S, R, L, G, N, x, ldx, w_a, lda, w_b, ldb, s
 
 def lora_shrink_expand_workspace_size(dtype, T, K, S, R, G, N) -> int:
     return int(lib().lora_shrink_expand_workspace_size(dtype, T, K, S, R, G, N))
+
+
+def lora_linear_prepare_backward(dtype, K, N, w, w_t, stream) -> None:
+    _check("lora_linear_prepare_backward",
+           lib().lora_linear_prepare_backward(dtype, K, N, _p(w), _p(w_t), stream))
+
+
+def lora_linear_backward(dtype, M, K, N, r, scale, x, ldx, dout, lddo, w_t, a, b, dx, lddx, da,
+                         db, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_linear_backward(dtype, M, K, N, r, scale, _p(x), ldx, _p(dout), lddo, _p(w_t),
+                                    _p(a), _p(b), _p(dx), lddx, _p(da), _p(db), _p(workspace),
+                                    workspace_bytes, stream)
+    _check("lora_linear_backward", st)
+
+
+def lora_linear_backward_workspace_size(dtype, M, K, N, r) -> int:
+    return int(lib().lora_linear_backward_workspace_size(dtype, M, K, N, r))
 
 
 LORA_SHRINK_EXPAND_FLAG_OFFSET = 32764  # byte offset of the wait-bound flag in the workspace

@@ -620,6 +620,42 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   return LORA_OK;
 }
 
+// Workspace of the projection backward: byte offsets of its sections (256-byte aligned).
+struct LinBwdLayout {
+  int64_t rp;
+  lmx::SumJobs in, cols;  // row sides (xa from x, dxa from dout); sums over tokens (dA, dB)
+  size_t sbt, ap, at, xa, dxa, rowpart, colpart, total;
+};
+
+LinBwdLayout lin_bwd_layout(int64_t M, int64_t K, int64_t N, int32_t r) {
+  LinBwdLayout L{};
+  L.rp = cdiv(r, 32) * 32;
+  const int JB = int(cdiv(r, 16));
+  int64_t rf[2] = {0, 0}, cf[2] = {0, 0};
+  auto init = [&](lmx::SumJobs& j, int n) { j.n = n; j.M = int(M); j.JB = JB; };
+  auto job = [](lmx::SumJob& j, int64_t C, int nr, int nh) { j.C = int(C); j.nr = nr; j.nh = nh; };
+  init(L.in, 2);
+  job(L.in.job[0], K, 1, 0);  // x: xa
+  job(L.in.job[1], N, 1, 0);  // dout: dxa
+  lmx::plan_sums(L.in, LMX_SUMS_ROWS_TARGET, &rf[0], &cf[0]);
+  init(L.cols, 2);
+  job(L.cols.job[0], K, 0, 1);  // x: dA
+  job(L.cols.job[1], N, 0, 1);  // dout: dB
+  lmx::plan_sums(L.cols, LMX_SUMS_COLS_TARGET, &rf[1], &cf[1]);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
+  const size_t rp = size_t(L.rp);
+  L.sbt = take(rp * N * 2);
+  L.ap = take(rp * K * 2);
+  L.at = take(size_t(K) * rp * 2);
+  L.xa = take(size_t(M) * rp * 2);
+  L.dxa = take(size_t(M) * rp * 2);
+  L.rowpart = take(size_t(std::max(rf[0], rf[1])) * 4);
+  L.colpart = take(size_t(std::max(cf[0], cf[1])) * 4);
+  L.total = off;
+  return L;
+}
+
 // Workspace of lora_shrink_expand. Single launch: every counter sits in the leading 32 KiB that
 // every call leaves zero, at offsets that do not depend on the sizes, so calls of any size can
 // share one workspace: the shrink's arrival counters in [0, 16 KiB), the per-tile done counters
@@ -1222,6 +1258,103 @@ lora_status lora_mlp_backward(lora_dtype dtype, int64_t M, int64_t H, int64_t I,
     g.A2 = dxa_gu; g.lda2 = 2 * rp; g.B2 = agut; g.ldb2 = 2 * rp;
     g.C = static_cast<uint16_t*>(dx); g.ldc = lddx;
     g.M = int(M); g.N = int(H); g.K = int(2 * I); g.K2 = 2 * rp;
+    if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;
+  }
+  return LORA_OK;
+}
+
+lora_status lora_linear_prepare_backward(lora_dtype dtype, int64_t K, int64_t N, const void* w,
+                                         void* w_t, void* stream) {
+  if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
+  if (K < 1 || N < 1) return LORA_EINVAL;
+  if (K >= INT_MAX / 4 || N >= INT_MAX / 4) return LORA_EUNSUPPORTED;
+  if (K > 65535 * 64 || N > 65535 * 64) return LORA_EUNSUPPORTED;  // transpose grid rows
+  if (!w || !w_t) return LORA_EINVAL;
+  // W^T as [K][N]
+  return hip_status(lmx::launch_transpose(static_cast<const uint16_t*>(w), K,
+                                          static_cast<uint16_t*>(w_t), N, int(N), int(K),
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t lora_linear_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t N,
+                                           int32_t r) {
+  if (dtype != LORA_BF16 || M <= 0 || K <= 0 || N <= 0 || r <= 0 || r > 64) return 0;
+  return lin_bwd_layout(M, K, N, r).total;
+}
+
+lora_status lora_linear_backward(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r,
+                                 float scale, const void* x, int64_t ldx, const void* dout,
+                                 int64_t lddo, const void* w_t, const void* a, const void* b,
+                                 void* dx, int64_t lddx, void* da, void* db, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
+  if (M < 0 || K < 1 || N < 1 || r < 1) return LORA_EINVAL;
+  if (r > 64 || K % 32 != 0 || N % 32 != 0) return LORA_EUNSUPPORTED;
+  if (M >= INT_MAX || K >= INT_MAX / 8 || N >= INT_MAX / 8) return LORA_EUNSUPPORTED;
+  if (M == 0) return LORA_OK;
+  if (!x || !dout || !w_t || !a || !b || !dx || !da || !db) return LORA_EINVAL;
+  if (ldx < K || lddo < N || lddx < K) return LORA_EINVAL;
+  if (dx == x || dx == dout) return LORA_EINVAL;  // the saved input is never overwritten
+  if (!al16(x) || (ldx * 2) % 16 != 0 || !al16(dout) || (lddo * 2) % 16 != 0 || !al16(w_t))
+    return LORA_EUNSUPPORTED;
+  const LinBwdLayout L = lin_bwd_layout(M, K, N, r);
+  if (workspace == nullptr || workspace_bytes < L.total || !al16(workspace)) return LORA_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto W = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  auto u16 = [](const void* q) { return static_cast<const uint16_t*>(q); };
+  const int rp = int(L.rp);
+  uint16_t *sbt = W(L.sbt), *ap = W(L.ap), *at = W(L.at), *xa = W(L.xa), *dxa = W(L.dxa);
+  float* rowpart = reinterpret_cast<float*>(ws + L.rowpart);
+  float* colpart = reinterpret_cast<float*>(ws + L.colpart);
+  const int JB = L.in.JB;
+  auto ncb = [](const lmx::SumJobs& j, int q) { return j.blk0[q + 1] - j.blk0[q]; };
+  // 1. operands, rank rows past r zero: s B^T [rp][N], A [rp][K], A^T [K][rp]
+  {
+    lmx::TJobs t{};
+    t.n = 3;
+    t.job[0] = {u16(b), r, sbt, N, rp, int(N), 0, int(N), r, scale, false};
+    t.job[1] = {u16(a), K, ap, K, rp, int(K), 0, int(K), r, 1.0f, true};
+    t.job[2] = {u16(a), K, at, rp, int(K), rp, 0, r, int(K), 1.0f, false};
+    if (lmx::launch_small_transposes(t, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 2. xa = round(x A^T) and dxa = round(dout (s B)): sums over the columns of x and dout in one
+  //    launch, then their fixed-order reduction (rank padding zeroed)
+  {
+    lmx::SumJobs j = L.in;
+    j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].R[0] = ap; j.job[0].ldr = K;
+    j.job[1].P = u16(dout); j.job[1].ldp = lddo; j.job[1].R[0] = sbt; j.job[1].ldr = N;
+    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+    const int64_t rs = M * JB * 16;
+    lmx::RedJobs rj{};
+    rj.n = 2;
+    rj.JB = JB;
+    rj.job[0] = {rowpart + j.job[0].rp0, rs, xa, rp, 1, int(M), rp, r, ncb(j, 0), 1.0f};
+    rj.job[1] = {rowpart + j.job[1].rp0, rs, dxa, rp, 1, int(M), rp, r, ncb(j, 1), 1.0f};
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 3. sums over tokens: dA = dxa^T x [r][K], dB = s dout^T xa [N][r]
+  {
+    lmx::SumJobs j = L.cols;
+    j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].Q[0] = dxa; j.job[0].ldq = rp;
+    j.job[1].P = u16(dout); j.job[1].ldp = lddo; j.job[1].Q[0] = xa; j.job[1].ldq = rp;
+    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+    lmx::RedJobs rj{};
+    rj.n = 2;
+    rj.JB = JB;
+    rj.job[0] = {colpart + j.job[0].cp0, K * JB * 16, static_cast<uint16_t*>(da), 1, K, int(K), r, r,
+                 j.chunks, 1.0f};
+    rj.job[1] = {colpart + j.job[1].cp0, N * JB * 16, static_cast<uint16_t*>(db), r, 1, int(N), r, r,
+                 j.chunks, scale};
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 4. dx = round(dout W + dxa A): the plain GEMM over the reduction N with the LoRA term in K
+  {
+    lmx::GemmArgs g{};
+    g.A = u16(dout); g.lda = lddo; g.W0 = u16(w_t); g.W1 = u16(w_t); g.ldw = N;
+    g.A2 = dxa; g.lda2 = rp; g.B2 = at; g.ldb2 = rp;
+    g.C = static_cast<uint16_t*>(dx); g.ldc = lddx;
+    g.M = int(M); g.N = int(K); g.K = int(N); g.K2 = rp;
     if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;
   }
   return LORA_OK;

@@ -377,6 +377,40 @@ def linear_fused(x, w, a, b, scale: float, out: torch.Tensor | None = None,
     return out
 
 
+def linear_prepare_backward(w):
+    """W^T [K][N] of a projection's frozen weight w [N][K], as the backward reads it
+    (``lora_linear_prepare_backward``). Done once per layer."""
+    _dev(w)
+    N, K = w.shape
+    _bf16_mat(w, (N, K), "w")
+    w_t = torch.empty((K, N), dtype=torch.bfloat16, device=w.device)
+    _lib.lora_linear_prepare_backward(_lib.LORA_BF16, K, N, w, w_t, _stream())
+    return w_t
+
+
+def linear_backward(x, dout, w_t, a, b, scale: float, workspace: torch.Tensor | None = None):
+    """Gradients of ``linear_fused`` (``lora_linear_backward``): dict with dx [M][K], da [r][K],
+    db [N][r] (bf16). x: the saved input [M][K]; dout [M][N]; w_t = W^T [K][N] from
+    ``linear_prepare_backward``; a [r][K]; b [N][r]. x is only read."""
+    _dev(x, dout, w_t, a, b, workspace)
+    M, K = x.shape
+    N, r = b.shape
+    for t, shape, name in ((w_t, (K, N), "w_t"), (a, (r, K), "a"), (b, (N, r), "b"),
+                           (dout, (M, N), "dout")):
+        _bf16_mat(t, shape, name)
+    _bf16_in(x, "x")
+    dev, bf = x.device, torch.bfloat16
+    g = {"dx": torch.empty((M, K), dtype=bf, device=dev), "da": torch.empty((r, K), dtype=bf, device=dev),
+         "db": torch.empty((N, r), dtype=bf, device=dev)}
+    nbytes = _lib.lora_linear_backward_workspace_size(_lib.LORA_BF16, M, K, N, r)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _lib.lora_linear_backward(_lib.LORA_BF16, M, K, N, r, float(scale), x, _rows(x, "x"), dout, N,
+                              w_t, a, b, g["dx"], K, g["da"], g["db"], workspace, workspace.numel(),
+                              _stream())
+    return g
+
+
 def qkv_fused(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, scale: float,
               workspace: torch.Tensor | None = None):
     """(q, k, v) projections of one x with one adapter each (``lora_qkv_fused``)."""

@@ -447,6 +447,46 @@ size_t lora_qkv_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t N
                                int32_t r);
 
 /*
+ * lora_linear_prepare_backward -- the frozen weight of a projection in the layout
+ * lora_linear_backward reads, written once per layer (bf16): w [N][K] (nn.Linear [out][in]) ->
+ * w_t [K][N] (W^T, row-major, pitch N). Both device buffers are the caller's.
+ */
+lora_status lora_linear_prepare_backward(lora_dtype dtype, int64_t K, int64_t N, const void* w,
+                                         void* w_t, void* stream);
+
+/*
+ * lora_linear_backward -- gradients of the single-adapter LoRA projection (bf16) for the fast
+ * path's backward ("Add optional fast lora path for qwen2/qwen3 on npu", Verification advice:
+ * gradients of the projection fast paths checked against a reference; What this PR does: the
+ * LoRA projections of the attention). For y = x W^T + scale * round(x A^T) B^T and
+ * dout = dL/dy, with the forward's rounding points (every stored intermediate and result
+ * rounded once to bf16, fp32 accumulation):
+ *     xa  = round(x A^T)                     (recomputed)
+ *     dxa = round(dout (scale B))
+ *     dx  = round(dout W + dxa A)            [M][K]
+ *     dA  = round(dxa^T x)                   [r][K]
+ *     dB  = round(scale dout^T xa)           [N][r]
+ * The frozen W takes no gradient. scale is folded into a bf16 copy of B (exact for a power of
+ * two, as alpha / rank usually is).
+ *
+ *   x [M][ldx >= K] (the saved input, only read); dout [M][lddo >= N]; w_t = W^T [K][N] from
+ *   lora_linear_prepare_backward; a [r][K]; b [N][r]; dx [M][lddx >= K], which must not be x or
+ *   dout; da [r][K]; db [N][r] (contiguous). 1 <= r <= 64; K and N multiples of 32; x, dout,
+ *   w_t 16-byte aligned with 16-byte aligned row pitches. workspace of
+ *   lora_linear_backward_workspace_size(...) bytes, 16-byte aligned, not read before written.
+ * Errors: LORA_EINVAL (sizes, null pointers, pitches, dx aliasing an input),
+ * LORA_EUNSUPPORTED (dtype, rank, multiples, alignment), LORA_EWORKSPACE, LORA_EHIP.
+ */
+lora_status lora_linear_backward(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r,
+                                 float scale, const void* x, int64_t ldx, const void* dout,
+                                 int64_t lddo, const void* w_t, const void* a, const void* b,
+                                 void* dx, int64_t lddx, void* da, void* db, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+size_t lora_linear_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t N,
+                                           int32_t r);
+
+/*
  * lora_embedding_a -- the LoRA-A product of an embedding layer (the embedding LoRA-A forward of
  * "Decode LoRA kernels are optimized", Summary and Behaviour changes; the page does not print
  * the arithmetic, this is its reading): for segment g (adapter a, rank r = lora_ranks[a]) and

@@ -1,0 +1,116 @@
+"""GPU parity of the LoRA projection backward (lora_linear_prepare_backward, lora_linear_backward)
+through the C ABI against the CPU oracle computed from x, dout and the weights alone.
+
+The three gradients are sums whose terms carry bf16-stored factors (xa, dxa), so they are
+compared with the bar of the MLP backward (tests/parity.py): |err| <= 1e-2 + 1e-2 |ref| + 2u RSS
+per entry (u = 2^-8, RSS the root-sum-square of the sum's terms from the oracle's values) and
+normwise within 2u; the fraction outside the plain bar 1e-2 + 1e-2 |ref| is printed. Small
+projections (ragged token tiles, odd and full ranks, a scale that is not a power of two) and the
+Qwen3-8B output projection (M = 4096, K = N = 4096, r = 16, scale 4) compare every output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import lora_inputs as li
+import oracle
+from tests.parity import assert_close_sum_lowp, f64, strict_fail_fraction
+
+pytestmark = pytest.mark.gpu
+
+
+def _alp():
+    return __import__("adapter_lora_projection_amd")
+
+
+def _case(seed, M, K, N, r, scale):
+    c = li.config_qkv(seed=seed, M=M, H=K, Nq=N, Nkv=32, r=r, scale=scale)
+    (dout,) = li.projection_douts(seed=seed, M=M, widths=(N,))
+    return c, dout  # the projection under test: w_q [N][K], a_q [r][K], b_q [N][r]
+
+
+def _gpu(c, dout):
+    alp = _alp()
+    g = lambda t: t.to("cuda").contiguous()
+    x, w, a, b = g(c.x), g(c.w_q), g(c.a_q), g(c.b_q)
+    w_t = alp.linear_prepare_backward(w)
+    x_before = x.clone()
+    out = alp.linear_backward(x, g(dout), w_t, a, b, c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(x, x_before)  # the saved input is only read
+    assert torch.equal(w_t.cpu(), c.w_q.T.contiguous())  # W^T bit for bit
+    return {k: t.cpu() for k, t in out.items()}
+
+
+def _rss(c, dout):
+    """Root-sum-square of the terms of each gradient's sum, from the oracle's fp64 values:
+    dx[m][k] = sum_n dout W + sum_j dxa A; dA[j][k] = sum_m dxa x; dB[n][j] = s sum_m dout xa."""
+    X, D, W, A, B = (f64(t) for t in (c.x, dout, c.w_q, c.a_q, c.b_q))
+    xa = oracle.rho(X @ A.T, "bf16")
+    dxa = oracle.rho(c.scale * (D @ B), "bf16")
+    sq = np.square
+    return {"dx": np.sqrt(sq(D) @ sq(W) + sq(dxa) @ sq(A)),
+            "da": np.sqrt(sq(dxa).T @ sq(X)),
+            "db": np.sqrt(c.scale ** 2 * (sq(D).T @ sq(xa)))}
+
+
+def _check(c, dout, got):
+    ref = oracle.lora_linear_backward(c.x, dout, c.w_q, c.a_q, c.b_q, c.scale, "bf16")
+    rss = _rss(c, dout)
+    for k in ("dx", "da", "db"):
+        print(f"{k}: outside the plain bar {strict_fail_fraction(got[k], ref[k]):.2e}", flush=True)
+        assert_close_sum_lowp(got[k], ref[k], rss[k], k)
+
+
+@pytest.mark.parametrize("M,K,N,r,scale", [(300, 256, 192, 16, 4.0), (77, 128, 320, 7, 1.5),
+                                           (513, 320, 256, 64, 2.0), (16, 64, 96, 32, 0.5)])
+def test_small_projections(M, K, N, r, scale):
+    c, dout = _case(31, M, K, N, r, scale)
+    print("case", M, K, N, r, scale, flush=True)
+    _check(c, dout, _gpu(c, dout))
+
+
+def test_b_zero():
+    """B = 0: dA is exactly zero and dx is the plain product dout W."""
+    c, dout = _case(32, 200, 256, 128, 16, 4.0)
+    c.b_q = torch.zeros_like(c.b_q)
+    got = _gpu(c, dout)
+    assert int(got["da"].count_nonzero()) == 0
+    _check(c, dout, got)
+
+
+def test_qwen3_8b_output_projection():
+    """The attention output projection of the Qwen3-8B layer: x [4096][4096] (the attention
+    output), W_o [4096][4096], r = 16, scale 4; every output of the three gradients."""
+    c, dout = _case(5, 4096, 4096, 4096, 16, 4.0)
+    print("case qwen3-8b o_proj", flush=True)
+    _check(c, dout, _gpu(c, dout))
+
+
+def test_argument_errors():
+    from adapter_lora_projection_amd import _lib
+
+    alp = _alp()
+    c, dout = _case(33, 64, 128, 96, 8, 2.0)
+    g = lambda t: t.to("cuda").contiguous()
+    x, d, a, b = g(c.x), g(dout), g(c.a_q), g(c.b_q)
+    w_t = alp.linear_prepare_backward(g(c.w_q))
+    n = _lib.lora_linear_backward_workspace_size(_lib.LORA_BF16, 64, 128, 96, 8)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    da = torch.empty((8, 128), dtype=torch.bfloat16, device="cuda")
+    db = torch.empty((96, 8), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    L = _lib.lib()
+    call = lambda dx, K=128, N=96, nbytes=n: L.lora_linear_backward(
+        _lib.LORA_BF16, 64, K, N, 8, 2.0, x.data_ptr(), 128, d.data_ptr(), 96, w_t.data_ptr(),
+        a.data_ptr(), b.data_ptr(), dx, 128, da.data_ptr(), db.data_ptr(), ws.data_ptr(), nbytes,
+        stream)
+    assert call(x.data_ptr()) == _lib.LORA_EINVAL          # dx aliasing the saved input
+    assert call(d.data_ptr()) == _lib.LORA_EINVAL          # ... or dout
+    dx = torch.empty((64, 128), dtype=torch.bfloat16, device="cuda")
+    assert call(dx.data_ptr(), K=120) == _lib.LORA_EUNSUPPORTED  # K not a multiple of 32
+    assert call(dx.data_ptr(), nbytes=n - 256) == _lib.LORA_EWORKSPACE
+    torch.cuda.synchronize()
+    assert call(dx.data_ptr()) == 0
+    torch.cuda.synchronize()
