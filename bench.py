@@ -211,6 +211,50 @@ def mlp_backward_flops(M: int, H: int, I: int, r: int) -> tuple[int, int]:
     return base, lora
 
 
+def projection_backward_object(steps: int, warmup: int) -> dict:
+    """The LoRA projection backward (bf16) at the Qwen3-8B output projection (M = 4096, K = N =
+    4096, r = 16, scale 4): lora_linear_backward, K calls back to back after a warm-up, HIP
+    events on its stream; flops of the gradient arithmetic (dx = dout W + dxa A, dxa, dA, dB; the
+    recomputed xa not counted), against dense bf16 MFMA."""
+    import torch
+
+    import lora_inputs as li
+    from adapter_lora_projection_amd import _lib
+
+    M = K = N = 4096
+    r, scale = 16, 4.0
+    c = li.config_qkv(seed=5, M=M, H=K, Nq=N, Nkv=32, r=r, scale=scale)
+    (dout,) = li.projection_douts(seed=5, M=M, widths=(N,))
+    g = lambda t: t.to("cuda").contiguous()
+    x, d, w, a, b = g(c.x), g(dout), g(c.w_q), g(c.a_q), g(c.b_q)
+    w_t = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    _lib.lora_linear_prepare_backward(_lib.LORA_BF16, K, N, w, w_t, stream)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    da = torch.empty((r, K), dtype=torch.bfloat16, device="cuda")
+    db = torch.empty((N, r), dtype=torch.bfloat16, device="cuda")
+    n = _lib.lora_linear_backward_workspace_size(_lib.LORA_BF16, M, K, N, r)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        _lib.lora_linear_backward(_lib.LORA_BF16, M, K, N, r, scale, x, K, d, N, w_t, a, b, dx, K,
+                                  da, db, ws, n, stream)
+
+    for _ in range(max(warmup, 30)):
+        call()
+    torch.cuda.synchronize()
+    ms, _ = timed_windows(call, steps)
+    flops = 2 * M * N * K + 4 * M * N * r + 4 * M * r * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"LoRA projection backward bf16 (Qwen3-8B output projection), M={M} K={K} "
+                        f"N={N} r={r} scale={scale:g}", "ms_per_call": round(ms, 4),
+            "flops_per_call": int(flops), "value": round(tflops, 1), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "lora_linear_backward (all launches of one call)"}}
+
+
 def mlp_backward_object(steps: int, warmup: int) -> dict:
     """The LoRA MLP backward (lora_mlp_backward, bf16, M=4096, H=4096, I=12288, r=16, scale 4)
     after one training forward (lora_mlp_fused_train, timed beside it): K calls back to back
@@ -648,6 +692,8 @@ def main() -> int:
     if "backward" in extras:
         print("[bench] timing the LoRA MLP training forward and backward", file=sys.stderr, flush=True)
         out["mlp_backward"] = mlp_backward_object(args.steps, args.warmup)
+        print("[bench] timing the LoRA projection backward", file=sys.stderr, flush=True)
+        out["projection_backward"] = projection_backward_object(args.steps, args.warmup)
     if "embedding" in extras:
         print("[bench] timing the embedding LoRA-A product", file=sys.stderr, flush=True)
         out["embedding_a"] = embedding_object(args.steps, args.warmup)

@@ -65,7 +65,7 @@ def command_block(*keys: str) -> str:
             "\ncd $GRAFT_REPO_ROOT && python bench_profiles.py gpurun_out\n```\n\n")
 SGMV_SHRINK = ("shrink_kernel", "shrink_lds_kernel", "shrink_gemv_kernel")
 GEMM_LABEL = {
-    "gemm_lora_kernel<0": "plain LoRA-in-K GEMM (mlp down, backward dx, attention q/k/v, o)",
+    "gemm_lora_kernel<0": "plain LoRA-in-K GEMM (mlp down, mlp and projection backward dx, attention q/k/v, o)",
     "gemm_lora_kernel<1": "mlp gate/up + SwiGLU (forward)",
     "gemm_lora_kernel<2": "mlp gate/up + SwiGLU (training forward, stores e, v)",
     "gemm_lora_kernel<3": "mlp backward: dhmid + SwiGLU backward",
