@@ -49,6 +49,11 @@ SIGNATURES = {
     "lora_linear_backward": (_i32, [_i32, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64, _vp,
                                     _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "lora_linear_backward_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32]),
+    "lora_qkv_prepare_backward": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "lora_qkv_backward": (_i32, [_i32, _i64, _i64, _i64, _i64, _i32, ctypes.c_float, _vp, _i64,
+                                 _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lora_qkv_backward_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i64, _i32]),
     "lora_schedule_tiles": (_i32, [_i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                    _sz, _vp]),
     "lora_shrink_ex": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
@@ -223,6 +228,27 @@ def lora_linear_backward(dtype, M, K, N, r, scale, x, ldx, dout, lddo, w_t, a, b
 
 def lora_linear_backward_workspace_size(dtype, M, K, N, r) -> int:
     return int(lib().lora_linear_backward_workspace_size(dtype, M, K, N, r))
+
+
+def lora_qkv_prepare_backward(dtype, K, Nq, Nkv, w_q, w_k, w_v, w_qkv_t, stream) -> None:
+    _check("lora_qkv_prepare_backward",
+           lib().lora_qkv_prepare_backward(dtype, K, Nq, Nkv, _p(w_q), _p(w_k), _p(w_v),
+                                           _p(w_qkv_t), stream))
+
+
+def lora_qkv_backward(dtype, M, K, Nq, Nkv, r, scale, x, ldx, dq, lddq, dk, lddk, dv, lddv,
+                      w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, dx, lddx, da_q, db_q, da_k, db_k,
+                      da_v, db_v, workspace, workspace_bytes, stream) -> None:
+    st = lib().lora_qkv_backward(dtype, M, K, Nq, Nkv, r, scale, _p(x), ldx, _p(dq), lddq, _p(dk),
+                                 lddk, _p(dv), lddv, _p(w_qkv_t), _p(a_q), _p(b_q), _p(a_k),
+                                 _p(b_k), _p(a_v), _p(b_v), _p(dx), lddx, _p(da_q), _p(db_q),
+                                 _p(da_k), _p(db_k), _p(da_v), _p(db_v), _p(workspace),
+                                 workspace_bytes, stream)
+    _check("lora_qkv_backward", st)
+
+
+def lora_qkv_backward_workspace_size(dtype, M, K, Nq, Nkv, r) -> int:
+    return int(lib().lora_qkv_backward_workspace_size(dtype, M, K, Nq, Nkv, r))
 
 
 LORA_SHRINK_EXPAND_FLAG_OFFSET = 32764  # byte offset of the wait-bound flag in the workspace

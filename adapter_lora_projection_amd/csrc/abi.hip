@@ -620,38 +620,61 @@ lora_status shrink_impl(lora_dtype dtype, int64_t T, int64_t K, int32_t S, int32
   return LORA_OK;
 }
 
-// Workspace of the projection backward: byte offsets of its sections (256-byte aligned).
+// Workspace of the projection backward (P = 1, or 3 projections of one x): byte offsets of its
+// sections (256-byte aligned). Token-side sums need P + 2 jobs (x carries at most two Q
+// operands per job) and a sums launch takes four, so P = 3 makes two launches (cols, cols2).
 struct LinBwdLayout {
   int64_t rp;
-  lmx::SumJobs in, cols;  // row sides (xa from x, dxa from dout); sums over tokens (dA, dB)
-  size_t sbt, ap, at, xa, dxa, rowpart, colpart, total;
+  int P, ncols;           // projections; sums launches on the token side (1 or 2)
+  lmx::SumJobs in, cols, cols2;
+  size_t sbt[3], ap[3], at, xa, dxa, dcat, rowpart, colpart, total;
 };
 
-LinBwdLayout lin_bwd_layout(int64_t M, int64_t K, int64_t N, int32_t r) {
+LinBwdLayout lin_bwd_layout(int64_t M, int64_t K, const int64_t* N, int P, int32_t r) {
   LinBwdLayout L{};
   L.rp = cdiv(r, 32) * 32;
+  L.P = P;
   const int JB = int(cdiv(r, 16));
-  int64_t rf[2] = {0, 0}, cf[2] = {0, 0};
+  int64_t rf[3] = {0, 0, 0}, cf[3] = {0, 0, 0};
   auto init = [&](lmx::SumJobs& j, int n) { j.n = n; j.M = int(M); j.JB = JB; };
   auto job = [](lmx::SumJob& j, int64_t C, int nr, int nh) { j.C = int(C); j.nr = nr; j.nh = nh; };
-  init(L.in, 2);
-  job(L.in.job[0], K, 1, 0);  // x: xa
-  job(L.in.job[1], N, 1, 0);  // dout: dxa
+  init(L.in, P + 1);
+  job(L.in.job[0], K, P, 0);                                 // x: xa of every projection
+  for (int p = 0; p < P; ++p) job(L.in.job[1 + p], N[p], 1, 0);  // dout_p: dxa_p
   lmx::plan_sums(L.in, LMX_SUMS_ROWS_TARGET, &rf[0], &cf[0]);
-  init(L.cols, 2);
-  job(L.cols.job[0], K, 0, 1);  // x: dA
-  job(L.cols.job[1], N, 0, 1);  // dout: dB
-  lmx::plan_sums(L.cols, LMX_SUMS_COLS_TARGET, &rf[1], &cf[1]);
+  if (P == 1) {
+    L.ncols = 1;
+    init(L.cols, 2);
+    job(L.cols.job[0], K, 0, 1);     // x: dA
+    job(L.cols.job[1], N[0], 0, 1);  // dout: dB
+    lmx::plan_sums(L.cols, LMX_SUMS_COLS_TARGET, &rf[1], &cf[1]);
+  } else {
+    L.ncols = 2;
+    init(L.cols, 4);
+    job(L.cols.job[0], K, 0, 2);     // x: dA_q, dA_k
+    job(L.cols.job[1], K, 0, 1);     // x: dA_v
+    job(L.cols.job[2], N[0], 0, 1);  // dq: dB_q
+    job(L.cols.job[3], N[1], 0, 1);  // dk: dB_k
+    lmx::plan_sums(L.cols, LMX_SUMS_COLS_TARGET, &rf[1], &cf[1]);
+    init(L.cols2, 1);
+    job(L.cols2.job[0], N[2], 0, 1);  // dv: dB_v
+    lmx::plan_sums(L.cols2, LMX_SUMS_COLS_TARGET, &rf[2], &cf[2]);
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
   const size_t rp = size_t(L.rp);
-  L.sbt = take(rp * N * 2);
-  L.ap = take(rp * K * 2);
-  L.at = take(size_t(K) * rp * 2);
-  L.xa = take(size_t(M) * rp * 2);
-  L.dxa = take(size_t(M) * rp * 2);
-  L.rowpart = take(size_t(std::max(rf[0], rf[1])) * 4);
-  L.colpart = take(size_t(std::max(cf[0], cf[1])) * 4);
+  int64_t ntot = 0;
+  for (int p = 0; p < P; ++p) {
+    L.sbt[p] = take(rp * N[p] * 2);
+    L.ap[p] = take(rp * K * 2);
+    ntot += N[p];
+  }
+  L.at = take(size_t(K) * P * rp * 2);
+  L.xa = take(size_t(M) * P * rp * 2);
+  L.dxa = take(size_t(M) * P * rp * 2);
+  L.dcat = P > 1 ? take(size_t(M) * ntot * 2) : 0;
+  L.rowpart = take(size_t(std::max({rf[0], rf[1], rf[2]})) * 4);
+  L.colpart = take(size_t(std::max({cf[0], cf[1], cf[2]})) * 4);
   L.total = off;
   return L;
 }
@@ -700,6 +723,168 @@ PairWs pair_ws(int dtype, int64_t T, int64_t K, int32_t S, int32_t R, int32_t G)
   w.expand_off = align256(st);
   w.two_total = w.expand_off + schedule_bytes(T, G, 16);
   return w;
+}
+
+// The projection backward for P = 1 or 3 projections of one x (the query, key and value
+// projections; their dx terms summed and rounded once). w_t = [W_0^T | .. | W_{P-1}^T] [K][Ntot].
+lora_status linear_backward(lora_dtype dtype, int64_t M, int64_t K, const int64_t* N, int P,
+                            int32_t r, float scale, const void* x, int64_t ldx,
+                            const void* const* dout, const int64_t* lddo, const void* w_t,
+                            const void* const* a, const void* const* b, void* dx, int64_t lddx,
+                            void* const* da, void* const* db, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
+  if (M < 0 || K < 1 || r < 1) return LORA_EINVAL;
+  int64_t ntot = 0;
+  for (int p = 0; p < P; ++p) {
+    if (N[p] < 1) return LORA_EINVAL;
+    if (N[p] % 32 != 0 || N[p] >= INT_MAX / 8) return LORA_EUNSUPPORTED;
+    ntot += N[p];
+  }
+  if (r > 64 || K % 32 != 0) return LORA_EUNSUPPORTED;
+  if (M >= INT_MAX || K >= INT_MAX / 8 || ntot >= INT_MAX / 8) return LORA_EUNSUPPORTED;
+  if (M == 0) return LORA_OK;
+  if (!x || !w_t || !dx) return LORA_EINVAL;
+  for (int p = 0; p < P; ++p)
+    if (!dout[p] || !a[p] || !b[p] || !da[p] || !db[p]) return LORA_EINVAL;
+  if (ldx < K || lddx < K) return LORA_EINVAL;
+  for (int p = 0; p < P; ++p) {
+    if (lddo[p] < N[p]) return LORA_EINVAL;
+    if (dx == dout[p]) return LORA_EINVAL;
+  }
+  if (dx == x) return LORA_EINVAL;  // the saved input is never overwritten
+  if (!al16(x) || (ldx * 2) % 16 != 0 || !al16(w_t)) return LORA_EUNSUPPORTED;
+  for (int p = 0; p < P; ++p)
+    if (!al16(dout[p]) || (lddo[p] * 2) % 16 != 0) return LORA_EUNSUPPORTED;
+  const LinBwdLayout L = lin_bwd_layout(M, K, N, P, r);
+  if (workspace == nullptr || workspace_bytes < L.total || !al16(workspace)) return LORA_EWORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto W = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  auto u16 = [](const void* q) { return static_cast<const uint16_t*>(q); };
+  const int rp = int(L.rp), prp = P * rp;
+  uint16_t *at = W(L.at), *xa = W(L.xa), *dxa = W(L.dxa);
+  float* rowpart = reinterpret_cast<float*>(ws + L.rowpart);
+  float* colpart = reinterpret_cast<float*>(ws + L.colpart);
+  const int JB = L.in.JB;
+  auto ncb = [](const lmx::SumJobs& j, int q) { return j.blk0[q + 1] - j.blk0[q]; };
+  // 1. operands, rank rows past r zero: s B_p^T [rp][N_p], A_p [rp][K], and
+  //    [A_0^T | .. | A_{P-1}^T] [K][P rp]
+  {
+    lmx::TJobs t{};
+    t.n = 3 * P;
+    for (int p = 0; p < P; ++p) {
+      t.job[3 * p] = {u16(b[p]), r, W(L.sbt[p]), N[p], rp, int(N[p]), 0, int(N[p]), r, scale, false};
+      t.job[3 * p + 1] = {u16(a[p]), K, W(L.ap[p]), K, rp, int(K), 0, int(K), r, 1.0f, true};
+      t.job[3 * p + 2] = {u16(a[p]), K, at + p * rp, prp, int(K), rp, 0, r, int(K), 1.0f, false};
+    }
+    if (lmx::launch_small_transposes(t, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 2. xa_p = round(x A_p^T) in one pass over x and dxa_p = round(dout_p (s B_p)): the sums
+  //    kernel's row side in one launch, then the fixed-order reduction (rank padding zeroed)
+  {
+    lmx::SumJobs j = L.in;
+    j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].ldr = K;
+    for (int p = 0; p < P; ++p) {
+      j.job[0].R[p] = W(L.ap[p]);
+      j.job[1 + p].P = u16(dout[p]); j.job[1 + p].ldp = lddo[p];
+      j.job[1 + p].R[0] = W(L.sbt[p]); j.job[1 + p].ldr = N[p];
+    }
+    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+    const int64_t rs = M * JB * 16;
+    const int nx = ncb(j, 0);
+    lmx::RedJobs rj{};
+    rj.n = 2 * P;
+    rj.JB = JB;
+    for (int p = 0; p < P; ++p) {
+      rj.job[p] = {rowpart + j.job[0].rp0 + p * nx * rs, rs, xa + p * rp, prp, 1, int(M), rp, r,
+                   nx, 1.0f};
+      rj.job[P + p] = {rowpart + j.job[1 + p].rp0, rs, dxa + p * rp, prp, 1, int(M), rp, r,
+                       ncb(j, 1 + p), 1.0f};
+    }
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
+  }
+  // 3. sums over tokens: dA_p = dxa_p^T x [r][K], dB_p = s dout_p^T xa_p [N_p][r]
+  auto out16 = [](void* q) { return static_cast<uint16_t*>(q); };
+  auto da_job = [&](lmx::RedJob& rj, const float* src, void* out) {
+    rj = {src, K * JB * 16, out16(out), 1, K, int(K), r, r, 0, 1.0f};
+  };
+  auto db_job = [&](lmx::RedJob& rj, const float* src, int p) {
+    rj = {src, N[p] * JB * 16, out16(db[p]), r, 1, int(N[p]), r, r, 0, scale};
+  };
+  if (P == 1) {
+    lmx::SumJobs j = L.cols;
+    j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].Q[0] = dxa; j.job[0].ldq = prp;
+    j.job[1].P = u16(dout[0]); j.job[1].ldp = lddo[0]; j.job[1].Q[0] = xa; j.job[1].ldq = prp;
+    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+    lmx::RedJobs rj{};
+    rj.n = 2;
+    rj.JB = JB;
+    da_job(rj.job[0], colpart + j.job[0].cp0, da[0]);
+    db_job(rj.job[1], colpart + j.job[1].cp0, 0);
+    for (int q = 0; q < 2; ++q) rj.job[q].np = j.chunks;
+    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
+  } else {
+    {
+      lmx::SumJobs j = L.cols;
+      j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].ldq = prp;
+      j.job[0].Q[0] = dxa; j.job[0].Q[1] = dxa + rp;
+      j.job[1].P = u16(x); j.job[1].ldp = ldx; j.job[1].Q[0] = dxa + 2 * rp; j.job[1].ldq = prp;
+      for (int p = 0; p < 2; ++p) {
+        j.job[2 + p].P = u16(dout[p]); j.job[2 + p].ldp = lddo[p];
+        j.job[2 + p].Q[0] = xa + p * rp; j.job[2 + p].ldq = prp;
+      }
+      if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+      const int64_t hstride = int64_t(j.chunks) * K * JB * 16;
+      lmx::RedJobs rj{};
+      rj.n = 5;
+      rj.JB = JB;
+      da_job(rj.job[0], colpart + j.job[0].cp0, da[0]);
+      da_job(rj.job[1], colpart + j.job[0].cp0 + hstride, da[1]);
+      da_job(rj.job[2], colpart + j.job[1].cp0, da[2]);
+      db_job(rj.job[3], colpart + j.job[2].cp0, 0);
+      db_job(rj.job[4], colpart + j.job[3].cp0, 1);
+      for (int q = 0; q < 5; ++q) rj.job[q].np = j.chunks;
+      if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
+    }
+    {
+      lmx::SumJobs j = L.cols2;
+      j.job[0].P = u16(dout[2]); j.job[0].ldp = lddo[2];
+      j.job[0].Q[0] = xa + 2 * rp; j.job[0].ldq = prp;
+      if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
+      lmx::RedJobs rj{};
+      rj.n = 1;
+      rj.JB = JB;
+      db_job(rj.job[0], colpart + j.job[0].cp0, 2);
+      rj.job[0].np = j.chunks;
+      if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
+    }
+  }
+  // 4. dx = round(sum_p dout_p W_p + dxa_p A_p): the plain GEMM over the reduction Ntot with the
+  //    LoRA terms in K ([dout_0 | ..] copied side by side first when P > 1)
+  const uint16_t* dA = u16(dout[0]);
+  int64_t ldA = lddo[0];
+  if (P > 1) {
+    uint16_t* dcat = W(L.dcat);
+    int64_t c0 = 0;
+    for (int p = 0; p < P; ++p) {
+      if (hipMemcpy2DAsync(dcat + c0, size_t(ntot) * 2, dout[p], size_t(lddo[p]) * 2,
+                           size_t(N[p]) * 2, size_t(M), hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return LORA_EHIP;
+      c0 += N[p];
+    }
+    dA = dcat;
+    ldA = ntot;
+  }
+  {
+    lmx::GemmArgs g{};
+    g.A = dA; g.lda = ldA; g.W0 = u16(w_t); g.W1 = u16(w_t); g.ldw = ntot;
+    g.A2 = dxa; g.lda2 = prp; g.B2 = at; g.ldb2 = prp;
+    g.C = static_cast<uint16_t*>(dx); g.ldc = lddx;
+    g.M = int(M); g.N = int(K); g.K = int(ntot); g.K2 = prp;
+    if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;
+  }
+  return LORA_OK;
 }
 
 }  // namespace
@@ -1279,7 +1464,7 @@ lora_status lora_linear_prepare_backward(lora_dtype dtype, int64_t K, int64_t N,
 size_t lora_linear_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t N,
                                            int32_t r) {
   if (dtype != LORA_BF16 || M <= 0 || K <= 0 || N <= 0 || r <= 0 || r > 64) return 0;
-  return lin_bwd_layout(M, K, N, r).total;
+  return lin_bwd_layout(M, K, &N, 1, r).total;
 }
 
 lora_status lora_linear_backward(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r,
@@ -1287,77 +1472,60 @@ lora_status lora_linear_backward(lora_dtype dtype, int64_t M, int64_t K, int64_t
                                  int64_t lddo, const void* w_t, const void* a, const void* b,
                                  void* dx, int64_t lddx, void* da, void* db, void* workspace,
                                  size_t workspace_bytes, void* stream) {
+  const void* d[1] = {dout};
+  const int64_t ld[1] = {lddo};
+  const void* aa[1] = {a};
+  const void* bb[1] = {b};
+  void* dda[1] = {da};
+  void* ddb[1] = {db};
+  return linear_backward(dtype, M, K, &N, 1, r, scale, x, ldx, d, ld, w_t, aa, bb, dx, lddx, dda,
+                         ddb, workspace, workspace_bytes, stream);
+}
+
+lora_status lora_qkv_prepare_backward(lora_dtype dtype, int64_t K, int64_t Nq, int64_t Nkv,
+                                      const void* w_q, const void* w_k, const void* w_v,
+                                      void* w_qkv_t, void* stream) {
   if (dtype != LORA_BF16) return LORA_EUNSUPPORTED;
-  if (M < 0 || K < 1 || N < 1 || r < 1) return LORA_EINVAL;
-  if (r > 64 || K % 32 != 0 || N % 32 != 0) return LORA_EUNSUPPORTED;
-  if (M >= INT_MAX || K >= INT_MAX / 8 || N >= INT_MAX / 8) return LORA_EUNSUPPORTED;
-  if (M == 0) return LORA_OK;
-  if (!x || !dout || !w_t || !a || !b || !dx || !da || !db) return LORA_EINVAL;
-  if (ldx < K || lddo < N || lddx < K) return LORA_EINVAL;
-  if (dx == x || dx == dout) return LORA_EINVAL;  // the saved input is never overwritten
-  if (!al16(x) || (ldx * 2) % 16 != 0 || !al16(dout) || (lddo * 2) % 16 != 0 || !al16(w_t))
-    return LORA_EUNSUPPORTED;
-  const LinBwdLayout L = lin_bwd_layout(M, K, N, r);
-  if (workspace == nullptr || workspace_bytes < L.total || !al16(workspace)) return LORA_EWORKSPACE;
+  if (K < 1 || Nq < 1 || Nkv < 1) return LORA_EINVAL;
+  if (K >= INT_MAX / 4 || Nq >= INT_MAX / 8 || Nkv >= INT_MAX / 8) return LORA_EUNSUPPORTED;
+  if (K > 65535 * 64 || Nq > 65535 * 64 || Nkv > 65535 * 64) return LORA_EUNSUPPORTED;
+  if (!w_q || !w_k || !w_v || !w_qkv_t) return LORA_EINVAL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  auto W = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   auto u16 = [](const void* q) { return static_cast<const uint16_t*>(q); };
-  const int rp = int(L.rp);
-  uint16_t *sbt = W(L.sbt), *ap = W(L.ap), *at = W(L.at), *xa = W(L.xa), *dxa = W(L.dxa);
-  float* rowpart = reinterpret_cast<float*>(ws + L.rowpart);
-  float* colpart = reinterpret_cast<float*>(ws + L.colpart);
-  const int JB = L.in.JB;
-  auto ncb = [](const lmx::SumJobs& j, int q) { return j.blk0[q + 1] - j.blk0[q]; };
-  // 1. operands, rank rows past r zero: s B^T [rp][N], A [rp][K], A^T [K][rp]
-  {
-    lmx::TJobs t{};
-    t.n = 3;
-    t.job[0] = {u16(b), r, sbt, N, rp, int(N), 0, int(N), r, scale, false};
-    t.job[1] = {u16(a), K, ap, K, rp, int(K), 0, int(K), r, 1.0f, true};
-    t.job[2] = {u16(a), K, at, rp, int(K), rp, 0, r, int(K), 1.0f, false};
-    if (lmx::launch_small_transposes(t, st) != hipSuccess) return LORA_EHIP;
-  }
-  // 2. xa = round(x A^T) and dxa = round(dout (s B)): sums over the columns of x and dout in one
-  //    launch, then their fixed-order reduction (rank padding zeroed)
-  {
-    lmx::SumJobs j = L.in;
-    j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].R[0] = ap; j.job[0].ldr = K;
-    j.job[1].P = u16(dout); j.job[1].ldp = lddo; j.job[1].R[0] = sbt; j.job[1].ldr = N;
-    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
-    const int64_t rs = M * JB * 16;
-    lmx::RedJobs rj{};
-    rj.n = 2;
-    rj.JB = JB;
-    rj.job[0] = {rowpart + j.job[0].rp0, rs, xa, rp, 1, int(M), rp, r, ncb(j, 0), 1.0f};
-    rj.job[1] = {rowpart + j.job[1].rp0, rs, dxa, rp, 1, int(M), rp, r, ncb(j, 1), 1.0f};
-    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
-  }
-  // 3. sums over tokens: dA = dxa^T x [r][K], dB = s dout^T xa [N][r]
-  {
-    lmx::SumJobs j = L.cols;
-    j.job[0].P = u16(x); j.job[0].ldp = ldx; j.job[0].Q[0] = dxa; j.job[0].ldq = rp;
-    j.job[1].P = u16(dout); j.job[1].ldp = lddo; j.job[1].Q[0] = xa; j.job[1].ldq = rp;
-    if (lmx::launch_sums(j, rowpart, colpart, st) != hipSuccess) return LORA_EHIP;
-    lmx::RedJobs rj{};
-    rj.n = 2;
-    rj.JB = JB;
-    rj.job[0] = {colpart + j.job[0].cp0, K * JB * 16, static_cast<uint16_t*>(da), 1, K, int(K), r, r,
-                 j.chunks, 1.0f};
-    rj.job[1] = {colpart + j.job[1].cp0, N * JB * 16, static_cast<uint16_t*>(db), r, 1, int(N), r, r,
-                 j.chunks, scale};
-    if (lmx::launch_reduce_sums(rj, st) != hipSuccess) return LORA_EHIP;
-  }
-  // 4. dx = round(dout W + dxa A): the plain GEMM over the reduction N with the LoRA term in K
-  {
-    lmx::GemmArgs g{};
-    g.A = u16(dout); g.lda = lddo; g.W0 = u16(w_t); g.W1 = u16(w_t); g.ldw = N;
-    g.A2 = dxa; g.lda2 = rp; g.B2 = at; g.ldb2 = rp;
-    g.C = static_cast<uint16_t*>(dx); g.ldc = lddx;
-    g.M = int(M); g.N = int(K); g.K = int(N); g.K2 = rp;
-    if (lmx::launch_gemm_lora(g, lmx::kGemmPlain, st) != hipSuccess) return LORA_EHIP;
-  }
+  uint16_t* t = static_cast<uint16_t*>(w_qkv_t);
+  const int64_t ntot = Nq + 2 * Nkv;
+  // [W_q^T | W_k^T | W_v^T] as [K][Nq + 2 Nkv]
+  if (lmx::launch_transpose(u16(w_q), K, t, ntot, int(Nq), int(K), st) != hipSuccess ||
+      lmx::launch_transpose(u16(w_k), K, t + Nq, ntot, int(Nkv), int(K), st) != hipSuccess ||
+      lmx::launch_transpose(u16(w_v), K, t + Nq + Nkv, ntot, int(Nkv), int(K), st) != hipSuccess)
+    return LORA_EHIP;
   return LORA_OK;
+}
+
+size_t lora_qkv_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq,
+                                        int64_t Nkv, int32_t r) {
+  if (dtype != LORA_BF16 || M <= 0 || K <= 0 || Nq <= 0 || Nkv <= 0 || r <= 0 || r > 64) return 0;
+  const int64_t N[3] = {Nq, Nkv, Nkv};
+  return lin_bwd_layout(M, K, N, 3, r).total;
+}
+
+lora_status lora_qkv_backward(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,
+                              int32_t r, float scale, const void* x, int64_t ldx, const void* dq,
+                              int64_t lddq, const void* dk, int64_t lddk, const void* dv,
+                              int64_t lddv, const void* w_qkv_t, const void* a_q, const void* b_q,
+                              const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                              void* dx, int64_t lddx, void* da_q, void* db_q, void* da_k,
+                              void* db_k, void* da_v, void* db_v, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const int64_t N[3] = {Nq, Nkv, Nkv};
+  const void* d[3] = {dq, dk, dv};
+  const int64_t ld[3] = {lddq, lddk, lddv};
+  const void* aa[3] = {a_q, a_k, a_v};
+  const void* bb[3] = {b_q, b_k, b_v};
+  void* dda[3] = {da_q, da_k, da_v};
+  void* ddb[3] = {db_q, db_k, db_v};
+  return linear_backward(dtype, M, K, N, 3, r, scale, x, ldx, d, ld, w_qkv_t, aa, bb, dx, lddx,
+                         dda, ddb, workspace, workspace_bytes, stream);
 }
 
 size_t lora_linear_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t r) {

@@ -411,6 +411,49 @@ def linear_backward(x, dout, w_t, a, b, scale: float, workspace: torch.Tensor | 
     return g
 
 
+def qkv_prepare_backward(w_q, w_k, w_v):
+    """[W_q^T | W_k^T | W_v^T] [K][Nq + 2 Nkv] as the q/k/v backward reads it
+    (``lora_qkv_prepare_backward``). Done once per layer."""
+    _dev(w_q, w_k, w_v)
+    Nq, K = w_q.shape
+    Nkv = w_k.shape[0]
+    for t, shape, name in ((w_q, (Nq, K), "w_q"), (w_k, (Nkv, K), "w_k"), (w_v, (Nkv, K), "w_v")):
+        _bf16_mat(t, shape, name)
+    w_t = torch.empty((K, Nq + 2 * Nkv), dtype=torch.bfloat16, device=w_q.device)
+    _lib.lora_qkv_prepare_backward(_lib.LORA_BF16, K, Nq, Nkv, w_q, w_k, w_v, w_t, _stream())
+    return w_t
+
+
+def qkv_backward(x, dq, dk, dv, w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, scale: float,
+                 workspace: torch.Tensor | None = None):
+    """Gradients of ``qkv_fused`` (``lora_qkv_backward``): dict with dx [M][K] (the three
+    projections' terms summed, rounded once), da_q/da_k/da_v [r][K], db_q [Nq][r], db_k, db_v
+    [Nkv][r] (bf16). x is only read."""
+    _dev(x, dq, dk, dv, w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, workspace)
+    M, K = x.shape
+    Nq, r = b_q.shape
+    Nkv = b_k.shape[0]
+    for t, shape, name in ((w_qkv_t, (K, Nq + 2 * Nkv), "w_qkv_t"), (a_q, (r, K), "a_q"),
+                           (a_k, (r, K), "a_k"), (a_v, (r, K), "a_v"), (b_q, (Nq, r), "b_q"),
+                           (b_k, (Nkv, r), "b_k"), (b_v, (Nkv, r), "b_v"), (dq, (M, Nq), "dq"),
+                           (dk, (M, Nkv), "dk"), (dv, (M, Nkv), "dv")):
+        _bf16_mat(t, shape, name)
+    _bf16_in(x, "x")
+    dev, bf = x.device, torch.bfloat16
+    g = {"dx": torch.empty((M, K), dtype=bf, device=dev)}
+    for p, n in (("q", Nq), ("k", Nkv), ("v", Nkv)):
+        g["da_" + p] = torch.empty((r, K), dtype=bf, device=dev)
+        g["db_" + p] = torch.empty((n, r), dtype=bf, device=dev)
+    nbytes = _lib.lora_qkv_backward_workspace_size(_lib.LORA_BF16, M, K, Nq, Nkv, r)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _lib.lora_qkv_backward(_lib.LORA_BF16, M, K, Nq, Nkv, r, float(scale), x, _rows(x, "x"), dq,
+                           Nq, dk, Nkv, dv, Nkv, w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, g["dx"], K,
+                           g["da_q"], g["db_q"], g["da_k"], g["db_k"], g["da_v"], g["db_v"],
+                           workspace, workspace.numel(), _stream())
+    return g
+
+
 def qkv_fused(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, scale: float,
               workspace: torch.Tensor | None = None):
     """(q, k, v) projections of one x with one adapter each (``lora_qkv_fused``)."""

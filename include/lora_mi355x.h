@@ -487,6 +487,43 @@ size_t lora_linear_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t 
                                            int32_t r);
 
 /*
+ * lora_qkv_prepare_backward -- the frozen query, key and value weights in the layout
+ * lora_qkv_backward reads, written once per layer (bf16): w_q [Nq][K], w_k and w_v [Nkv][K] ->
+ * w_qkv_t = [W_q^T | W_k^T | W_v^T] [K][Nq + 2 Nkv] (row-major). Buffers are the caller's.
+ */
+lora_status lora_qkv_prepare_backward(lora_dtype dtype, int64_t K, int64_t Nq, int64_t Nkv,
+                                      const void* w_q, const void* w_k, const void* w_v,
+                                      void* w_qkv_t, void* stream);
+
+/*
+ * lora_qkv_backward -- gradients of lora_qkv_fused (bf16): the query, key and value projections
+ * of one x, each as lora_linear_backward, with the three projections' contributions to dx summed
+ * in fp32 and rounded once (same source as lora_linear_backward):
+ *     dx = round( sum_{p in q,k,v} dout_p W_p + dxa_p A_p ),   dxa_p = round(dout_p (scale B_p))
+ *     dA_p = round(dxa_p^T x),   dB_p = round(scale dout_p^T xa_p),   xa_p = round(x A_p^T)
+ *
+ *   x [M][ldx >= K]; dq [M][lddq >= Nq], dk [M][lddk >= Nkv], dv [M][lddv >= Nkv]; w_qkv_t from
+ *   lora_qkv_prepare_backward; a_* [r][K]; b_q [Nq][r], b_k and b_v [Nkv][r]; dx [M][lddx >= K]
+ *   (not x, dq, dk or dv); da_* [r][K]; db_q [Nq][r], db_k and db_v [Nkv][r] (contiguous).
+ *   1 <= r <= 64; K, Nq and Nkv multiples of 32; x, dq, dk, dv and w_qkv_t 16-byte aligned with
+ *   16-byte aligned row pitches. workspace of lora_qkv_backward_workspace_size(...) bytes,
+ *   16-byte aligned, not read before written (it also holds [dq | dk | dv] side by side for the
+ *   dx product).
+ * Errors as lora_linear_backward.
+ */
+lora_status lora_qkv_backward(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,
+                              int32_t r, float scale, const void* x, int64_t ldx, const void* dq,
+                              int64_t lddq, const void* dk, int64_t lddk, const void* dv,
+                              int64_t lddv, const void* w_qkv_t, const void* a_q, const void* b_q,
+                              const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                              void* dx, int64_t lddx, void* da_q, void* db_q, void* da_k,
+                              void* db_k, void* da_v, void* db_v, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+size_t lora_qkv_backward_workspace_size(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq,
+                                        int64_t Nkv, int32_t r);
+
+/*
  * lora_embedding_a -- the LoRA-A product of an embedding layer (the embedding LoRA-A forward of
  * "Decode LoRA kernels are optimized", Summary and Behaviour changes; the page does not print
  * the arithmetic, this is its reading): for segment g (adapter a, rank r = lora_ranks[a]) and

@@ -114,3 +114,60 @@ def test_argument_errors():
     torch.cuda.synchronize()
     assert call(dx.data_ptr()) == 0
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ query, key and value in one call
+
+def _qkv_gpu(c, douts):
+    alp = _alp()
+    g = lambda t: t.to("cuda").contiguous()
+    w_t = alp.qkv_prepare_backward(g(c.w_q), g(c.w_k), g(c.w_v))
+    ref_t = torch.cat([c.w_q.T, c.w_k.T, c.w_v.T], dim=1).contiguous()
+    assert torch.equal(w_t.cpu(), ref_t)  # [W_q^T | W_k^T | W_v^T] bit for bit
+    x = g(c.x)
+    x_before = x.clone()
+    out = alp.qkv_backward(x, *[g(d) for d in douts], w_t, g(c.a_q), g(c.b_q), g(c.a_k), g(c.b_k),
+                           g(c.a_v), g(c.b_v), c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(x, x_before)
+    return {k: t.cpu() for k, t in out.items()}
+
+
+def _qkv_check(c, douts, got):
+    ref = oracle.lora_qkv_backward(c.x, *douts, c.w_q, c.w_k, c.w_v, c.a_q, c.b_q, c.a_k, c.b_k,
+                                   c.a_v, c.b_v, c.scale, "bf16")
+    X = f64(c.x)
+    sq = np.square
+    dx2 = 0.0
+    rss = {}
+    for p, d, W, A, B in (("q", douts[0], c.w_q, c.a_q, c.b_q), ("k", douts[1], c.w_k, c.a_k, c.b_k),
+                          ("v", douts[2], c.w_v, c.a_v, c.b_v)):
+        D, W, A, B = f64(d), f64(W), f64(A), f64(B)
+        xa = oracle.rho(X @ A.T, "bf16")
+        dxa = oracle.rho(c.scale * (D @ B), "bf16")
+        dx2 = dx2 + sq(D) @ sq(W) + sq(dxa) @ sq(A)
+        rss["da_" + p] = np.sqrt(sq(dxa).T @ sq(X))
+        rss["db_" + p] = np.sqrt(c.scale ** 2 * (sq(D).T @ sq(xa)))
+    rss["dx"] = np.sqrt(dx2)
+    for k in ("dx", "da_q", "db_q", "da_k", "db_k", "da_v", "db_v"):
+        print(f"{k}: outside the plain bar {strict_fail_fraction(got[k], ref[k]):.2e}", flush=True)
+        assert_close_sum_lowp(got[k], ref[k], rss[k], k)
+
+
+@pytest.mark.parametrize("M,K,Nq,Nkv,r,scale", [(300, 256, 192, 64, 16, 4.0),
+                                                (77, 128, 96, 32, 7, 1.5),
+                                                (130, 64, 128, 96, 64, 0.5)])
+def test_qkv_small(M, K, Nq, Nkv, r, scale):
+    c = li.config_qkv(seed=34, M=M, H=K, Nq=Nq, Nkv=Nkv, r=r, scale=scale)
+    douts = li.projection_douts(seed=34, M=M, widths=(Nq, Nkv, Nkv))
+    print("case qkv", M, K, Nq, Nkv, r, scale, flush=True)
+    _qkv_check(c, douts, _qkv_gpu(c, douts))
+
+
+def test_qkv_qwen3_8b():
+    """The query, key and value projections of the Qwen3-8B layer (M = 4096, K = 4096,
+    Nq = 4096, Nkv = 1024, r = 16, scale 4); every output of the seven gradients."""
+    c = li.config_qkv()
+    douts = li.projection_douts(seed=5, M=c.M, widths=(c.Nq, c.Nkv, c.Nkv))
+    print("case qwen3-8b qkv", flush=True)
+    _qkv_check(c, douts, _qkv_gpu(c, douts))
