@@ -212,47 +212,67 @@ def mlp_backward_flops(M: int, H: int, I: int, r: int) -> tuple[int, int]:
 
 
 def projection_backward_object(steps: int, warmup: int) -> dict:
-    """The LoRA projection backward (bf16) at the Qwen3-8B output projection (M = 4096, K = N =
-    4096, r = 16, scale 4): lora_linear_backward, K calls back to back after a warm-up, HIP
-    events on its stream; flops of the gradient arithmetic (dx = dout W + dxa A, dxa, dA, dB; the
-    recomputed xa not counted), against dense bf16 MFMA."""
+    """The LoRA attention-projection backward (bf16, the Qwen3-8B shapes of the forward object:
+    M = 4096, H = 4096, Nq = 4096, Nkv = 1024, r = 16, scale 4): lora_qkv_backward for the query,
+    key and value projections of x, then lora_linear_backward for the output projection; K pairs
+    back to back after a warm-up, HIP events on their stream; flops of the gradient arithmetic
+    (dx, dxa, dA, dB; the recomputed xa not counted), against dense bf16 MFMA. The output
+    projection alone is timed beside it."""
     import torch
 
     import lora_inputs as li
     from adapter_lora_projection_amd import _lib
 
-    M = K = N = 4096
-    r, scale = 16, 4.0
-    c = li.config_qkv(seed=5, M=M, H=K, Nq=N, Nkv=32, r=r, scale=scale)
-    (dout,) = li.projection_douts(seed=5, M=M, widths=(N,))
+    c = li.config_qkv()
+    M, H, Nq, Nkv, r, s = c.M, c.H, c.Nq, c.Nkv, c.r, c.scale
+    dq, dk, dv, do = li.projection_douts(seed=5, M=M, widths=(Nq, Nkv, Nkv, H))
     g = lambda t: t.to("cuda").contiguous()
-    x, d, w, a, b = g(c.x), g(dout), g(c.w_q), g(c.a_q), g(c.b_q)
-    w_t = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
+    d = {k: g(getattr(c, k)) for k in ("x", "w_q", "w_k", "w_v", "a_q", "b_q", "a_k", "b_k", "a_v",
+                                       "b_v", "w_o", "a_o", "b_o")}
+    dq, dk, dv, do = g(dq), g(dk), g(dv), g(do)
+    q_in = g(c.x[:, :Nq]) if Nq == H else torch.randn(M, Nq, device="cuda").to(torch.bfloat16)
     stream = torch.cuda.current_stream().cuda_stream
-    _lib.lora_linear_prepare_backward(_lib.LORA_BF16, K, N, w, w_t, stream)
-    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
-    da = torch.empty((r, K), dtype=torch.bfloat16, device="cuda")
-    db = torch.empty((N, r), dtype=torch.bfloat16, device="cuda")
-    n = _lib.lora_linear_backward_workspace_size(_lib.LORA_BF16, M, K, N, r)
-    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    bf = torch.bfloat16
+    w_qkv_t = torch.empty((H, Nq + 2 * Nkv), dtype=bf, device="cuda")
+    _lib.lora_qkv_prepare_backward(_lib.LORA_BF16, H, Nq, Nkv, d["w_q"], d["w_k"], d["w_v"], w_qkv_t,
+                                   stream)
+    w_o_t = torch.empty((Nq, H), dtype=bf, device="cuda")
+    _lib.lora_linear_prepare_backward(_lib.LORA_BF16, Nq, H, d["w_o"], w_o_t, stream)
+    e = lambda *shape: torch.empty(shape, dtype=bf, device="cuda")
+    dx, da_q, da_k, da_v, db_q, db_k, db_v = e(M, H), e(r, H), e(r, H), e(r, H), e(Nq, r), e(Nkv, r), e(Nkv, r)
+    dq_in, da_o, db_o = e(M, Nq), e(r, Nq), e(H, r)
+    n = max(_lib.lora_qkv_backward_workspace_size(_lib.LORA_BF16, M, H, Nq, Nkv, r),
+            _lib.lora_linear_backward_workspace_size(_lib.LORA_BF16, M, Nq, H, r), 1)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def o_call():  # output projection: input q_in [M][Nq] (the attention output), out [M][H]
+        _lib.lora_linear_backward(_lib.LORA_BF16, M, Nq, H, r, s, q_in, Nq, do, H, w_o_t, d["a_o"],
+                                  d["b_o"], dq_in, Nq, da_o, db_o, ws, n, stream)
 
     def call():
-        _lib.lora_linear_backward(_lib.LORA_BF16, M, K, N, r, scale, x, K, d, N, w_t, a, b, dx, K,
-                                  da, db, ws, n, stream)
+        _lib.lora_qkv_backward(_lib.LORA_BF16, M, H, Nq, Nkv, r, s, d["x"], H, dq, Nq, dk, Nkv, dv,
+                               Nkv, w_qkv_t, d["a_q"], d["b_q"], d["a_k"], d["b_k"], d["a_v"],
+                               d["b_v"], dx, H, da_q, db_q, da_k, db_k, da_v, db_v, ws, n, stream)
+        o_call()
 
     for _ in range(max(warmup, 30)):
         call()
     torch.cuda.synchronize()
     ms, _ = timed_windows(call, steps)
-    flops = 2 * M * N * K + 4 * M * N * r + 4 * M * r * K
-    tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": f"LoRA projection backward bf16 (Qwen3-8B output projection), M={M} K={K} "
-                        f"N={N} r={r} scale={scale:g}", "ms_per_call": round(ms, 4),
-            "flops_per_call": int(flops), "value": round(tflops, 1), "unit": "TFLOP/s",
+    ms_o, _ = timed_windows(o_call, steps)
+    nt = Nq + 2 * Nkv
+    flops_qkv = 2 * M * H * nt + 4 * M * r * nt + 12 * M * r * H
+    flops_o = 2 * M * H * Nq + 4 * M * H * r + 4 * M * r * Nq
+    tflops = (flops_qkv + flops_o) / (ms * 1e-3) / 1e12
+    return {"workload": f"LoRA q/k/v + o projection backward bf16, M={M} H={H} Nq={Nq} Nkv={Nkv} "
+                        f"r={r} scale={s:g}", "ms_per_call": round(ms, 4),
+            "flops_per_call": int(flops_qkv + flops_o), "value": round(tflops, 1), "unit": "TFLOP/s",
+            "o_projection_ms": round(ms_o, 4),
+            "o_projection_tflops": round(flops_o / (ms_o * 1e-3) / 1e12, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                          "traffic": None,
-                         "kernel": "lora_linear_backward (all launches of one call)"}}
+                         "kernel": "lora_qkv_backward + lora_linear_backward (all launches)"}}
 
 
 def mlp_backward_object(steps: int, warmup: int) -> dict:
