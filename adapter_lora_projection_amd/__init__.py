@@ -8,7 +8,7 @@ stream. Every step runs in the HIP library; there is no CPU path.
 """
 
 from ._lib import LoraError, Plan, lib, lora_version
-from .ops import (LoraMlpFunction, check_metadata, embedding_a, expand, fast_path_eligible,
+from .ops import (LoraLinearFunction, LoraMlpFunction, LoraQkvFunction, check_metadata, embedding_a, expand, fast_path_eligible,
                   linear_backward, linear_prepare_backward, qkv_backward, qkv_prepare_backward,
                   fast_path_ineligibility, linear_fused, mlp_backward, mlp_fused, mlp_fused_train,
                   mlp_prepare_backward, qkv_fused, require_fast_path, schedule_tiles, shrink,
@@ -19,4 +19,5 @@ __all__ = ["LoraError", "Plan", "lib", "lora_version", "shrink", "expand", "shri
            "mlp_fused", "linear_fused", "qkv_fused", "embedding_a", "mlp_fused_train",
            "mlp_prepare_backward", "mlp_backward", "LoraMlpFunction", "check_metadata",
            "fast_path_eligible", "fast_path_ineligibility", "require_fast_path",
-           "linear_prepare_backward", "linear_backward", "qkv_prepare_backward", "qkv_backward"]
+           "linear_prepare_backward", "linear_backward", "qkv_prepare_backward", "qkv_backward",
+           "LoraLinearFunction", "LoraQkvFunction"]

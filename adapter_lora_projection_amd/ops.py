@@ -349,6 +349,46 @@ class LoraMlpFunction(torch.autograd.Function):
                 g["db_down"], None, None, None, None, None, None)
 
 
+class LoraLinearFunction(torch.autograd.Function):
+    """autograd wrapper of one LoRA projection: forward = lora_linear_fused (saving x), backward =
+    lora_linear_backward. W is frozen; its backward layout (linear_prepare_backward) is passed
+    in. x is saved and never written."""
+
+    @staticmethod
+    def forward(ctx, x, a, b, w, w_t, scale):
+        out = linear_fused(x, w, a, b, scale)
+        ctx.save_for_backward(x, a, b, w_t)
+        ctx.scale = scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, a, b, w_t = ctx.saved_tensors
+        g = linear_backward(x, dout.contiguous(), w_t, a, b, ctx.scale)
+        return g["dx"], g["da"], g["db"], None, None, None
+
+
+class LoraQkvFunction(torch.autograd.Function):
+    """autograd wrapper of the query, key and value projections of one x: forward =
+    lora_qkv_fused (saving x), backward = lora_qkv_backward. The W are frozen; their backward
+    layout (qkv_prepare_backward) is passed in."""
+
+    @staticmethod
+    def forward(ctx, x, a_q, b_q, a_k, b_k, a_v, b_v, w_q, w_k, w_v, w_qkv_t, scale):
+        q, k, v = qkv_fused(x, w_q, w_k, w_v, a_q, b_q, a_k, b_k, a_v, b_v, scale)
+        ctx.save_for_backward(x, a_q, b_q, a_k, b_k, a_v, b_v, w_qkv_t)
+        ctx.scale = scale
+        return q, k, v
+
+    @staticmethod
+    def backward(ctx, dq, dk, dv):
+        x, a_q, b_q, a_k, b_k, a_v, b_v, w_qkv_t = ctx.saved_tensors
+        g = qkv_backward(x, dq.contiguous(), dk.contiguous(), dv.contiguous(), w_qkv_t, a_q, b_q,
+                         a_k, b_k, a_v, b_v, ctx.scale)
+        return (g["dx"], g["da_q"], g["db_q"], g["da_k"], g["db_k"], g["da_v"], g["db_v"], None,
+                None, None, None, None)
+
+
 def _bf16_mat(t, shape, name):
     if tuple(t.shape) != shape or not t.is_contiguous() or t.dtype != torch.bfloat16:
         raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape}")

@@ -171,3 +171,42 @@ def test_qkv_qwen3_8b():
     douts = li.projection_douts(seed=5, M=c.M, widths=(c.Nq, c.Nkv, c.Nkv))
     print("case qwen3-8b qkv", flush=True)
     _qkv_check(c, douts, _qkv_gpu(c, douts))
+
+
+# ------------------------------------------------------------ autograd wrappers
+
+def test_autograd_functions_match_the_direct_calls():
+    """LoraLinearFunction and LoraQkvFunction: forward outputs and every gradient equal the
+    direct calls bit for bit, and the q/k/v gradients agree with the oracle chain."""
+    alp = _alp()
+    c = li.config_qkv(seed=35, M=192, H=128, Nq=160, Nkv=64, r=8, scale=2.0)
+    dq, dk, dv, do = [t.to("cuda") for t in li.projection_douts(seed=35, M=192, widths=(160, 64, 64, 128))]
+    g = lambda t: t.to("cuda").contiguous()
+    d = {k: g(getattr(c, k)) for k in ("x", "w_q", "w_k", "w_v", "a_q", "b_q", "a_k", "b_k", "a_v",
+                                       "b_v", "w_o", "a_o", "b_o")}
+    print("case autograd projections", flush=True)
+    # q/k/v
+    w_qkv_t = alp.qkv_prepare_backward(d["w_q"], d["w_k"], d["w_v"])
+    names = ("x", "a_q", "b_q", "a_k", "b_k", "a_v", "b_v")
+    leaves = {k: d[k].clone().requires_grad_(True) for k in names}
+    q, k, v = alp.LoraQkvFunction.apply(*[leaves[n] for n in names], d["w_q"], d["w_k"], d["w_v"],
+                                        w_qkv_t, c.scale)
+    torch.autograd.backward((q, k, v), (dq, dk, dv))
+    q0, k0, v0 = alp.qkv_fused(d["x"], d["w_q"], d["w_k"], d["w_v"], d["a_q"], d["b_q"], d["a_k"],
+                               d["b_k"], d["a_v"], d["b_v"], c.scale)
+    ref = alp.qkv_backward(d["x"], dq, dk, dv, w_qkv_t, d["a_q"], d["b_q"], d["a_k"], d["b_k"],
+                           d["a_v"], d["b_v"], c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(q.detach(), q0) and torch.equal(k.detach(), k0) and torch.equal(v.detach(), v0)
+    for n, key in zip(names, ("dx", "da_q", "db_q", "da_k", "db_k", "da_v", "db_v")):
+        assert torch.equal(leaves[n].grad, ref[key]), key
+    # output projection, on q as its input
+    w_o_t = alp.linear_prepare_backward(d["w_o"])
+    lv = {n: t.clone().requires_grad_(True) for n, t in (("x", q0), ("a", d["a_o"]), ("b", d["b_o"]))}
+    o = alp.LoraLinearFunction.apply(lv["x"], lv["a"], lv["b"], d["w_o"], w_o_t, c.scale)
+    o.backward(do)
+    ref = alp.linear_backward(q0, do, w_o_t, d["a_o"], d["b_o"], c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), alp.linear_fused(q0, d["w_o"], d["a_o"], d["b_o"], c.scale))
+    for n, key in (("x", "dx"), ("a", "da"), ("b", "db")):
+        assert torch.equal(lv[n].grad, ref[key]), key
