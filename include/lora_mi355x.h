@@ -262,9 +262,10 @@ lora_status lora_expand_ex(lora_dtype dtype, int64_t T, int32_t S, int32_t R, in
  *              any size, lora_shrink calls and graph replays with no clearing. Calls that
  *              overlap in time must not share it.
  *              The int at byte offset LORA_SHRINK_EXPAND_FLAG_OFFSET is set to 1 if a wait for
- *              the shrink's pieces ever exceeded its one-second bound (the shrink workgroups are
- *              dispatched first and never wait, so this does not happen; the bound only
- *              guarantees that every wave ends); the y of that call is then undefined, its
+ *              the shrink's pieces ever exceeded its one-second bound (the shrink workgroups
+ *              never wait, the single launch is taken only when the whole grid fits on the GPU
+ *              at once, and workgroups are dispatched in order, so this does not happen; the
+ *              bound only guarantees that every wave ends); the y of that call is then undefined, its
  *              counters may be left nonzero, and the workspace must be zero-filled again before
  *              its next use. The library never clears the flag.
  *
