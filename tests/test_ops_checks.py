@@ -120,3 +120,41 @@ def test_expand_shapes_checked(no_device_check):
     with pytest.raises(ValueError, match="scalings"):
         ops.expand(h, w_b, sl, m["seg_indptr"], m["weight_indices"], m["permutation"],
                    m["lora_ranks"], sc[:2], torch.zeros(10, 48, dtype=bf), S=3, R=2)
+
+
+def test_linear_backward_checks(no_device_check):
+    z = lambda *s: torch.zeros(*s, dtype=bf)
+    good = dict(x=z(8, 64), dout=z(8, 32), w_t=z(64, 32), a=z(4, 64), b=z(32, 4))
+    for name, bad in (("w_t", z(32, 64)), ("a", z(4, 32)), ("dout", z(8, 16)),
+                      ("x", torch.zeros(8, 64, dtype=torch.float32))):
+        kw = dict(good, **{name: bad})
+        with pytest.raises(ValueError):
+            ops.linear_backward(**kw, scale=2.0)
+    with pytest.raises(ValueError, match="w"):
+        ops.linear_prepare_backward(torch.zeros(32, 64, dtype=torch.float16))
+
+
+def test_qkv_backward_checks(no_device_check):
+    z = lambda *s: torch.zeros(*s, dtype=bf)
+    good = dict(x=z(8, 64), dq=z(8, 64), dk=z(8, 32), dv=z(8, 32), w_qkv_t=z(64, 128), a_q=z(4, 64),
+                b_q=z(64, 4), a_k=z(4, 64), b_k=z(32, 4), a_v=z(4, 64), b_v=z(32, 4))
+    for name, bad in (("w_qkv_t", z(64, 96)), ("dv", z(8, 64)), ("a_v", z(4, 32)),
+                      ("x", torch.zeros(8, 64, dtype=torch.float16))):
+        kw = dict(good, **{name: bad})
+        with pytest.raises(ValueError):
+            ops.qkv_backward(**kw, scale=2.0)
+
+
+def test_shrink_expand_checks(no_device_check):
+    z = lambda *s: torch.zeros(*s, dtype=bf)
+    i32 = lambda *v: torch.tensor(v, dtype=torch.int32)
+    good = dict(x=z(10, 64), w_a=z(2, 48, 64), w_b=z(2, 96, 16), slice_offsets=i32(0, 32, 64, 96),
+                seg_indptr=i32(0, 4, 10), weight_indices=i32(0, 1), permutation=None,
+                lora_ranks=i32(16, 8), scalings=torch.ones(2), y=z(10, 96))
+    for name, bad in (("w_a", z(2, 32, 64)), ("w_b", z(2, 96, 8)), ("y", z(9, 96)),
+                      ("scalings", torch.ones(2, dtype=torch.float64)), ("seg_indptr", i32(0, 10))):
+        kw = dict(good, **{name: bad})
+        with pytest.raises((ValueError, TypeError)):
+            ops.shrink_expand(**kw, S=3, R=16)
+    with pytest.raises(ValueError, match="h"):
+        ops.shrink_expand(**good, S=3, R=16, h=z(10, 40))
