@@ -2,9 +2,10 @@
 
 Through the C ABI (ctypes binding):
 - h and y equal those of lora_shrink followed by lora_expand bit for bit, on the single-launch
-  path (split and direct shrink, bf16 and fp16, rank-0 and odd-rank adapters, empty segments, the
-  identity permutation, y rows and slice starts off the 16-byte grid, K not a multiple of the
-  MFMA step, padded rank 32) and on sizes that take the two-launch path;
+  path (bf16 and fp16, rank-0 and odd-rank adapters, empty segments, the identity permutation, y
+  rows and slice starts off the 16-byte grid, K not a multiple of the MFMA step, padded rank 32,
+  one token) and on sizes that take the two-launch path (one workgroup per tile at 1000 and 1024
+  tokens, fp32, rows off the 16-byte grid);
 - y against the oracle's whole chain from x (nothing computed on the GPU is fed to the oracle);
 - one workspace reused across calls of different sizes and across graph replays, with the
   counters left zero and the wait-bound flag never set.
@@ -56,7 +57,7 @@ def _pair(c, d, y0, ws=None, h=None):
 def _case(kind: str):
     if kind.startswith("sweep"):
         return li.sweep_case(int(kind[5:]))
-    if kind == "direct1000":  # one workgroup per tile (no split), XCD-ordered grid
+    if kind == "direct1000":  # one workgroup per tile (no split): the two launches
         return li.sweep_case(1000)
     if kind == "f16":
         return li.make_sgmv("pair_f16", seed=21, T=200, K=4096, S=3, R=16, L=4,
@@ -158,8 +159,9 @@ def _ws_for(cases):
 
 
 def test_pair_workspace_reuse():
-    """One workspace across calls of different sizes (split and direct shrink): every call equals
-    the separate calls bit for bit, the flag stays 0 and the arrival counters end zero."""
+    """One workspace across calls of different sizes (single launches and, at 1000 tokens, the two
+    launches): every call equals the separate calls bit for bit, the flag stays 0 and the counters
+    end zero."""
     cases = [li.sweep_case(t) for t in (128, 50, 512, 1000, 256, 128)]
     ws = _ws_for(cases)
     for c in cases:
