@@ -861,10 +861,14 @@ lora_status linear_backward(lora_dtype dtype, int64_t M, int64_t K, const int64_
     }
   }
   // 4. dx = round(sum_p dout_p W_p + dxa_p A_p): the plain GEMM over the reduction Ntot with the
-  //    LoRA terms in K ([dout_0 | ..] copied side by side first when P > 1)
+  //    LoRA terms in K ([dout_0 | ..] copied side by side first when P > 1, unless it already is)
   const uint16_t* dA = u16(dout[0]);
   int64_t ldA = lddo[0];
-  if (P > 1) {
+  // already side by side (views of one [M][>= Ntot] gradient of a fused projection): read in place
+  bool adjacent = true;
+  for (int p = 1; p < P; ++p)
+    adjacent = adjacent && lddo[p] == lddo[0] && u16(dout[p]) == u16(dout[p - 1]) + N[p - 1];
+  if (P > 1 && !adjacent) {
     uint16_t* dcat = W(L.dcat);
     int64_t c0 = 0;
     for (int p = 0; p < P; ++p) {

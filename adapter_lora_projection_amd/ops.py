@@ -383,8 +383,9 @@ class LoraQkvFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dq, dk, dv):
         x, a_q, b_q, a_k, b_k, a_v, b_v, w_qkv_t = ctx.saved_tensors
-        g = qkv_backward(x, dq.contiguous(), dk.contiguous(), dv.contiguous(), w_qkv_t, a_q, b_q,
-                         a_k, b_k, a_v, b_v, ctx.scale)
+        rm = lambda t: t if t.dim() == 2 and t.stride(1) == 1 else t.contiguous()  # row-major
+        g = qkv_backward(x, rm(dq), rm(dk), rm(dv), w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v,
+                         ctx.scale)
         return (g["dx"], g["da_q"], g["db_q"], g["da_k"], g["db_k"], g["da_v"], g["db_v"], None,
                 None, None, None, None)
 
@@ -475,9 +476,14 @@ def qkv_backward(x, dq, dk, dv, w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, scale: fl
     Nkv = b_k.shape[0]
     for t, shape, name in ((w_qkv_t, (K, Nq + 2 * Nkv), "w_qkv_t"), (a_q, (r, K), "a_q"),
                            (a_k, (r, K), "a_k"), (a_v, (r, K), "a_v"), (b_q, (Nq, r), "b_q"),
-                           (b_k, (Nkv, r), "b_k"), (b_v, (Nkv, r), "b_v"), (dq, (M, Nq), "dq"),
-                           (dk, (M, Nkv), "dk"), (dv, (M, Nkv), "dv")):
+                           (b_k, (Nkv, r), "b_k"), (b_v, (Nkv, r), "b_v")):
         _bf16_mat(t, shape, name)
+    # upstream gradients: row-major with any row pitch (column views of one fused gradient are
+    # read in place)
+    for t, shape, name in ((dq, (M, Nq), "dq"), (dk, (M, Nkv), "dk"), (dv, (M, Nkv), "dv")):
+        if tuple(t.shape) != shape or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a bf16 tensor of shape {shape}")
+    lds = [_rows(t, n) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
     _bf16_in(x, "x")
     dev, bf = x.device, torch.bfloat16
     g = {"dx": torch.empty((M, K), dtype=bf, device=dev)}
@@ -488,7 +494,7 @@ def qkv_backward(x, dq, dk, dv, w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, scale: fl
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _lib.lora_qkv_backward(_lib.LORA_BF16, M, K, Nq, Nkv, r, float(scale), x, _rows(x, "x"), dq,
-                           Nq, dk, Nkv, dv, Nkv, w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, g["dx"], K,
+                           lds[0], dk, lds[1], dv, lds[2], w_qkv_t, a_q, b_q, a_k, b_k, a_v, b_v, g["dx"], K,
                            g["da_q"], g["db_q"], g["da_k"], g["db_k"], g["da_v"], g["db_v"],
                            workspace, workspace.numel(), _stream())
     return g

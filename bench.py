@@ -216,8 +216,9 @@ def projection_backward_object(steps: int, warmup: int) -> dict:
     M = 4096, H = 4096, Nq = 4096, Nkv = 1024, r = 16, scale 4): lora_qkv_backward for the query,
     key and value projections of x, then lora_linear_backward for the output projection; K pairs
     back to back after a warm-up, HIP events on their stream; flops of the gradient arithmetic
-    (dx, dxa, dA, dB; the recomputed xa not counted), against dense bf16 MFMA. The output
-    projection alone is timed beside it."""
+    (dx, dxa, dA, dB; the recomputed xa not counted), against dense bf16 MFMA. Beside it: the
+    output projection alone, and the q/k/v backward on column views of one fused gradient (read
+    in place instead of copied side by side)."""
     import torch
 
     import lora_inputs as li
@@ -255,12 +256,23 @@ def projection_backward_object(steps: int, warmup: int) -> dict:
                                d["b_v"], dx, H, da_q, db_q, da_k, db_k, da_v, db_v, ws, n, stream)
         o_call()
 
+    # the same gradients as column views of one fused [M][Nq + 2 Nkv] gradient: read in place
+    fused = torch.cat([dq, dk, dv], dim=1)
+    fq, fk, fv = fused[:, :Nq], fused[:, Nq:Nq + Nkv], fused[:, Nq + Nkv:]
+    nt = Nq + 2 * Nkv
+
+    def qkv_fused_grad():
+        _lib.lora_qkv_backward(_lib.LORA_BF16, M, H, Nq, Nkv, r, s, d["x"], H, fq.data_ptr(), nt,
+                               fk.data_ptr(), nt, fv.data_ptr(), nt, w_qkv_t, d["a_q"], d["b_q"],
+                               d["a_k"], d["b_k"], d["a_v"], d["b_v"], dx, H, da_q, db_q, da_k,
+                               db_k, da_v, db_v, ws, n, stream)
+
     for _ in range(max(warmup, 30)):
         call()
     torch.cuda.synchronize()
     ms, _ = timed_windows(call, steps)
     ms_o, _ = timed_windows(o_call, steps)
-    nt = Nq + 2 * Nkv
+    ms_f, _ = timed_windows(qkv_fused_grad, steps)
     flops_qkv = 2 * M * H * nt + 4 * M * r * nt + 12 * M * r * H
     flops_o = 2 * M * H * Nq + 4 * M * H * r + 4 * M * r * Nq
     tflops = (flops_qkv + flops_o) / (ms * 1e-3) / 1e12
@@ -269,6 +281,8 @@ def projection_backward_object(steps: int, warmup: int) -> dict:
             "flops_per_call": int(flops_qkv + flops_o), "value": round(tflops, 1), "unit": "TFLOP/s",
             "o_projection_ms": round(ms_o, 4),
             "o_projection_tflops": round(flops_o / (ms_o * 1e-3) / 1e12, 1),
+            "qkv_ms_fused_gradient": round(ms_f, 4),
+            "qkv_ms": round(ms - ms_o, 4),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                          "traffic": None,

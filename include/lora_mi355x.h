@@ -509,7 +509,8 @@ lora_status lora_qkv_prepare_backward(lora_dtype dtype, int64_t K, int64_t Nq, i
  *   1 <= r <= 64; K, Nq and Nkv multiples of 32; x, dq, dk, dv and w_qkv_t 16-byte aligned with
  *   16-byte aligned row pitches. workspace of lora_qkv_backward_workspace_size(...) bytes,
  *   16-byte aligned, not read before written (it also holds [dq | dk | dv] side by side for the
- *   dx product).
+ *   dx product; when dk == dq + Nq and dv == dk + Nkv elements with one row pitch -- column views
+ *   of the gradient of a fused q/k/v output -- they are read in place instead).
  * Errors as lora_linear_backward.
  */
 lora_status lora_qkv_backward(lora_dtype dtype, int64_t M, int64_t K, int64_t Nq, int64_t Nkv,

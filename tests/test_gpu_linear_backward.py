@@ -210,3 +210,23 @@ def test_autograd_functions_match_the_direct_calls():
     assert torch.equal(o.detach(), alp.linear_fused(q0, d["w_o"], d["a_o"], d["b_o"], c.scale))
     for n, key in (("x", "dx"), ("a", "da"), ("b", "db")):
         assert torch.equal(lv[n].grad, ref[key]), key
+
+
+def test_qkv_fused_gradient_read_in_place():
+    """dq, dk, dv as column views of one [M][Nq + 2 Nkv] gradient (read in place by the dx
+    product) give the same gradients, bit for bit, as contiguous copies (copied side by side
+    through the workspace)."""
+    alp = _alp()
+    c = li.config_qkv(seed=36, M=300, H=256, Nq=192, Nkv=64, r=16, scale=4.0)
+    g = lambda t: t.to("cuda").contiguous()
+    fused = torch.randn(300, 192 + 128, device="cuda").to(torch.bfloat16)
+    views = (fused[:, :192], fused[:, 192:256], fused[:, 256:])
+    w_t = alp.qkv_prepare_backward(g(c.w_q), g(c.w_k), g(c.w_v))
+    lora = [g(t) for t in (c.a_q, c.b_q, c.a_k, c.b_k, c.a_v, c.b_v)]
+    got = alp.qkv_backward(g(c.x), *views, w_t, *lora, c.scale)
+    ref = alp.qkv_backward(g(c.x), *[v.contiguous() for v in views], w_t, *lora, c.scale)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
+    douts = [v.cpu() for v in views]
+    _qkv_check(c, douts, {k: t.cpu() for k, t in got.items()})
