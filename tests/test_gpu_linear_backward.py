@@ -230,3 +230,37 @@ def test_qkv_fused_gradient_read_in_place():
         assert torch.equal(got[k], ref[k]), k
     douts = [v.cpu() for v in views]
     _qkv_check(c, douts, {k: t.cpu() for k, t in got.items()})
+
+
+def test_qkv_backward_graph_replay():
+    """The q/k/v backward (with its side-by-side copy of the gradients) captured in a HIP graph:
+    every replay, with eager work and synchronisations between them, equals the eager result bit
+    for bit."""
+    alp = _alp()
+    c = li.config_qkv(seed=37, M=256, H=128, Nq=128, Nkv=64, r=16, scale=4.0)
+    douts = [t.to("cuda") for t in li.projection_douts(seed=37, M=256, widths=(128, 64, 64))]
+    g = lambda t: t.to("cuda").contiguous()
+    w_t = alp.qkv_prepare_backward(g(c.w_q), g(c.w_k), g(c.w_v))
+    lora = [g(t) for t in (c.a_q, c.b_q, c.a_k, c.b_k, c.a_v, c.b_v)]
+    x = g(c.x)
+    from adapter_lora_projection_amd import _lib
+    n = _lib.lora_qkv_backward_workspace_size(_lib.LORA_BF16, 256, 128, 128, 64, 16)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ref = alp.qkv_backward(x, *douts, w_t, *lora, c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    ref = {k: t.clone() for k, t in ref.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        out = alp.qkv_backward(x, *douts, w_t, *lora, c.scale, workspace=ws)
+    for rep in range(4):
+        for t in out.values():
+            t.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(out[k], ref[k]), (rep, k)
+        del junk
