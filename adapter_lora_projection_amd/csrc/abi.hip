@@ -872,8 +872,8 @@ lora_status linear_backward(lora_dtype dtype, int64_t M, int64_t K, const int64_
     uint16_t* dcat = W(L.dcat);
     int64_t c0 = 0;
     for (int p = 0; p < P; ++p) {
-      if (hipMemcpy2DAsync(dcat + c0, size_t(ntot) * 2, dout[p], size_t(lddo[p]) * 2,
-                           size_t(N[p]) * 2, size_t(M), hipMemcpyDeviceToDevice, st) != hipSuccess)
+      if (lmx::launch_copy2d(u16(dout[p]), lddo[p], dcat + c0, ntot, int(M), int(N[p]), st) !=
+          hipSuccess)
         return LORA_EHIP;
       c0 += N[p];
     }

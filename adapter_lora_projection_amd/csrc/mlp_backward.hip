@@ -79,6 +79,31 @@ hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int
   return hipGetLastError();
 }
 
+// ---- 2-D copy of a bf16 matrix ---------------------------------------------------------------
+// dst[m][c] = src[m][c] for m < rows, c < cols; 16 bytes per thread (cols, the pitches and both
+// bases 16-byte multiples, which the host checks); workgroup (x, y) copies 256 x 8 columns of
+// rows y, y + gridDim.y, ...
+__global__ __launch_bounds__(256) void copy2d_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                     uint16_t* __restrict__ dst, int64_t ldd,
+                                                     int rows, int cols) {
+  const int c = (int(blockIdx.x) * 256 + int(threadIdx.x)) * 8;
+  if (c >= cols) return;
+  for (int m = int(blockIdx.y); m < rows; m += int(gridDim.y))
+    *reinterpret_cast<uint4*>(dst + int64_t(m) * ldd + c) =
+        *reinterpret_cast<const uint4*>(src + int64_t(m) * lds + c);
+}
+
+hipError_t launch_copy2d(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int rows,
+                         int cols, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 8 != 0 || lds % 8 != 0 || ldd % 8 != 0 || (reinterpret_cast<uintptr_t>(src) & 15) ||
+      (reinterpret_cast<uintptr_t>(dst) & 15))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy2d_kernel, dim3(unsigned((cols / 8 + 255) / 256), unsigned(std::min(rows, 4096))),
+                     dim3(256), 0, st, src, lds, dst, ldd, rows, cols);
+  return hipGetLastError();
+}
+
 // ---- sums over columns and over tokens in one pass over P --------------------------------
 // Workgroup (x = block of 512 columns of one job, y = chunk of rows, z = rank block of 16): 4
 // waves, wave w owning columns [128 w, 128 w + 128) of the block. Steps of 16 rows of P (and of

@@ -93,6 +93,10 @@ hipError_t launch_small_transposes(const TJobs& jobs, hipStream_t st);
 // Plain bf16 transpose dst[c][r] = src[r][c] of a rows x cols matrix (LDS tiles of 64 x 64).
 hipError_t launch_transpose(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int rows,
                             int cols, hipStream_t st);
+// Plain bf16 copy dst[m][c] = src[m][c] of a rows x cols matrix, 16 bytes per thread (cols,
+// pitches and bases 16-byte multiples).
+hipError_t launch_copy2d(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int rows,
+                         int cols, hipStream_t st);
 
 // Sums over one pass of a bf16 matrix P [M][C] (row pitch ldp), up to 4 matrices per launch, in
 // fp32:
