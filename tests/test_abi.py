@@ -334,3 +334,17 @@ def test_shrink_expand_workspace_size():
     assert _lib.lora_shrink_expand_workspace_size(1, 50, 4096, 3, 16, 0, 6144) == 0
     assert _lib.lora_shrink_expand_workspace_size(7, 50, 4096, 3, 16, 4, 6144) == 0
     assert _lib.LORA_SHRINK_EXPAND_FLAG_OFFSET == 32764
+
+
+def test_projection_backward_workspace_sizes():
+    """The projection-backward queries: positive and growing with M for valid sizes; 0 for an
+    unsupported dtype, a rank above 64 or an empty size. The q/k/v workspace holds at least the
+    side-by-side copy of the three gradients."""
+    lin = lambda M, K, N, r, dt=1: _lib.lora_linear_backward_workspace_size(dt, M, K, N, r)
+    qkv = lambda M, K, Nq, Nkv, r, dt=1: _lib.lora_qkv_backward_workspace_size(dt, M, K, Nq, Nkv, r)
+    assert 0 < lin(128, 256, 192, 16) < lin(4096, 256, 192, 16)
+    assert 0 < qkv(128, 256, 192, 64, 16) < qkv(4096, 256, 192, 64, 16)
+    assert qkv(4096, 4096, 4096, 1024, 16) >= 4096 * 6144 * 2
+    assert lin(128, 256, 192, 16, dt=0) == 0 and qkv(128, 256, 192, 64, 16, dt=2) == 0
+    assert lin(128, 256, 192, 65) == 0 and qkv(128, 256, 192, 64, 0) == 0
+    assert lin(0, 256, 192, 16) == 0 and qkv(128, 0, 192, 64, 16) == 0
