@@ -211,6 +211,8 @@ size_t lora_shrink_workspace_size_ex(lora_dtype dtype, int64_t T, int64_t K, int
  *   slice_offsets  device int32 [S+1]: 0 <= slice_offsets[0] <= ... <= slice_offsets[S] = N.
  *   scalings       device float32 [L] (alpha / rank of each adapter).
  *   y              device [T][ldy] read and written in place, ldy >= N; row t is token t.
+ *                  (A pitch a little above N, such as N + 256 for N = 6144, measured 4-5%
+ *                  faster than ldy = N from 4096 tokens on MI355X.)
  *   workspace      device scratch of lora_expand_workspace_size(...) bytes (the segment
  *                  schedule for many segments; nonzero only then), 16-byte aligned; not read
  *                  before written.
