@@ -92,17 +92,26 @@ int esize(int dtype) { return dtype == LORA_F32 ? 4 : 2; }
 // Columns per expand workgroup, in multiples of the 64-column chunks the waves walk: the widest
 // blocks (up to 4096 columns) that still give about 400 workgroups. Longer column runs per wave
 // measured faster than more workgroups once the chip is covered (rocprofv3 sweeps on MI355X).
-// The shared-B kernel (three 256-thread workgroups resident per compute unit, 768 on the chip)
-// also takes at least 600 / tiles blocks: more blocks than that leave a second round of
-// workgroups (8192 tokens: 660 workgroups 55.7 us, 792 workgroups 63.6 us), fewer leave the
-// chip half idle (6144 tokens: 500 workgroups 44.0 us, 600 workgroups 40.6 us).
-int expand_bn(const Knobs& kn, int64_t T, int32_t G, int64_t N, int bm, int waves, int chunk,
-              bool shared) {
+// The shared-B kernel takes the narrowest power-of-two multiple of its 128-column unit whose
+// grid (tiles x (column blocks + slices)) stays within 1200 workgroups. Power-of-two widths
+// divide the usual slice widths evenly (the host cannot read the slice offsets), and blocks
+// that end part-way into a slice left some workgroups with far less work than others. Event
+// timings after a 512 MiB write on the decode sweep (q/k/v slices 4096/1024/1024): 8192 tokens
+// 1024 columns (1188 workgroups) 53.6 us against 55.7 us for 1536 (924) and 54.9 us for 512
+// (1980); 6144 tokens 1024 columns 40.8 us against 42.4 for 768 and 46.7 for 512 (1500);
+// 4096: 512 columns 31.0 against 31.4 for 768; 2048: 256 columns 19.3 against 20.4 for 384
+// and 21.3 for 128 (1836); 1024: 128 columns 13.3 against 14.0 for 256.
+int expand_bn(const Knobs& kn, int64_t T, int32_t G, int32_t S, int64_t N, int bm, int waves,
+              int chunk, bool shared) {
   const int unit = chunk * waves;
   if (kn.ebn > 0) return int(cdiv(kn.ebn, unit) * unit);
   const int64_t tiles = cdiv(T, bm) + G;
-  int64_t blocks = std::max<int64_t>(1, cdiv(400, tiles));
-  if (shared) blocks = std::max<int64_t>(blocks, 600 / tiles);
+  if (shared) {
+    int64_t bn = unit;
+    while (bn < 4096 && tiles * (cdiv(N, bn) + S) > 1200) bn *= 2;
+    return int(std::min<int64_t>(bn, 4096));
+  }
+  const int64_t blocks = std::max<int64_t>(1, cdiv(400, tiles));
   int64_t bn = cdiv(cdiv(N, blocks), unit) * unit;
   bn = std::min<int64_t>(std::max<int64_t>(bn, unit), 4096);
   return int(bn);
@@ -136,9 +145,10 @@ struct ShrinkWs {
   size_t sched, part, total;  // byte offsets: schedule list at kCounterBytes, partial planes
 };
 
-// Expand kernel shape (rocprofv3 sweeps and event timings on MI355X). From 1024 tokens, slices of
+// Expand kernel shape (rocprofv3 sweeps and event timings on MI355X). From 512 tokens, slices of
 // rank exactly 16 with 16-bit types and 16-byte aligned h, B and y rows take the shared-B kernel
-// (8192 tokens: 62 -> 56 us; 1024: 17.6 -> 16.7 us). Otherwise 4 waves with a 2-deep ring of y
+// (8192 tokens: 62 -> 56 us; 1024: 17.6 -> 16.7 us; 512, after a 512 MiB write: 12.2 -> 11.0 us;
+// at 256 tokens and below it is no faster). Otherwise 4 waves with a 2-deep ring of y
 // and B chunks up to 1024 tokens, and from 2048 tokens 128-column chunks with 16-byte y pieces
 // and a 1-deep ring (fewer bytes in flight per compute unit measured faster than deeper rings;
 // the wide chunks saved 3-12% at 2048..6144 tokens). Blocks whose y rows or start are not
@@ -148,7 +158,7 @@ int expand_variant(const Knobs& kn, int64_t T, bool shared_ok) {
     const bool shared = kn.eshape == lmx::kExpandSharedD1 || kn.eshape == lmx::kExpandSharedD2;
     return (shared && !shared_ok) ? 6 : kn.eshape;
   }
-  if (shared_ok && T >= 1024) return lmx::kExpandSharedD1;
+  if (shared_ok && T >= 512) return lmx::kExpandSharedD1;
   return T >= 2048 ? 6 : 3;
 }
 
@@ -1002,7 +1012,7 @@ lora_status lora_expand_ex(lora_dtype dtype, int64_t T, int32_t S, int32_t R, in
   const int bm = lmx::expand_plan_bm(int(dtype), variant);
   const bool shared = dtype != LORA_F32 && (variant == lmx::kExpandSharedD1 ||
                                             variant == lmx::kExpandSharedD2);
-  const int bn = expand_bn(kn, T, G, N, bm, lmx::expand_plan_waves(int(dtype), variant),
+  const int bn = expand_bn(kn, T, G, S, N, bm, lmx::expand_plan_waves(int(dtype), variant),
                            lmx::expand_plan_chunk(int(dtype), variant), shared);
   if (cdiv(N, bn) + S > 65535) return LORA_EUNSUPPORTED;
   const size_t need = schedule_bytes(T, G, bm);
@@ -1081,7 +1091,7 @@ lora_status lora_shrink_expand(lora_dtype dtype, int64_t T, int64_t K, int32_t S
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return LORA_EHIP;
     const int64_t swgs = int64_t(ws.grid_x) * ws.gy;
-    bn = expand_bn(Knobs{}, T, G, N, 16, 8, 64, false);
+    bn = expand_bn(Knobs{}, T, G, S, N, 16, 8, 64, false);
     while (bn < 4096 && swgs + ws.bound * (cdiv(N, bn) + S) > 2 * int64_t(cus)) bn += 512;
     single = swgs + ws.bound * (cdiv(N, bn) + S) <= 2 * int64_t(cus);
   }

@@ -122,11 +122,20 @@ def label_dispatches(disp: list[tuple[str, tuple]]) -> list[str]:
             keymap[(name, grid)].append(lab)
         i += 1
     labels, in_sweep = [], True
+    last_shrink: set = set()  # token counts the latest shrink dispatch can belong to
     for name, grid in disp:
         if "gemm_lora_kernel" in name or "embedding" in name or "sums_kernel" in name or "scale_lora_b" in name:
             in_sweep = False
-        if in_sweep and (name, grid) in keymap:
-            labels.append(" / ".join(keymap[(name, grid)]))
+        labs = keymap.get((name, grid), []) if in_sweep else []
+        if labs and all(l.startswith("shrink_tok") and " " not in l for l in labs):
+            last_shrink = {l[len("shrink_tok"):] for l in labs}
+        cand = {l[len("expand_tok"):] for l in labs if l.startswith("expand_tok")} & last_shrink
+        if len(labs) > 1 and "expand" in name and len(cand) == 1:
+            # grids that coincide once flattened (counter runs give only the total size): every
+            # call sequence runs a case's shrink right before its expand
+            labels.append(f"expand_tok{cand.pop()}")
+        elif labs:
+            labels.append(" / ".join(labs))
         elif "gemm_lora_kernel" in name:
             key = name[:name.index("<") + 2]
             labels.append(GEMM_LABEL.get(key, name))
